@@ -1,0 +1,626 @@
+/*
+ * kvq_oracle.c -- plain, slow, CPU reference for low-bit KV-cache decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or calls
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the bench
+ * use it.  It shares no code, header, table or constant generator with the HIP path.
+ *
+ * What it computes, and where the pages define it:
+ *   - asymmetric INT-b keys/values with FP16 scale and zero per 32-channel group,
+ *     channel 0 kept in BF16 and left out of the range estimate
+ *       (Dual-QK: Sharp Queries and Flat Keys for Prunable 2-bit KV Caches, sec. 3.3
+ *        and sec. C.3);
+ *   - channel-major key storage so that decode can skip unselected rows (same, sec. 3.3);
+ *   - Walsh-Hadamard rotation and a Lloyd-Max scalar codebook on keys
+ *       (TurboQuant on Quantized Models, abstract and topic list; Statistical Inference
+ *        and Quality Measures of KV Cache Quantisations Inspired by TurboQuant,
+ *        "Quantisierungsschemata", scheme KQV, and "Theoretischer Rahmen" for the
+ *        Beta -> Gaussian marginal that makes an N(0,1) codebook the right one);
+ *   - BF16 sink tokens (TurboQuant on Quantized Models, abstract: sink-token preservation;
+ *     Dual-QK sec. 3.3 / 4.1: first tokens kept in BF16);
+ *   - dynamic query-channel-group pruning with one mask per GQA group, ranked by
+ *     query energy summed over the group's heads (Dual-QK sec. 3.2, sec. C.2, App. A);
+ *   - attention over the decoded cache with one softmax over all positions
+ *     (Dual-QK sec. 3.4: bucket scores share one global softmax).
+ *
+ * Precision.  The encoding (quantize + pack) runs in fp32 with a fixed operation order;
+ * build with -ffp-contract=off and without fast-math so that every fp32 operation is a
+ * single IEEE-754 round-to-nearest-even operation.  Decoding and attention run in fp64.
+ *
+ * Readings taken where the pages are silent are listed in the design notes; the ones
+ * that change arithmetic are repeated at the function that implements them.
+ *
+ * Parity pins: every function here is checked by the CPU test-suite against something
+ * other than itself (library conversions, explicit Hadamard matrices, brute-force code
+ * search, exhaustive subset search, closed forms, published Lloyd-Max tables).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------ */
+/* Format constants.  Key format ids: 0 = asymmetric INT2, 1 = asymmetric INT4,
+ * 2 = 4-bit Lloyd-Max codebook, 3 = asymmetric INT8 (oracle only, for the convergence
+ * check that 8-bit codes approach dense attention).  Values are always asymmetric INT4.  */
+enum { OK_ASYM2 = 0, OK_ASYM4 = 1, OK_LLOYD4 = 2, OK_ASYM8 = 3 };
+
+static int key_bits(int kfmt) { return kfmt == OK_ASYM2 ? 2 : kfmt == OK_ASYM8 ? 8 : 4; }
+
+/* ------------------------------------------------------------------------------------ */
+/* Conversions.  fp32 -> binary16 and fp32 -> bfloat16, both round-to-nearest-even,
+ * written from the IEEE-754 definitions.                                                 */
+
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint32_t sign = (x >> 16) & 0x8000u;
+    uint32_t ex = (x >> 23) & 0xFFu;
+    uint32_t man = x & 0x7FFFFFu;
+    if (ex == 0xFFu) /* inf or nan */
+        return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));
+    int e = (int)ex - 127 + 15; /* biased binary16 exponent */
+    if (e >= 31)
+        return (uint16_t)(sign | 0x7C00u);
+    if (e >= 1) {
+        /* normal result: keep 10 mantissa bits, round on the 13 dropped ones */
+        uint32_t h = sign | ((uint32_t)e << 10) | (man >> 13);
+        uint32_t rest = man & 0x1FFFu;
+        if (rest > 0x1000u || (rest == 0x1000u && (h & 1u)))
+            h += 1u; /* a carry into the exponent is the correct rounding, up to inf */
+        return (uint16_t)h;
+    }
+    /* subnormal (or zero) result: value = m * 2^-24 with m = sig * 2^(ex-126) */
+    if (ex == 0)
+        return (uint16_t)sign; /* fp32 subnormals are far below half of 2^-24 */
+    uint32_t sig = man | 0x800000u;
+    int shift = 126 - (int)ex; /* >= 14 here */
+    if (shift >= 25)
+        return (uint16_t)sign; /* below or at half of the smallest subnormal: even = 0 */
+    uint32_t m = sig >> shift;
+    uint32_t rest = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rest > half || (rest == half && (m & 1u)))
+        m += 1u; /* m may reach 1024, which is the smallest normal: still correct */
+    return (uint16_t)(sign | m);
+}
+
+float oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+    uint32_t e = ((uint32_t)h >> 10) & 0x1Fu;
+    uint32_t m = (uint32_t)h & 0x3FFu;
+    float out;
+    if (e == 0) {
+        /* zero or subnormal: m * 2^-24, exact in fp32 */
+        out = (float)m * 5.9604644775390625e-08f;
+        if (sign)
+            out = -out;
+        return out;
+    }
+    uint32_t x;
+    if (e == 31)
+        x = sign | 0x7F800000u | (m << 13);
+    else
+        x = sign | ((e - 15 + 127) << 23) | (m << 13);
+    memcpy(&out, &x, 4);
+    return out;
+}
+
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    if ((x & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((x >> 16) | 0x40u); /* quiet nan */
+    uint32_t lsb = (x >> 16) & 1u;
+    x += 0x7FFFu + lsb;
+    return (uint16_t)(x >> 16);
+}
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t x = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &x, 4);
+    return f;
+}
+
+/* array forms, for the conversion pins */
+void oracle_f32_to_f16_array(const float *x, uint16_t *h, size_t n)
+{
+    for (size_t i = 0; i < n; i++)
+        h[i] = oracle_f32_to_f16(x[i]);
+}
+
+void oracle_f16_to_f32_array(const uint16_t *h, float *x, size_t n)
+{
+    for (size_t i = 0; i < n; i++)
+        x[i] = oracle_f16_to_f32(h[i]);
+}
+
+void oracle_f32_to_bf16_array(const float *x, uint16_t *h, size_t n)
+{
+    for (size_t i = 0; i < n; i++)
+        h[i] = oracle_f32_to_bf16(x[i]);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Walsh-Hadamard transform, unnormalised Sylvester ordering, in place.  Stage h pairs
+ * element j with j+h inside each block of 2h and writes (a+b, a-b), lower minus upper.
+ * H*H = d*I, so the inverse is H/d.  (TurboQuant on Quantized Models: topic list,
+ * Walsh-Hadamard transform; Statistical Inference ... TurboQuant: scheme KQV.)          */
+
+void oracle_fwht_f32(float *y, int d)
+{
+    for (int h = 1; h < d; h <<= 1)
+        for (int i = 0; i < d; i += 2 * h)
+            for (int j = i; j < i + h; j++) {
+                float a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+}
+
+void oracle_fwht_f64(double *y, int d)
+{
+    for (int h = 1; h < d; h <<= 1)
+        for (int i = 0; i < d; i += 2 * h)
+            for (int j = i; j < i + h; j++) {
+                double a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+}
+
+/* Stride-halving tree sum in fp32: for h = n/2, n/4, ..., 1: a[i] += a[i+h] (i < h).
+ * This fixed order is the one every fp32 sum of squares in the encoder and in the
+ * pruning ranking uses.  n must be a power of two; a is clobbered.                      */
+float oracle_tree_sum_f32(float *a, int n)
+{
+    for (int h = n / 2; h >= 1; h /= 2)
+        for (int i = 0; i < h; i++)
+            a[i] = a[i] + a[i + h];
+    return a[0];
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Lloyd-Max quantiser for N(0,1), symmetric, 2^bits levels, fp64.  Iterates the two
+ * Lloyd conditions (thresholds at midpoints, centroids at conditional means) on the
+ * positive half and mirrors it.  The conditional mean of N(0,1) on (a, b] is
+ * (phi(a) - phi(b)) / (Phi(b) - Phi(a)).  (Lloyd-Max codebook: TurboQuant on Quantized
+ * Models, topic list; the N(0,1) target follows from the Beta((d-1)/2,(d-1)/2) ->
+ * Gaussian marginal in Statistical Inference ... TurboQuant, "Theoretischer Rahmen".)
+ * Writes cent[L] ascending and thr[L-1] = midpoints.  Returns iterations used.          */
+
+static double npdf(double x) { return 0.39894228040143267794 * exp(-0.5 * x * x); }
+/* upper tail Q(x) = 1 - Phi(x), accurate for x >= 0 */
+static double nupper(double x) { return 0.5 * erfc(x * 0.70710678118654752440); }
+
+int oracle_lloyd_max_gaussian(int levels, double tol, int max_iter, double *cent, double *thr)
+{
+    int half = levels / 2;
+    double m[64], t[65];
+    for (int i = 0; i < half; i++)
+        m[i] = (i + 0.5) * (3.0 / half); /* spread over [0, 3] */
+    int it;
+    for (it = 0; it < max_iter; it++) {
+        t[0] = 0.0;
+        for (int i = 1; i < half; i++)
+            t[i] = 0.5 * (m[i - 1] + m[i]);
+        double delta = 0.0;
+        for (int i = 0; i < half; i++) {
+            double a = t[i];
+            double mass, num;
+            if (i + 1 < half) {
+                double b = t[i + 1];
+                mass = nupper(a) - nupper(b);
+                num = npdf(a) - npdf(b);
+            } else {
+                mass = nupper(a);
+                num = npdf(a);
+            }
+            double nm = num / mass;
+            double dd = fabs(nm - m[i]);
+            if (dd > delta)
+                delta = dd;
+            m[i] = nm;
+        }
+        if (delta < tol) {
+            it++;
+            break;
+        }
+    }
+    for (int i = 0; i < half; i++) {
+        cent[half + i] = m[i];
+        cent[half - 1 - i] = -m[i];
+    }
+    for (int i = 0; i + 1 < levels; i++)
+        thr[i] = 0.5 * (cent[i] + cent[i + 1]);
+    return it;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Cache geometry shared by all entry points below.  Buffers are whole-cache host arrays
+ * of U = batch * n_kv_heads units, indexed by absolute token position:
+ *   k_codes u32 [U][R][cap]       R = d/16 (2-bit) | d/8 (4-bit) | d/4 (8-bit): row r of
+ *                                 token t holds channels r*(32/b) .. ; channel
+ *                                 r*(32/b)+j sits in bits [b*j, b*j+b-1]
+ *   k_sz    u32 [U][d/32][cap]    asymmetric keys: low 16 bits fp16 scale, high fp16 zero
+ *   k_norm  u16 [U][cap]          Lloyd-Max keys: fp16 rho
+ *   k_ch0   u16 [U][cap]          protected channel 0: bf16
+ *   v_codes u32 [U][cap/2][d/4]   word j of token pair P: bits [4k,4k+3] = channel 4j+k of
+ *                                 token 2P, bits [16+4k, 16+4k+3] = same channel of 2P+1
+ *   v_sz    u32 [U][d/32][cap]    fp16 scale (low) / zero (high)
+ *   sink_k  u16 [U][n_sink][d]    bf16 key in stored coordinates (rotated if rotation on)
+ *   sink_v  u16 [U][n_sink][d]    bf16 value
+ * Slots t < n_sink of the quantised arrays are never written.                           */
+typedef struct {
+    int d, cap, n_sink, kfmt, rotate, ch0;
+    uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
+    uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
+    const float *cent, *thr; /* Lloyd-Max: 16 centroids, 15 thresholds (fp32) */
+} ocache;
+
+static size_t krows(const ocache *c) { return (size_t)(c->d * key_bits(c->kfmt) / 32); }
+
+/* Asymmetric INT-b quantisation of one group (Dual-QK sec. 3.3, "asymmetric INT2").
+ * Reading: scale = (max-min)/(2^b-1) and zero = min, both stored as fp16, and the codes
+ * are computed against the fp16-rounded values that decode will use; a group whose
+ * range is zero (or whose fp16 scale is zero) codes to all zeros.  skip0 drops element 0
+ * from the range estimate and codes it as 0 (channel-0 protection, Dual-QK sec. C.3).   */
+static void asym_group(const float *x, int n, int bits, int skip0, uint8_t *code,
+                       uint16_t *sh_out, uint16_t *zh_out)
+{
+    int qmax = (1 << bits) - 1;
+    int first = skip0 ? 1 : 0;
+    float mn = x[first], mx = x[first];
+    for (int i = first + 1; i < n; i++) {
+        if (x[i] < mn)
+            mn = x[i];
+        if (x[i] > mx)
+            mx = x[i];
+    }
+    float range = mx - mn;
+    float scale32 = range / (float)qmax;
+    uint16_t sh = oracle_f32_to_f16(scale32);
+    uint16_t zh = oracle_f32_to_f16(mn);
+    float sf = oracle_f16_to_f32(sh);
+    float zf = oracle_f16_to_f32(zh);
+    float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+    for (int i = 0; i < n; i++) {
+        if (i == 0 && skip0) {
+            code[i] = 0;
+            continue;
+        }
+        float diff = x[i] - zf;
+        float u = diff * inv;
+        float r = rintf(u);
+        if (r < 0.0f)
+            r = 0.0f;
+        if (r > (float)qmax)
+            r = (float)qmax;
+        code[i] = (uint8_t)r;
+    }
+    *sh_out = sh;
+    *zh_out = zh;
+}
+
+/* Quantise and store one token (K and V) at absolute position t of unit u.
+ * k and v are d fp32 values each.                                                        */
+static void quant_token(const ocache *c, size_t u, int t, const float *k, const float *v)
+{
+    const int d = c->d;
+    const size_t cap = (size_t)c->cap;
+    float y[256];
+    memcpy(y, k, sizeof(float) * (size_t)d);
+    if (c->rotate)
+        oracle_fwht_f32(y, d);
+
+    if (t < c->n_sink) {
+        /* Sink token: BF16 key (in stored coordinates) and BF16 value.
+         * (TurboQuant on Quantized Models: sink-token preservation.)                    */
+        uint16_t *sk = c->sink_k + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
+        uint16_t *sv = c->sink_v + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
+        for (int i = 0; i < d; i++) {
+            sk[i] = oracle_f32_to_bf16(y[i]);
+            sv[i] = oracle_f32_to_bf16(v[i]);
+        }
+        return;
+    }
+
+    uint8_t code[256];
+    const int kb = key_bits(c->kfmt);
+    if (c->kfmt == OK_LLOYD4) {
+        /* rho = RMS of the stored coordinates (= ||k|| when rotated), fp16; z = y / rho;
+         * code = number of thresholds strictly below z.                                  */
+        float sq[256];
+        for (int i = 0; i < d; i++)
+            sq[i] = y[i] * y[i];
+        float s2 = oracle_tree_sum_f32(sq, d);
+        float rho32 = sqrtf(s2 / (float)d);
+        uint16_t rh = oracle_f32_to_f16(rho32);
+        float rf = oracle_f16_to_f32(rh);
+        float inv = rf > 0.0f ? 1.0f / rf : 0.0f;
+        for (int i = 0; i < d; i++) {
+            float z = y[i] * inv;
+            int cnt = 0;
+            for (int j = 0; j < 15; j++)
+                if (z > c->thr[j])
+                    cnt++;
+            code[i] = (uint8_t)cnt;
+        }
+        c->k_norm[u * cap + (size_t)t] = rh;
+    } else {
+        for (int g = 0; g < d / 32; g++) {
+            uint16_t sh, zh;
+            asym_group(y + 32 * g, 32, kb, (g == 0 && c->ch0), code + 32 * g, &sh, &zh);
+            c->k_sz[(u * (size_t)(d / 32) + (size_t)g) * cap + (size_t)t] =
+                (uint32_t)sh | ((uint32_t)zh << 16);
+        }
+        if (c->ch0)
+            c->k_ch0[u * cap + (size_t)t] = oracle_f32_to_bf16(y[0]);
+    }
+    /* channel-major rows: row r holds 32/kb channels of this token */
+    const int per = 32 / kb;
+    const size_t R = krows(c);
+    for (size_t r = 0; r < R; r++) {
+        uint32_t w = 0;
+        for (int j = 0; j < per; j++)
+            w |= (uint32_t)code[(int)r * per + j] << (kb * j);
+        c->k_codes[(u * R + r) * cap + (size_t)t] = w;
+    }
+
+    /* values: asymmetric INT4 per 32-channel group, no channel exclusion */
+    uint8_t vc[256];
+    for (int g = 0; g < d / 32; g++) {
+        uint16_t sh, zh;
+        asym_group(v + 32 * g, 32, 4, 0, vc + 32 * g, &sh, &zh);
+        c->v_sz[(u * (size_t)(d / 32) + (size_t)g) * cap + (size_t)t] =
+            (uint32_t)sh | ((uint32_t)zh << 16);
+    }
+    const size_t W = (size_t)(d / 4);
+    uint32_t *pairrow = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * W;
+    const int sh16 = (t & 1) ? 16 : 0;
+    for (size_t j = 0; j < W; j++) {
+        uint32_t half = 0;
+        for (int k2 = 0; k2 < 4; k2++)
+            half |= (uint32_t)vc[4 * j + (size_t)k2] << (4 * k2);
+        pairrow[j] = (pairrow[j] & ~(0xFFFFu << sh16)) | (half << sh16);
+    }
+}
+
+/* Append n_new tokens per unit at positions [t0, t0+n_new) for units [0, n_units).
+ * k_new, v_new: fp32 [n_units][n_new][d].  OpenMP over units.                            */
+void oracle_quant_append(int d, int cap, int n_sink, int kfmt, int rotate, int ch0,
+                         uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
+                         uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
+                         const float *cent, const float *thr, int n_units, int t0, int n_new,
+                         const float *k_new, const float *v_new)
+{
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, k_codes, k_sz, v_codes, v_sz,
+                k_norm, k_ch0, sink_k, sink_v, cent, thr};
+#pragma omp parallel for schedule(static)
+    for (int u = 0; u < n_units; u++)
+        for (int i = 0; i < n_new; i++) {
+            size_t off = ((size_t)u * (size_t)n_new + (size_t)i) * (size_t)d;
+            quant_token(&c, (size_t)u, t0 + i, k_new + off, v_new + off);
+        }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Query-channel-group pruning mask (Dual-QK sec. 3.2 and sec. C.2): groups of 16
+ * channels of the stored key coordinates; energy of group p for head h is the fp32
+ * tree sum of qt^2 over its 16 channels; the group score sums the G heads of the GQA
+ * group in ascending head order; keep the m highest scores, ties to the lower index.
+ * qt: fp32 [G][d] query in stored coordinates.  m <= 0 or m >= d/16 keeps everything.
+ * Returns a bit mask, bit p = group p kept.                                              */
+uint32_t oracle_prune_mask(const float *qt, int G, int d, int m)
+{
+    const int P = d / 16;
+    uint32_t all = (P >= 32) ? 0xFFFFFFFFu : ((1u << P) - 1u);
+    if (m <= 0 || m >= P)
+        return all;
+    float E[16];
+    for (int p = 0; p < P; p++) {
+        float acc = 0.0f;
+        for (int h = 0; h < G; h++) {
+            float sq[16];
+            for (int i = 0; i < 16; i++) {
+                float qv = qt[(size_t)h * (size_t)d + (size_t)(16 * p + i)];
+                sq[i] = qv * qv;
+            }
+            float e = oracle_tree_sum_f32(sq, 16);
+            acc = (h == 0) ? e : acc + e;
+        }
+        E[p] = acc;
+    }
+    uint32_t mask = 0;
+    for (int p = 0; p < P; p++) {
+        int rank = 0;
+        for (int o = 0; o < P; o++)
+            if (E[o] > E[p] || (E[o] == E[p] && o < p))
+                rank++;
+        if (rank < m)
+            mask |= 1u << p;
+    }
+    return mask;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Decoding of stored tokens into fp64 (stored coordinates).                             */
+
+static void decode_key(const ocache *c, size_t u, int t, double *kh)
+{
+    const int d = c->d;
+    const size_t cap = (size_t)c->cap;
+    if (t < c->n_sink) {
+        const uint16_t *sk = c->sink_k + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
+        for (int i = 0; i < d; i++)
+            kh[i] = (double)oracle_bf16_to_f32(sk[i]);
+        return;
+    }
+    const int kb = key_bits(c->kfmt);
+    const int per = 32 / kb;
+    const size_t R = krows(c);
+    const uint32_t msk = (kb == 32) ? 0xFFFFFFFFu : ((1u << kb) - 1u);
+    int code[256];
+    for (size_t r = 0; r < R; r++) {
+        uint32_t w = c->k_codes[(u * R + r) * cap + (size_t)t];
+        for (int j = 0; j < per; j++)
+            code[(int)r * per + j] = (int)((w >> (kb * j)) & msk);
+    }
+    if (c->kfmt == OK_LLOYD4) {
+        double rf = (double)oracle_f16_to_f32(c->k_norm[u * cap + (size_t)t]);
+        for (int i = 0; i < d; i++)
+            kh[i] = rf * (double)c->cent[code[i]];
+        return;
+    }
+    for (int g = 0; g < d / 32; g++) {
+        uint32_t sz = c->k_sz[(u * (size_t)(d / 32) + (size_t)g) * cap + (size_t)t];
+        double sf = (double)oracle_f16_to_f32((uint16_t)(sz & 0xFFFFu));
+        double zf = (double)oracle_f16_to_f32((uint16_t)(sz >> 16));
+        for (int i = 0; i < 32; i++)
+            kh[32 * g + i] = (double)code[32 * g + i] * sf + zf;
+    }
+    if (c->ch0)
+        kh[0] = (double)oracle_bf16_to_f32(c->k_ch0[u * cap + (size_t)t]);
+}
+
+static void decode_value(const ocache *c, size_t u, int t, double *vh)
+{
+    const int d = c->d;
+    const size_t cap = (size_t)c->cap;
+    if (t < c->n_sink) {
+        const uint16_t *sv = c->sink_v + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
+        for (int i = 0; i < d; i++)
+            vh[i] = (double)oracle_bf16_to_f32(sv[i]);
+        return;
+    }
+    const size_t W = (size_t)(d / 4);
+    const uint32_t *pairrow = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * W;
+    const int sh16 = (t & 1) ? 16 : 0;
+    for (int g = 0; g < d / 32; g++) {
+        uint32_t sz = c->v_sz[(u * (size_t)(d / 32) + (size_t)g) * cap + (size_t)t];
+        double sf = (double)oracle_f16_to_f32((uint16_t)(sz & 0xFFFFu));
+        double zf = (double)oracle_f16_to_f32((uint16_t)(sz >> 16));
+        for (int i = 32 * g; i < 32 * g + 32; i++) {
+            uint32_t w = pairrow[i / 4] >> sh16;
+            int cd = (int)((w >> (4 * (i % 4))) & 0xFu);
+            vh[i] = (double)cd * sf + zf;
+        }
+    }
+}
+
+/* Decoded cache of one unit, for tests: keys in stored coordinates, values. [len][d]. */
+void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int ch0,
+                         uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
+                         uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
+                         const float *cent, int unit, int len, double *kh, double *vh)
+{
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, k_codes, k_sz, v_codes, v_sz,
+                k_norm, k_ch0, sink_k, sink_v, cent, 0};
+    for (int t = 0; t < len; t++) {
+        decode_key(&c, (size_t)unit, t, kh + (size_t)t * (size_t)d);
+        decode_value(&c, (size_t)unit, t, vh + (size_t)t * (size_t)d);
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Decode attention for units [0, n_units) (OpenMP over units).
+ * q: fp32 [n_units][G][d] raw query (G = query heads of the unit's GQA group; query head
+ *    h of a sequence reads KV head floor(h/G), so the G rows of a unit are consecutive).
+ * For each head: logits l_t = sm * sum_{c kept} qs_c * k^_{t,c} / d_rot over t in [0, len),
+ * where qs is the query in stored coordinates (FWHT(q) when keys are rotated, then
+ * d_rot = d; otherwise qs = q and d_rot = 1), k^ the decoded stored key; p = softmax(l);
+ * out = sum_t p_t v^_t.  All in fp64, two passes (max, then exp and sums).
+ * The mask is computed from the fp32 stored-coordinate query (oracle_prune_mask) and
+ * written to mask_out[u] when mask_out is not null.  logits_out (nullable) receives the
+ * fp64 logits [n_units][G][len].                                                         */
+void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch0,
+                        uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
+                        uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
+                        const float *cent, int n_units, int len, int G, const float *q,
+                        double sm, int keep_groups, double *out, uint8_t *mask_out,
+                        double *logits_out)
+{
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, k_codes, k_sz, v_codes, v_sz,
+                k_norm, k_ch0, sink_k, sink_v, cent, 0};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < n_units; u++) {
+        const float *qu = q + (size_t)u * (size_t)G * (size_t)d;
+        /* fp32 stored-coordinate query for the mask */
+        float *qt32 = (float *)malloc(sizeof(float) * (size_t)G * (size_t)d);
+        double *qs = (double *)malloc(sizeof(double) * (size_t)G * (size_t)d);
+        double *lg = (double *)malloc(sizeof(double) * (size_t)G * (size_t)(len > 0 ? len : 1));
+        double kh[256], vh[256];
+        for (int h = 0; h < G; h++) {
+            memcpy(qt32 + (size_t)h * (size_t)d, qu + (size_t)h * (size_t)d, sizeof(float) * (size_t)d);
+            if (rotate)
+                oracle_fwht_f32(qt32 + (size_t)h * (size_t)d, d);
+            for (int i = 0; i < d; i++)
+                qs[(size_t)h * (size_t)d + (size_t)i] = (double)qu[(size_t)h * (size_t)d + (size_t)i];
+            if (rotate)
+                oracle_fwht_f64(qs + (size_t)h * (size_t)d, d);
+        }
+        uint32_t mask = oracle_prune_mask(qt32, G, d, keep_groups);
+        if (mask_out)
+            mask_out[u] = (uint8_t)mask;
+        const double scale = sm / (rotate ? (double)d : 1.0);
+        /* pass 1: logits */
+        for (int t = 0; t < len; t++) {
+            decode_key(&c, (size_t)u, t, kh);
+            for (int h = 0; h < G; h++) {
+                double s = 0.0;
+                for (int i = 0; i < d; i++)
+                    if (mask & (1u << (i / 16)))
+                        s += qs[(size_t)h * (size_t)d + (size_t)i] * kh[i];
+                lg[(size_t)h * (size_t)len + (size_t)t] = scale * s;
+            }
+        }
+        if (logits_out)
+            memcpy(logits_out + (size_t)u * (size_t)G * (size_t)len, lg,
+                   sizeof(double) * (size_t)G * (size_t)len);
+        /* pass 2: softmax-weighted values */
+        double mx[64], den[64];
+        for (int h = 0; h < G; h++) {
+            mx[h] = -INFINITY;
+            for (int t = 0; t < len; t++)
+                if (lg[(size_t)h * (size_t)len + (size_t)t] > mx[h])
+                    mx[h] = lg[(size_t)h * (size_t)len + (size_t)t];
+            den[h] = 0.0;
+        }
+        double *o = out + (size_t)u * (size_t)G * (size_t)d;
+        for (size_t i = 0; i < (size_t)G * (size_t)d; i++)
+            o[i] = 0.0;
+        for (int t = 0; t < len; t++) {
+            decode_value(&c, (size_t)u, t, vh);
+            for (int h = 0; h < G; h++) {
+                double p = exp(lg[(size_t)h * (size_t)len + (size_t)t] - mx[h]);
+                den[h] += p;
+                for (int i = 0; i < d; i++)
+                    o[(size_t)h * (size_t)d + (size_t)i] += p * vh[i];
+            }
+        }
+        for (int h = 0; h < G; h++)
+            for (int i = 0; i < d; i++)
+                o[(size_t)h * (size_t)d + (size_t)i] = len > 0 ? o[(size_t)h * (size_t)d + (size_t)i] / den[h] : 0.0;
+        free(qt32);
+        free(qs);
+        free(lg);
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
