@@ -1,0 +1,166 @@
+"""ctypes binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every step of the quantized-KV path runs in the HIP kernels of libkvq.so; this module
+only fills the C descriptor from torch tensors (device memory) and passes torch's current
+HIP stream.  If the library is missing the import fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY = 0, -1, -2, -3
+KVQ_ERR_WORKSPACE, KVQ_ERR_ALIGN, KVQ_ERR_HIP = -4, -5, -6
+KVQ_F32, KVQ_BF16 = 0, 1
+K_ASYM2, K_ASYM4, K_LLOYD4 = 0, 1, 2
+BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", "sink_v",
+             "codebook", "thresholds"]
+EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
+           "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles",
+           "kvq_status_string"]
+
+
+class KvqCacheC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink",
+                                              "k_format", "k_hadamard", "k_ch0_bf16", "len")] + \
+               [(n, ctypes.c_void_p) for n in BUF_NAMES]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libkvq.so not built at {LIB_PATH}; run python -m bit_kv_cache_kvq_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cp = ctypes.POINTER(KvqCacheC)
+        L.kvq_buffer_bytes.restype = sz
+        L.kvq_buffer_bytes.argtypes = [cp, i32]
+        L.kvq_validate.restype = i32
+        L.kvq_validate.argtypes = [cp]
+        L.kvq_quant_append.restype = i32
+        L.kvq_quant_append.argtypes = [cp, P, P, i32, i32, P]
+        L.kvq_decode_workspace_bytes.restype = sz
+        L.kvq_decode_workspace_bytes.argtypes = [cp, i32]
+        L.kvq_decode_attn.restype = i32
+        L.kvq_decode_attn.argtypes = [cp, P, i32, i32, ctypes.c_float, i32, P, P, P, sz, P]
+        L.kvq_decode_splits.restype = i32
+        L.kvq_decode_splits.argtypes = [cp, i32]
+        L.kvq_codebook_gaussian.restype = i32
+        L.kvq_codebook_gaussian.argtypes = [i32, P, P]
+        L.kvq_set_split_tiles.restype = None
+        L.kvq_set_split_tiles.argtypes = [i32]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_status_string.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().kvq_status_string(int(s)).decode()
+
+
+def codebook_gaussian(bits: int = 4):
+    """Library's own Lloyd-Max codebook (host fp32): (centroids, thresholds) as lists."""
+    n = 1 << bits
+    c = (ctypes.c_float * n)()
+    t = (ctypes.c_float * (n - 1))()
+    st = lib().kvq_codebook_gaussian(bits, ctypes.cast(c, ctypes.c_void_p), ctypes.cast(t, ctypes.c_void_p))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_codebook_gaussian")
+    return list(c), list(t)
+
+
+def set_split_tiles(n: int) -> None:
+    lib().kvq_set_split_tiles(int(n))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Cache:
+    """A quantized KV cache whose buffers are torch device tensors (zero-initialised)."""
+
+    def __init__(self, batch, n_kv_heads, head_dim, capacity, n_sink=0, k_format=K_ASYM2,
+                 k_hadamard=0, k_ch0_bf16=0, device="cuda"):
+        self.c = KvqCacheC(batch, n_kv_heads, head_dim, capacity, n_sink, k_format, k_hadamard,
+                           k_ch0_bf16, 0)
+        self.device = torch.device(device)
+        self.buffers = {}
+        for i, name in enumerate(BUF_NAMES):
+            nbytes = int(lib().kvq_buffer_bytes(ctypes.byref(self.c), i))
+            if nbytes == 0:
+                continue
+            t = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self.buffers[name] = t
+            setattr(self.c, name, t.data_ptr())
+        if k_format == K_LLOYD4:
+            cent, thr = codebook_gaussian(4)
+            self.buffers["codebook"].view(torch.float32).copy_(torch.tensor(cent, dtype=torch.float32))
+            self.buffers["thresholds"].view(torch.float32).copy_(torch.tensor(thr, dtype=torch.float32))
+        st = lib().kvq_validate(ctypes.byref(self.c))
+        if st != KVQ_OK:
+            raise KvqError(st, "kvq_validate")
+        self._ws = {}
+
+    @property
+    def len(self) -> int:
+        return int(self.c.len)
+
+    def view(self, name, dtype):
+        return self.buffers[name].view(dtype)
+
+    def append(self, k, v, stream=None):
+        """k, v: [batch, n_kv_heads, n_new, head_dim] fp32 or bf16 contiguous device tensors."""
+        assert k.shape == v.shape and k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
+        assert k.shape[0] == self.c.batch and k.shape[1] == self.c.n_kv_heads and k.shape[3] == self.c.head_dim
+        dt = KVQ_BF16 if k.dtype == torch.bfloat16 else KVQ_F32
+        st = lib().kvq_quant_append(ctypes.byref(self.c), _ptr(k), _ptr(v), dt, int(k.shape[2]), _stream(stream))
+        if st != KVQ_OK:
+            raise KvqError(st, "kvq_quant_append")
+
+    def workspace(self, n_q_heads):
+        if n_q_heads not in self._ws:
+            nbytes = int(lib().kvq_decode_workspace_bytes(ctypes.byref(self.c), n_q_heads))
+            self._ws[n_q_heads] = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        return self._ws[n_q_heads]
+
+    def decode(self, q, sm_scale, keep_groups=0, out=None, mask_out=None, stream=None):
+        """q: [batch, n_q_heads, head_dim] fp32/bf16.  Returns (out fp32, mask uint8)."""
+        assert q.is_contiguous() and q.shape[0] == self.c.batch and q.shape[2] == self.c.head_dim
+        hq = int(q.shape[1])
+        if out is None:
+            out = torch.empty(q.shape[0], hq, q.shape[2], dtype=torch.float32, device=q.device)
+        if mask_out is None:
+            mask_out = torch.zeros(self.c.batch * self.c.n_kv_heads, dtype=torch.uint8, device=q.device)
+        ws = self.workspace(hq)
+        dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
+        st = lib().kvq_decode_attn(ctypes.byref(self.c), _ptr(q), dt, hq, float(sm_scale), int(keep_groups),
+                                   _ptr(out), _ptr(mask_out), _ptr(ws), ws.numel(), _stream(stream))
+        if st != KVQ_OK:
+            raise KvqError(st, "kvq_decode_attn")
+        return out, mask_out
+
+    def splits(self, n_q_heads) -> int:
+        return int(lib().kvq_decode_splits(ctypes.byref(self.c), n_q_heads))

@@ -1,0 +1,328 @@
+// kvq_api.cpp -- the C ABI of libkvq: host-side validation, buffer sizing, split planning
+// and kernel launches.  Everything here runs on the host; validation happens before any
+// HIP call, so every error path except KVQ_ERR_HIP leaves the cache untouched.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+std::atomic<int> g_split_tiles{0};
+
+int key_bits(int kfmt) { return kfmt == KVQ_K_ASYM2 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+kvq_status check_geometry(const kvq_cache *c)
+{
+    if (!c)
+        return KVQ_ERR_ARG;
+    if (c->batch <= 0 || c->n_kv_heads <= 0 || c->capacity <= 0 || c->len < 0)
+        return KVQ_ERR_ARG;
+    if ((long long)c->batch * c->n_kv_heads > 65535)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->capacity % kTile != 0)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->n_sink < 0 || c->n_sink > kMaxSink || c->n_sink >= c->capacity)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->k_format < KVQ_K_ASYM2 || c->k_format > KVQ_K_LLOYD4)
+        return KVQ_ERR_ARG;
+    if ((c->k_hadamard != 0 && c->k_hadamard != 1) || (c->k_ch0_bf16 != 0 && c->k_ch0_bf16 != 1))
+        return KVQ_ERR_ARG;
+    if (c->k_ch0_bf16 && (c->k_hadamard || c->k_format == KVQ_K_LLOYD4))
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->len > c->capacity)
+        return KVQ_ERR_CAPACITY;
+    return KVQ_OK;
+}
+
+size_t units_of(const kvq_cache *c) { return (size_t)c->batch * (size_t)c->n_kv_heads; }
+
+size_t buffer_bytes(const kvq_cache *c, int which)
+{
+    const size_t U = units_of(c), d = (size_t)c->head_dim, cap = (size_t)c->capacity;
+    const size_t ns = (size_t)c->n_sink;
+    const bool lloyd = c->k_format == KVQ_K_LLOYD4;
+    switch (which) {
+    case KVQ_BUF_K_CODES: return U * (d * (size_t)key_bits(c->k_format) / 32) * cap * 4;
+    case KVQ_BUF_K_SZ: return lloyd ? 0 : U * (d / 32) * cap * 4;
+    case KVQ_BUF_K_NORM: return lloyd ? U * cap * 2 : 0;
+    case KVQ_BUF_K_CH0: return c->k_ch0_bf16 ? U * cap * 2 : 0;
+    case KVQ_BUF_V_CODES: return U * (cap / 2) * (d / 4) * 4;
+    case KVQ_BUF_V_SZ: return U * (d / 32) * cap * 4;
+    case KVQ_BUF_SINK_K:
+    case KVQ_BUF_SINK_V: return U * ns * d * 2;
+    case KVQ_BUF_CODEBOOK: return lloyd ? 16 * 4 : 0;
+    case KVQ_BUF_THRESHOLDS: return lloyd ? 15 * 4 : 0;
+    default: return 0;
+    }
+}
+
+kvq_status check_buffers(const kvq_cache *c)
+{
+    const void *ptrs[10] = {c->k_codes, c->k_sz, c->k_norm, c->k_ch0, c->v_codes,
+                            c->v_sz, c->sink_k, c->sink_v, c->codebook, c->thresholds};
+    for (int i = 0; i < 10; i++) {
+        if (buffer_bytes(c, i) == 0)
+            continue;
+        if (!ptrs[i])
+            return KVQ_ERR_ARG;
+        if (!aligned16(ptrs[i]))
+            return KVQ_ERR_ALIGN;
+    }
+    return KVQ_OK;
+}
+
+struct Plan {
+    int tile_begin, tile_end, n_tiles, n_split, tiles_per_split;
+};
+
+// Split planner: enough workgroups to fill 256 CUs several times over while keeping at
+// least one 256-position tile per wave where the context allows it.
+Plan plan_splits(const kvq_cache *c, int len)
+{
+    Plan pl;
+    const int n_sink = c->n_sink < len ? c->n_sink : len;
+    pl.tile_begin = n_sink / kTile;
+    pl.tile_end = (len + kTile - 1) / kTile;
+    if (len <= n_sink)
+        pl.tile_end = pl.tile_begin; // only sink positions
+    pl.n_tiles = pl.tile_end - pl.tile_begin;
+    if (pl.n_tiles <= 0) {
+        pl.n_split = 1;
+        pl.tiles_per_split = 0;
+        return pl;
+    }
+    const long long units = (long long)units_of(c);
+    int tps = g_split_tiles.load();
+    if (tps <= 0) {
+        const long long target_blocks = 2048; // 8 per CU
+        long long want_split = (target_blocks + units - 1) / units;
+        long long by_tiles = (pl.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock; // >= 4 tiles per split
+        if (want_split > by_tiles)
+            want_split = by_tiles;
+        if (want_split < 1)
+            want_split = 1;
+        tps = (int)((pl.n_tiles + want_split - 1) / want_split);
+    }
+    if (tps > pl.n_tiles)
+        tps = pl.n_tiles;
+    pl.tiles_per_split = tps;
+    pl.n_split = (pl.n_tiles + tps - 1) / tps;
+    return pl;
+}
+
+int max_splits(const kvq_cache *c)
+{
+    // the planner never exceeds one split per tile of the full capacity
+    return c->capacity / kTile;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *kvq_status_string(kvq_status s)
+{
+    switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KVQ_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+size_t kvq_buffer_bytes(const kvq_cache *c, int32_t which)
+{
+    if (check_geometry(c) != KVQ_OK)
+        return 0;
+    return buffer_bytes(c, which);
+}
+
+kvq_status kvq_validate(const kvq_cache *c)
+{
+    kvq_status st = check_geometry(c);
+    if (st != KVQ_OK)
+        return st;
+    return check_buffers(c);
+}
+
+kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, int32_t dtype,
+                            int32_t n_new, void *stream)
+{
+    kvq_status st = kvq_validate(c);
+    if (st != KVQ_OK)
+        return st;
+    if (n_new < 0 || (dtype != KVQ_F32 && dtype != KVQ_BF16))
+        return KVQ_ERR_ARG;
+    if (n_new == 0)
+        return KVQ_OK;
+    if (!k_new || !v_new)
+        return KVQ_ERR_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return KVQ_ERR_ALIGN;
+    if ((long long)c->len + n_new > c->capacity)
+        return KVQ_ERR_CAPACITY;
+    AppendParams p;
+    p.k_codes = c->k_codes;
+    p.k_sz = c->k_sz;
+    p.v_codes = c->v_codes;
+    p.v_sz = c->v_sz;
+    p.k_norm = c->k_norm;
+    p.k_ch0 = c->k_ch0;
+    p.sink_k = c->sink_k;
+    p.sink_v = c->sink_v;
+    p.thresholds = c->thresholds;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.units = (int)units_of(c);
+    p.n_new = n_new;
+    p.cap = c->capacity;
+    p.len = c->len;
+    p.n_sink = c->n_sink;
+    p.kfmt = c->k_format;
+    p.rotate = c->k_hadamard;
+    p.ch0 = c->k_ch0_bf16;
+    p.in_bf16 = dtype == KVQ_BF16;
+    if (launch_append(c->head_dim, p, (hipStream_t)stream) != hipSuccess)
+        return KVQ_ERR_HIP;
+    c->len += n_new;
+    return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
+{
+    if (check_geometry(c) != KVQ_OK || n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+        return 0;
+    const size_t U = units_of(c);
+    const size_t G = (size_t)(n_q_heads / c->n_kv_heads);
+    const size_t part = U * (size_t)max_splits(c) * G * (size_t)(c->head_dim + 2) * sizeof(float);
+    const size_t part_aligned = (part + 255) & ~(size_t)255;
+    return part_aligned + ((U * sizeof(uint32_t) + 255) & ~(size_t)255);
+}
+
+int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
+{
+    (void)n_q_heads;
+    if (check_geometry(c) != KVQ_OK)
+        return 0;
+    return plan_splits(c, c->len).n_split;
+}
+
+kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
+                           float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
+                           void *ws, size_t ws_bytes, void *stream)
+{
+    kvq_status st = kvq_validate(c);
+    if (st != KVQ_OK)
+        return st;
+    if (!q || !out || (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16))
+        return KVQ_ERR_ARG;
+    if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+        return KVQ_ERR_ARG;
+    const int G = n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return KVQ_ERR_UNSUPPORTED;
+    if (keep_groups < 0 || !isfinite(sm_scale))
+        return KVQ_ERR_ARG;
+    if (!aligned16(q) || !aligned16(out))
+        return KVQ_ERR_ALIGN;
+    const size_t need = kvq_decode_workspace_bytes(c, n_q_heads);
+    if (!ws || ws_bytes < need)
+        return KVQ_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return KVQ_ERR_ALIGN;
+
+    const Plan pl = plan_splits(c, c->len);
+    const size_t U = units_of(c);
+    const size_t part = U * (size_t)max_splits(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float);
+    DecodeParams p;
+    p.k_codes = c->k_codes;
+    p.k_sz = c->k_sz;
+    p.v_codes = c->v_codes;
+    p.v_sz = c->v_sz;
+    p.k_norm = c->k_norm;
+    p.k_ch0 = c->k_ch0;
+    p.sink_k = c->sink_k;
+    p.sink_v = c->sink_v;
+    p.codebook = c->codebook;
+    p.q = q;
+    p.out = out;
+    p.mask_out = mask_out;
+    p.part = static_cast<float *>(ws);
+    p.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + ((part + 255) & ~(size_t)255));
+    p.n_kv_heads = c->n_kv_heads;
+    p.cap = c->capacity;
+    p.len = c->len;
+    p.n_sink = c->n_sink;
+    p.rotate = c->k_hadamard;
+    p.ch0 = c->k_ch0_bf16;
+    p.keep = keep_groups;
+    p.q_bf16 = q_dtype == KVQ_BF16;
+    p.sm_log2e = sm_scale * 1.4426950408889634f;
+    p.n_split = pl.n_split;
+    p.tile_begin = pl.tile_begin;
+    p.tile_end = pl.tile_end;
+    p.tiles_per_split = pl.tiles_per_split;
+    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, (hipStream_t)stream) != hipSuccess)
+        return KVQ_ERR_HIP;
+    return KVQ_OK;
+}
+
+void kvq_set_split_tiles(int32_t tiles_per_split) { g_split_tiles.store(tiles_per_split > 0 ? tiles_per_split : 0); }
+
+// Symmetric Lloyd-Max quantiser for N(0,1): iterate centroid = conditional mean of the
+// cell and threshold = midpoint on the positive half, then mirror.  Conditional mean of
+// N(0,1) on (a, b]: (pdf(a) - pdf(b)) / (Q(a) - Q(b)) with Q the upper tail.
+kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *thresholds)
+{
+    if (bits < 1 || bits > 6 || !centroids || !thresholds)
+        return KVQ_ERR_ARG;
+    const int L = 1 << bits, H = L / 2;
+    double pos[32], edge[33];
+    for (int i = 0; i < H; i++)
+        pos[i] = 3.0 * (i + 0.5) / H;
+    auto pdf = [](double x) { return exp(-0.5 * x * x) / sqrt(2.0 * M_PI); };
+    auto upper = [](double x) { return 0.5 * erfc(x / sqrt(2.0)); };
+    for (int iter = 0; iter < 200000; iter++) {
+        edge[0] = 0.0;
+        for (int i = 1; i < H; i++)
+            edge[i] = 0.5 * (pos[i - 1] + pos[i]);
+        double worst = 0.0;
+        for (int i = 0; i < H; i++) {
+            const double a = edge[i];
+            const bool last = (i == H - 1);
+            const double num = last ? pdf(a) : pdf(a) - pdf(edge[i + 1]);
+            const double den = last ? upper(a) : upper(a) - upper(edge[i + 1]);
+            const double next = num / den;
+            worst = fmax(worst, fabs(next - pos[i]));
+            pos[i] = next;
+        }
+        if (worst < 1e-13)
+            break;
+    }
+    double full[64];
+    for (int i = 0; i < H; i++) {
+        full[H + i] = pos[i];
+        full[H - 1 - i] = -pos[i];
+    }
+    for (int i = 0; i < L; i++)
+        centroids[i] = (float)full[i];
+    for (int i = 0; i + 1 < L; i++)
+        thresholds[i] = (float)(0.5 * (full[i] + full[i + 1]));
+    return KVQ_OK;
+}
+
+} // extern "C"

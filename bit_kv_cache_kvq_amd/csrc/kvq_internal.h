@@ -1,0 +1,45 @@
+// kvq_internal.h -- launcher interface between the C ABI (kvq_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+
+// Decode tile: positions scored by one wave per pass (64 lanes x 4 positions).
+constexpr int kTile = 256;
+constexpr int kMaxSink = 64;
+
+struct AppendParams {
+    uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
+    uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
+    const float *thresholds;
+    const void *k_new, *v_new;
+    int units, n_new, cap, len, n_sink, kfmt, rotate, ch0, in_bf16;
+};
+
+struct DecodeParams {
+    const uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
+    const uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
+    const float *codebook;
+    const void *q;
+    float *out;
+    uint8_t *mask_out;
+    float *part;        // split partials [U][n_split][G][D + 2]
+    uint32_t *counters; // [U], zero between calls
+    int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
+    float sm_log2e;      // softmax scale times log2(e)
+    int n_split, tile_begin, tile_end, tiles_per_split;
+};
+
+hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
+hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
+                         hipStream_t s);
+
+} // namespace kvq

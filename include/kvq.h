@@ -1,0 +1,178 @@
+/*
+ * kvq.h -- C ABI of libkvq: low-bit quantized KV-cache append and decode attention on
+ * AMD MI355X (gfx950).
+ *
+ * The method (sources are the pages this library implements; sections as they name them):
+ *   - Keys: optionally Walsh-Hadamard-rotated, then either asymmetric INT2/INT4 with an
+ *     FP16 scale and zero per 32-channel group, channel 0 optionally kept in BF16 and left
+ *     out of the range estimate (Dual-QK: Sharp Queries and Flat Keys for Prunable 2-bit
+ *     KV Caches, sec. 3.3 and C.3), or 4-bit codes of an N(0,1) Lloyd-Max codebook with an
+ *     FP16 per-vector norm (TurboQuant on Quantized Models: abstract and topic list;
+ *     Statistical Inference and Quality Measures of KV Cache Quantisations Inspired by
+ *     TurboQuant: scheme KQV and the Beta -> Gaussian marginal).
+ *   - Keys stored channel-major so decode reads only the channel rows it keeps
+ *     (Dual-QK sec. 3.3).
+ *   - Values: asymmetric INT4, FP16 scale and zero per 32-channel group.
+ *   - The first n_sink positions of every sequence are stored in BF16 (TurboQuant on
+ *     Quantized Models, abstract: sink-token preservation; Dual-QK sec. 3.3 / 4.1).
+ *   - Decode scores queries straight against the packed codes (TurboQuant on Quantized
+ *     Models, abstract: fused scoring without key decompression), with optional dynamic
+ *     query-channel-group pruning: one mask per GQA group keeping the m 16-channel groups
+ *     of largest query energy summed over the group's heads (Dual-QK sec. 3.2, C.2,
+ *     App. A), and one softmax over all positions (Dual-QK sec. 3.4).
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers owned by the caller unless stated otherwise.
+ *     The library never allocates device memory and never synchronizes; all work is
+ *     enqueued on the caller's stream (`stream` is a hipStream_t, NULL = null stream).
+ *   - Arguments are validated on the host before anything is enqueued; on any error code
+ *     other than KVQ_ERR_HIP nothing was launched and the cache is unchanged.
+ *   - Calls on distinct caches are thread-safe; calls on one cache must be ordered.
+ *
+ * Packed layout (U = batch * n_kv_heads units; unit u = b * n_kv_heads + kv_head; every
+ * array is indexed by absolute token position t in [0, capacity)):
+ *   k_codes  u32 [U][R][capacity]  R = head_dim/16 (INT2) or head_dim/8 (4-bit).  Word
+ *                                  (r, t) holds channels r*(32/b) .. r*(32/b)+32/b-1 of
+ *                                  token t, channel r*(32/b)+j in bits [b*j, b*j+b-1].
+ *   k_sz     u32 [U][head_dim/32][capacity]  asymmetric keys: fp16 scale in bits 0-15,
+ *                                  fp16 zero (the group minimum) in bits 16-31.
+ *   k_norm   u16 [U][capacity]     Lloyd-Max keys: fp16 norm rho (RMS of the stored
+ *                                  coordinates; equals ||k|| when rotated).
+ *   k_ch0    u16 [U][capacity]     protected channel 0: bf16.
+ *   v_codes  u32 [U][capacity/2][head_dim/4]  word j of token pair P holds channels
+ *                                  4j..4j+3: token 2P in bits 0-15, token 2P+1 in bits
+ *                                  16-31, channel 4j+k at nibble k of its half.
+ *   v_sz     u32 [U][head_dim/32][capacity]  values: fp16 scale | fp16 zero << 16.
+ *   sink_k   u16 [U][n_sink][head_dim]  bf16 keys of positions < n_sink, in stored
+ *                                  coordinates (rotated when k_hadamard = 1).
+ *   sink_v   u16 [U][n_sink][head_dim]  bf16 values of positions < n_sink.
+ *   codebook f32 [16], thresholds f32 [15]  Lloyd-Max keys: centroids ascending and the
+ *                                  decision thresholds; a rotated coordinate z codes to the
+ *                                  number of thresholds strictly below z.
+ * Quantized arrays are never written or read at positions t < n_sink.
+ * Encoding arithmetic is fixed (fp32, IEEE round-to-nearest-even, no contraction) so the
+ * packed bytes are reproducible bit for bit:
+ *   asym b-bit group: scale = fp16((max - min) / (2^b - 1)), zero = fp16(min), with
+ *   channel 0 excluded from min/max when protected; code = clamp(rint((x - zero) *
+ *   (scale > 0 ? 1/scale : 0)), 0, 2^b - 1) using the fp16-rounded scale and zero.
+ *   Lloyd-Max: y = FWHT(k) (unnormalised, stages h = 1, 2, 4, ... writing (a+b, a-b)) when
+ *   rotated, else y = k; rho = fp16(sqrt(tree_sum(y*y) / d)) with the stride-halving
+ *   tree; z = y * (rho > 0 ? 1/rho : 0).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_ARG = -1,         /* null pointer, bad size or out-of-range argument       */
+    KVQ_ERR_UNSUPPORTED = -2, /* valid but unsupported combination (e.g. head_dim 96)   */
+    KVQ_ERR_CAPACITY = -3,    /* len + n_new > capacity                                 */
+    KVQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required             */
+    KVQ_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                       */
+    KVQ_ERR_HIP = -6          /* a kernel launch failed; appended range is undefined    */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+typedef enum { KVQ_K_ASYM2 = 0, KVQ_K_ASYM4 = 1, KVQ_K_LLOYD4 = 2 } kvq_kfmt;
+
+/* Cache descriptor.  Geometry and format fields are set once by the caller; `len` is the
+ * number of positions stored per sequence (uniform across sequences) and is advanced by
+ * kvq_quant_append.  Constraints: head_dim in {64, 128}; capacity a positive multiple of
+ * 256; 0 <= n_sink <= 64 and n_sink < capacity; k_hadamard and k_ch0_bf16 in {0, 1};
+ * k_ch0_bf16 requires an asymmetric key format and k_hadamard = 0.  Pointers unused by
+ * the chosen format may be NULL (see kvq_buffer_bytes).                                 */
+typedef struct kvq_cache {
+    int32_t batch, n_kv_heads, head_dim, capacity, n_sink;
+    int32_t k_format, k_hadamard, k_ch0_bf16;
+    int32_t len;
+    uint32_t *k_codes;
+    uint32_t *k_sz;
+    uint16_t *k_norm;
+    uint16_t *k_ch0;
+    uint32_t *v_codes;
+    uint32_t *v_sz;
+    uint16_t *sink_k;
+    uint16_t *sink_v;
+    const float *codebook;
+    const float *thresholds;
+} kvq_cache;
+
+enum {
+    KVQ_BUF_K_CODES = 0,
+    KVQ_BUF_K_SZ = 1,
+    KVQ_BUF_K_NORM = 2,
+    KVQ_BUF_K_CH0 = 3,
+    KVQ_BUF_V_CODES = 4,
+    KVQ_BUF_V_SZ = 5,
+    KVQ_BUF_SINK_K = 6,
+    KVQ_BUF_SINK_V = 7,
+    KVQ_BUF_CODEBOOK = 8,
+    KVQ_BUF_THRESHOLDS = 9
+};
+
+/* Bytes the caller must allocate for buffer `which` (KVQ_BUF_*) of this geometry; 0 when
+ * the format does not use that buffer or the geometry is invalid.  Host-only, no HIP.    */
+size_t kvq_buffer_bytes(const kvq_cache *c, int32_t which);
+
+/* Host-side check of a descriptor (geometry, format flags, pointers and their 16-byte
+ * alignment, 0 <= len <= capacity).  Returns KVQ_OK or the first error found.             */
+kvq_status kvq_validate(const kvq_cache *c);
+
+/* Append n_new tokens to every sequence: quantize and pack k_new / v_new
+ * ([batch][n_kv_heads][n_new][head_dim], dtype KVQ_F32 or KVQ_BF16, row-major, device)
+ * into positions [len, len + n_new), then set len += n_new.  Only those positions are
+ * written (O(1) work per appended token; TurboQuant on Quantized Models, abstract:
+ * incremental cache).  Positions below n_sink go to sink_k / sink_v in BF16.  Inputs must
+ * be finite with |x| < 65504 so the fp16 parameters stay finite; other inputs give
+ * unspecified codes.  n_new = 0 is a no-op.                                               */
+kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, int32_t dtype,
+                            int32_t n_new, void *stream);
+
+/* Workspace bytes kvq_decode_attn needs for this cache geometry (any len up to capacity)
+ * and n_q_heads.  The workspace holds split partials and one counter word per unit; it
+ * must be zero-filled once before its first use and is left zeroed by every call.        */
+size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
+
+/* Decode attention for one query step per sequence over positions [0, len).
+ *   q        [batch][n_q_heads][head_dim], KVQ_F32 or KVQ_BF16, device.  n_q_heads must be
+ *            a multiple of n_kv_heads with G = n_q_heads / n_kv_heads in {1, 2, 4, 8};
+ *            query head h reads KV head floor(h / G).
+ *   sm_scale softmax scale applied to q.k (1/sqrt(head_dim) for standard attention).
+ *   keep_groups  m: keep the m 16-channel groups of largest summed query energy (ties to
+ *            the lower group), 0 or >= head_dim/16 keeps all channels.  The mask applies to
+ *            every key (sink tokens included) and never to values.
+ *   out      [batch][n_q_heads][head_dim] fp32, device.
+ *   mask_out nullable, [batch * n_kv_heads] bytes, bit p set = group p was read.
+ *   ws       workspace of ws_bytes >= kvq_decode_workspace_bytes(c, n_q_heads).
+ * len = 0 writes zeros.                                                                   */
+kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
+                           float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Number of context splits kvq_decode_attn uses for the current len (host-only).        */
+int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads);
+
+/* Host helper: the 2^bits-level symmetric Lloyd-Max codebook of N(0,1) (fp64 iteration to
+ * 1e-13, rounded to fp32), written to HOST arrays centroids[2^bits], thresholds[2^bits-1].
+ * Only bits = 4 is used by the key formats.                                               */
+kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *thresholds);
+
+/* Tuning override for the split planner: target tiles of 256 positions per split, 0 = the
+ * built-in policy.  Process-wide; affects later decode calls only.                        */
+void kvq_set_split_tiles(int32_t tiles_per_split);
+
+const char *kvq_status_string(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -286,7 +286,11 @@ static void asym_group(const float *x, int n, int bits, int skip0, uint8_t *code
         if (x[i] > mx)
             mx = x[i];
     }
-    float range = mx - mn;
+    /* Reading: a zero minimum or range is taken as +0 (adding +0 turns -0 into +0 and
+     * leaves every other value unchanged), so the stored fp16 sign bit never depends on
+     * which of -0 / +0 a min/max scan meets first.                                      */
+    mn = mn + 0.0f;
+    float range = (mx - mn) + 0.0f;
     float scale32 = range / (float)qmax;
     uint16_t sh = oracle_f32_to_f16(scale32);
     uint16_t zh = oracle_f32_to_f16(mn);

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/kvq.h declares, sizes buffers per the layout, and rejects bad arguments
+before anything is launched (so these calls never reach HIP)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_kv_cache_kvq_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before any launch
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    L = B.lib()
+    names = _declared()
+    assert set(B.EXPORTS) == set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _cache(**kw):
+    c = dict(batch=2, n_kv_heads=3, head_dim=128, capacity=512, n_sink=0, k_format=0, k_hadamard=0,
+             k_ch0_bf16=0, len=0)
+    c.update(kw)
+    s = B.KvqCacheC(*[c[k] for k in ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink", "k_format",
+                                      "k_hadamard", "k_ch0_bf16", "len")])
+    for name in B.BUF_NAMES:
+        setattr(s, name, FAKE)
+    return s
+
+
+def test_buffer_bytes_follow_layout():
+    L = B.lib()
+    U, d, cap = 6, 128, 512
+    s = _cache(k_ch0_bf16=1, n_sink=4)
+    nb = [L.kvq_buffer_bytes(ctypes.byref(s), i) for i in range(10)]
+    assert nb == [U * 8 * cap * 4, U * 4 * cap * 4, 0, U * cap * 2, U * cap // 2 * 32 * 4, U * 4 * cap * 4,
+                  U * 4 * d * 2, U * 4 * d * 2, 0, 0]
+    s = _cache(k_format=2, k_hadamard=1, head_dim=64)
+    nb = [L.kvq_buffer_bytes(ctypes.byref(s), i) for i in range(10)]
+    assert nb == [U * 8 * cap * 4, 0, U * cap * 2, 0, U * cap // 2 * 16 * 4, U * 2 * cap * 4, 0, 0, 64, 60]
+    assert L.kvq_buffer_bytes(ctypes.byref(_cache(head_dim=96)), 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), B.KVQ_ERR_UNSUPPORTED),
+    (dict(capacity=300), B.KVQ_ERR_UNSUPPORTED),
+    (dict(n_sink=65), B.KVQ_ERR_UNSUPPORTED),
+    (dict(k_format=7), B.KVQ_ERR_ARG),
+    (dict(k_hadamard=1, k_ch0_bf16=1), B.KVQ_ERR_UNSUPPORTED),
+    (dict(k_format=2, k_ch0_bf16=1), B.KVQ_ERR_UNSUPPORTED),
+    (dict(batch=0), B.KVQ_ERR_ARG),
+    (dict(len=513), B.KVQ_ERR_CAPACITY),
+    (dict(batch=70000), B.KVQ_ERR_UNSUPPORTED),
+])
+def test_validate_rejects(kw, code):
+    assert B.lib().kvq_validate(ctypes.byref(_cache(**kw))) == code
+
+
+def test_validate_pointers():
+    L = B.lib()
+    s = _cache()
+    assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_OK
+    s.v_sz = None
+    assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_ERR_ARG
+    s = _cache()
+    s.k_codes = FAKE + 4
+    assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_ERR_ALIGN
+    s = _cache()
+    s.k_norm = None  # unused by asymmetric keys
+    s.codebook = None
+    assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_OK
+
+
+def test_append_errors_leave_len():
+    L = B.lib()
+    s = _cache(len=500)
+    P = ctypes.c_void_p
+    assert L.kvq_quant_append(ctypes.byref(s), P(FAKE), P(FAKE), 1, 13, None) == B.KVQ_ERR_CAPACITY
+    assert L.kvq_quant_append(ctypes.byref(s), P(FAKE), P(FAKE), 5, 1, None) == B.KVQ_ERR_ARG
+    assert L.kvq_quant_append(ctypes.byref(s), P(FAKE), P(FAKE), 1, -1, None) == B.KVQ_ERR_ARG
+    assert L.kvq_quant_append(ctypes.byref(s), P(FAKE + 2), P(FAKE), 1, 1, None) == B.KVQ_ERR_ALIGN
+    assert L.kvq_quant_append(ctypes.byref(s), None, P(FAKE), 1, 1, None) == B.KVQ_ERR_ARG
+    assert L.kvq_quant_append(ctypes.byref(s), P(FAKE), P(FAKE), 1, 0, None) == B.KVQ_OK
+    assert s.len == 500
+    assert L.kvq_quant_append(None, P(FAKE), P(FAKE), 1, 1, None) == B.KVQ_ERR_ARG
+
+
+def test_decode_errors():
+    L = B.lib()
+    s = _cache(len=100)
+    P = ctypes.c_void_p
+    need = L.kvq_decode_workspace_bytes(ctypes.byref(s), 12)
+    assert need > 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(s), 7) == 0
+
+    def call(hq=12, keep=0, ws_bytes=None, q=FAKE, dt=1, sm=0.088, ws=FAKE):
+        return L.kvq_decode_attn(ctypes.byref(s), P(q), dt, hq, sm, keep, P(FAKE), None, P(ws),
+                                 need if ws_bytes is None else ws_bytes, None)
+
+    assert call(hq=7) == B.KVQ_ERR_ARG
+    assert call(hq=3 * 3) == B.KVQ_ERR_UNSUPPORTED  # G = 3
+    assert call(keep=-1) == B.KVQ_ERR_ARG
+    assert call(ws_bytes=need - 1) == B.KVQ_ERR_WORKSPACE
+    assert call(ws=0) == B.KVQ_ERR_WORKSPACE
+    assert call(q=FAKE + 8) == B.KVQ_ERR_ALIGN
+    assert call(dt=9) == B.KVQ_ERR_ARG
+    assert call(sm=float("nan")) == B.KVQ_ERR_ARG
+    assert call(q=0) == B.KVQ_ERR_ARG
+
+
+def test_split_planner_counts():
+    L = B.lib()
+    s = _cache(batch=64, n_kv_heads=8, capacity=16640, len=16385, n_sink=4)
+    n = L.kvq_decode_splits(ctypes.byref(s), 32)
+    tiles = (16385 + 255) // 256
+    assert 1 <= n <= tiles
+    s = _cache(batch=1, n_kv_heads=1, capacity=256, len=0)
+    assert L.kvq_decode_splits(ctypes.byref(s), 1) == 1
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert B.status_string(st)
+    assert B.status_string(99) == "unknown status"
+
+
+def test_library_codebook_equals_oracle_codebook(oracle_mod):
+    """Two independent Lloyd-Max builders (library host code and oracle) agree bit for bit
+    after rounding to fp32."""
+    c, t = B.codebook_gaussian(4)
+    oc, ot = oracle_mod.codebook_f32(16)
+    np.testing.assert_array_equal(np.array(c, np.float32), oc)
+    np.testing.assert_array_equal(np.array(t, np.float32), ot)

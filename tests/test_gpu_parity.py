@@ -1,0 +1,151 @@
+"""GPU parity of the HIP path against the CPU oracle on small and ragged shapes.
+
+Packed bytes must match bit for bit; attention outputs within 2e-3 of the oracle row norm;
+pruning masks exactly.  Inputs come from the seeded generators (CPU draws copied to the
+GPU), so both sides see identical values.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_kvq_amd import binding as B
+from bit_kv_cache_kvq_amd import synth
+from gpu_util import compare_buffers, compare_outputs, note, oracle_geo, to_f32_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, Bsz, Hkv, T, d, dist="normal", dtype=torch.bfloat16, outliers=()):
+    shape = (Bsz, Hkv, T, d)
+    if dist == "t3":
+        k = synth.student_t3(shape, "cpu", seed, 100, 0)
+        v = synth.student_t3(shape, "cpu", seed, 100, 1)
+    else:
+        k = synth.normal(shape, "cpu", seed, 100, 0)
+        v = synth.normal(shape, "cpu", seed, 100, 1)
+    for ch, f in outliers:
+        k[..., ch] *= f
+    return k.to(dtype), v.to(dtype)
+
+
+def _run(oracle_mod, *, d=128, kfmt=0, rot=0, ch0=0, ns=0, T=300, G=4, Hkv=2, Bsz=2, keep=0,
+         dtype=torch.bfloat16, chunks=None, dist="normal", seed=0, cap=None, q_scale=1.0, outliers=()):
+    cap = cap or max(256, (T + 255) // 256 * 256)
+    note(f"case d={d} kfmt={kfmt} rot={rot} ch0={ch0} ns={ns} T={T} G={G} Hkv={Hkv} B={Bsz} keep={keep} "
+         f"dtype={dtype} chunks={chunks} dist={dist}")
+    c = B.Cache(Bsz, Hkv, d, cap, n_sink=ns, k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0)
+    oc = oracle_geo(oracle_mod, c)
+    k, v = _inputs(seed, Bsz, Hkv, T, d, dist, dtype, outliers)
+    chunks = chunks or [T]
+    assert sum(chunks) == T
+    t = 0
+    for n in chunks:
+        kc, vc = k[:, :, t:t + n].contiguous(), v[:, :, t:t + n].contiguous()
+        c.append(kc.cuda(), vc.cuda())
+        oc.append(to_f32_np(kc).reshape(Bsz * Hkv, n, d), to_f32_np(vc).reshape(Bsz * Hkv, n, d))
+        t += n
+    torch.cuda.synchronize()
+    assert c.len == T == oc.len
+    compare_buffers(c, oc, what="append")
+    q = (synth.normal((Bsz, Hkv * G, d), "cpu", seed, 100, 2) * q_scale).to(dtype)
+    sm = 1.0 / np.sqrt(d)
+    out, mask = c.decode(q.cuda(), sm, keep)
+    torch.cuda.synchronize()
+    ref, rmask = oc.decode(to_f32_np(q).reshape(Bsz * Hkv, G, d), sm, keep)
+    np.testing.assert_array_equal(mask.cpu().numpy(), rmask)
+    worst = compare_outputs(out, ref, "decode")
+    note(f"  ok, worst err/||o|| = {worst:.2e}")
+    return c, oc, q, out
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 255, 256, 257, 1000])
+def test_asym2_ch0_ragged_lengths(oracle_mod, T):
+    _run(oracle_mod, kfmt=0, ch0=1, T=T)
+
+
+@pytest.mark.parametrize("d,kfmt,rot,ch0,G,dtype", [
+    (64, 0, 0, 1, 1, torch.float32),
+    (64, 1, 0, 0, 2, torch.bfloat16),
+    (64, 2, 1, 0, 4, torch.bfloat16),
+    (64, 2, 0, 0, 8, torch.float32),
+    (128, 1, 0, 1, 1, torch.float32),
+    (128, 2, 1, 0, 4, torch.bfloat16),
+    (128, 2, 0, 0, 2, torch.bfloat16),
+    (128, 0, 0, 0, 8, torch.bfloat16),
+    (128, 1, 0, 0, 4, torch.bfloat16),
+])
+def test_formats_and_groups(oracle_mod, d, kfmt, rot, ch0, G, dtype):
+    _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, dtype=dtype, T=777)
+
+
+@pytest.mark.parametrize("keep", [1, 3, 5, 7, 8])
+@pytest.mark.parametrize("kfmt,rot,ch0", [(0, 0, 1), (2, 1, 0), (1, 0, 0)])
+def test_pruning(oracle_mod, keep, kfmt, rot, ch0):
+    _run(oracle_mod, kfmt=kfmt, rot=rot, ch0=ch0, keep=keep, T=600)
+
+
+@pytest.mark.parametrize("ns,T", [(4, 300), (3, 3), (4, 2), (64, 64), (64, 70), (1, 257), (5, 1000)])
+def test_sinks(oracle_mod, ns, T):
+    _run(oracle_mod, kfmt=0, ns=ns, T=T, dist="t3", keep=0)
+
+
+def test_sinks_with_pruning_and_rotation(oracle_mod):
+    _run(oracle_mod, kfmt=2, rot=1, ns=4, T=500, keep=4)
+    _run(oracle_mod, kfmt=0, ch0=1, ns=8, T=500, keep=3, d=64, G=2)
+
+
+def test_incremental_appends_match_bulk(oracle_mod):
+    _run(oracle_mod, kfmt=0, ch0=1, ns=4, T=300, chunks=[5, 1, 1, 100, 1, 192])
+    _run(oracle_mod, kfmt=2, rot=1, T=261, chunks=[256, 1, 1, 1, 1, 1])
+
+
+def test_heavy_tails_and_outliers(oracle_mod):
+    _run(oracle_mod, kfmt=0, ch0=1, T=2000, dist="t3", outliers=((7, 8.0), (45, 8.0)))
+    _run(oracle_mod, kfmt=0, T=2000, q_scale=6.0)  # sharp attention
+
+
+def test_zero_length_and_sink_only(oracle_mod):
+    c = B.Cache(2, 2, 128, 256, n_sink=4)
+    q = torch.randn(2, 8, 128, device="cuda")
+    out, _ = c.decode(q, 0.088)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    _run(oracle_mod, ns=4, T=4)
+
+
+def test_split_invariance_and_determinism(oracle_mod):
+    c, oc, q, out0 = _run(oracle_mod, kfmt=0, ch0=1, T=5000, Bsz=1, Hkv=2, G=4)
+    qg = q.cuda()
+    ref, _ = oc.decode(to_f32_np(q).reshape(2, 4, 128), 1 / np.sqrt(128))
+    outs = []
+    try:
+        for tps in (1, 2, 3, 7, 20):
+            B.set_split_tiles(tps)
+            note(f"  split tiles {tps}: {c.splits(8)} splits")
+            o1, _ = c.decode(qg, 1 / np.sqrt(128))
+            o2, _ = c.decode(qg, 1 / np.sqrt(128))
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2), "run-to-run difference"
+            compare_outputs(o1, ref, f"split tiles {tps}")
+            outs.append(o1)
+    finally:
+        B.set_split_tiles(0)
+
+
+def test_keep_all_equals_no_pruning(oracle_mod):
+    c, oc, q, out0 = _run(oracle_mod, kfmt=0, ch0=1, T=700, keep=0)
+    o8, m8 = c.decode(q.cuda(), 1 / np.sqrt(128), 8)
+    o9, _ = c.decode(q.cuda(), 1 / np.sqrt(128), 100)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, o8) and torch.equal(out0, o9)
+    assert torch.all(m8 == 0xFF)
+
+
+def test_decode_leaves_cache_unchanged(oracle_mod):
+    c, oc, q, _ = _run(oracle_mod, kfmt=0, ch0=1, T=400, keep=5)
+    before = {k: v.clone() for k, v in c.buffers.items()}
+    c.decode(q.cuda(), 0.088, 5)
+    c.decode(q.cuda(), 0.088, 2)
+    torch.cuda.synchronize()
+    for k, v in c.buffers.items():
+        assert torch.equal(before[k], v), k
