@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of quantized-KV decode attention on one MI355X.
+
+One step = one pass of the whole path over one batch: kvq_quant_append of one new
+token per sequence (quantize + pack), then kvq_decode_attn for every query head over
+the whole cache.  Default workload: batch 64, 32 query / 8 KV heads, head_dim 128,
+16384-token Student-t3 context, 4 BF16 sink tokens, INT2 keys, INT4 values, one appended
+token per step (the largest of the five workloads; the metric is an HBM-bandwidth figure
+and the smaller workloads fit in the 256 MB last-level cache).
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value           KV tokens scored per second (batch * positions attended, per step)
+  roofline        decode kernel: algorithmic bytes per launch / average launch duration
+                  (HIP events on the launch stream), against 8 TB/s HBM
+  cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
+Inputs are resident in HBM before the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_t16k_traffic.txt")
+DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_kvq_amd", "csrc", "kvq_decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes_unit(w, length, mask):
+    """Algorithmic HBM bytes one decode reads for one (sequence, KV head): the code words,
+    scale/zero words and channel-0 / norm halves of the kept key rows, every value word and
+    value scale/zero word, and the BF16 sink rows.  mask: kept 16-channel groups (bit p)."""
+    d = w.head_dim
+    P = d // 16
+    kept = [(mask >> p) & 1 for p in range(P)]
+    ns = min(w.n_sink, length)
+    quant = length - ns
+    kbits = 2 if w.k_format == 0 else 4
+    k_tok = sum(kept) * 16 * kbits // 8
+    if w.k_format == 2:
+        k_tok += 2
+    else:
+        k_tok += 4 * sum(1 for g in range(d // 32) if kept[2 * g] or kept[2 * g + 1])
+        if w.k_ch0_bf16 and kept[0]:
+            k_tok += 2
+    v_tok = d // 2 + 4 * (d // 32)
+    return quant * (k_tok + v_tok) + ns * d * 2 * 2
+
+
+def traffic_record():
+    """HBM bytes per decode launch measured with rocprofv3 counters, if the counters were
+    taken on the current decode source (sha256 recorded next to the numbers)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if kv.get("decode_source_sha256") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, length, budget_s):
+    """The oracle (plain C, fp64 attention) on a bounded sample of the same workload:
+    a few sequences at the bench's context length, timed over append + decode steps."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from bit_kv_cache_kvq_amd import synth
+
+    oracle.lib()
+    threads = oracle.num_threads()
+    H = w.n_kv_heads
+    nseq = max(1, math.ceil(threads / H))
+    geo = oracle.Geometry(batch=nseq, n_kv_heads=H, head_dim=w.head_dim, capacity=w.capacity(512),
+                          n_sink=w.n_sink, k_format=w.k_format, k_hadamard=w.k_hadamard,
+                          k_ch0_bf16=w.k_ch0_bf16)
+    oc = oracle.OracleCache(geo)
+    prefill_len = length - (1 if w.steps else 0)
+    k, v = synth.prefill(w, device="cpu", context=prefill_len, batch=nseq)
+    oc.append(k.float().numpy().reshape(nseq * H, prefill_len, w.head_dim),
+              v.float().numpy().reshape(nseq * H, prefill_len, w.head_dim))
+    del k, v
+    steps, tokens, t_used = 0, 0, 0.0
+    while t_used < budget_s and steps < 256:
+        q = synth.query(w, steps, device="cpu", batch=nseq).float().numpy().reshape(nseq * H, w.group, w.head_dim)
+        if w.steps:
+            kn, vn = synth.append_tokens(w, steps, device="cpu", batch=nseq)
+            kn = kn.float().numpy().reshape(nseq * H, 1, w.head_dim)
+            vn = vn.float().numpy().reshape(nseq * H, 1, w.head_dim)
+        t0 = time.perf_counter()
+        if w.steps:
+            oc.append(kn, vn)
+        oc.decode(q, w.sm_scale, w.keep_groups)
+        t_used += time.perf_counter() - t0
+        tokens += nseq * oc.len
+        steps += 1
+    return {"value": tokens / t_used, "unit": "tokens/s", "cores": min(threads, nseq * H), "kind": "oracle",
+            "sample": f"{nseq} of {w.batch} sequences x {H} KV heads at ~{oc.len} positions, {steps} "
+                      f"append+decode steps, {t_used:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs the decode path on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); multi-GPU sharding is design-only, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_kv_cache_kvq_amd import binding as B
+    from bit_kv_cache_kvq_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 5 copies of 1073741824 bytes")
+        return
+    w = synth.WORKLOADS[args.workload]
+    appends = args.warmup + args.steps if w.steps else 0
+    cap = w.capacity(appends)
+    c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
+                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, device=dev)
+    log(f"workload {w.name}: capacity {cap}, building cache ...")
+    k, v = synth.prefill(w, device=dev)
+    c.append(k, v)
+    torch.cuda.synchronize()
+    del k, v
+    torch.cuda.empty_cache()
+    nsteps = args.warmup + args.steps
+    queries = [synth.query(w, i, device=dev) for i in range(nsteps)]
+    news = [synth.append_tokens(w, i, device=dev) for i in range(nsteps)] if w.steps else []
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    mask = torch.zeros(w.units, dtype=torch.uint8, device=dev)
+    c.workspace(w.n_q_heads)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if w.steps:
+            c.append(*news[i])
+        if ev is not None:
+            ev[0].record(stream)
+        c.decode(queries[i], w.sm_scale, w.keep_groups, out=out, mask_out=mask)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    lens = []
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+        lens.append(c.len)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    full = (1 << (w.head_dim // 16)) - 1
+    masks = mask.cpu().tolist() if w.keep_groups else [full] * w.units
+    bytes_per = [sum(decode_bytes_unit(w, L, m) for m in masks) for L in lens]
+    avg_bytes = sum(bytes_per) / len(bytes_per)
+    tokens = sum(w.batch * L for L in lens)
+    value = tokens / elapsed
+    eff_gbps = sum(bytes_per) / elapsed / 1e9
+    achieved = avg_bytes / dec_avg_s / 1e9
+    traffic = traffic_record() if args.workload == 5 else None
+    log(f"decode kernel avg {dec_avg_s * 1e6:.1f} us, {avg_bytes / 1e9:.4f} GB/launch, {achieved:.0f} GB/s; "
+        f"step {elapsed / args.steps * 1e3:.3f} ms; splits {c.splits(w.n_q_heads)}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, lens[-1], args.cpu_budget)
+
+    res = {
+        "metric": "KV tokens scored/sec and effective HBM GB/s (% of peak), 1 GPU",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8/f16/f32",
+        "data": "synthetic (seeded Student-t3 keys/values, N(0,1) queries)" if w.dist == "t3"
+                else "synthetic (seeded N(0,1) keys/values/queries)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "context": w.context, "positions_attended_last_step": lens[-1],
+                   "key_format": ["asym_int2", "asym_int4", "wht_lloyd4"][w.k_format],
+                   "value_format": "asym_int4_g32", "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink,
+                   "keep_groups": w.keep_groups, "appends_per_step": 1 if w.steps else 0,
+                   "parallelism": "single GPU"},
+        "effective_GBps": eff_gbps,
+        "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
+        "decode_algorithmic_bytes_per_launch": avg_bytes,
+        "decode_kernel_us": dec_avg_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

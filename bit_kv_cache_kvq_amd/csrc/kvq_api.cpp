@@ -29,7 +29,7 @@ kvq_status check_geometry(const kvq_cache *c)
         return KVQ_ERR_UNSUPPORTED;
     if (c->head_dim != 64 && c->head_dim != 128)
         return KVQ_ERR_UNSUPPORTED;
-    if (c->capacity % kTile != 0)
+    if (c->capacity % kCapacityQuantum != 0)
         return KVQ_ERR_UNSUPPORTED;
     if (c->n_sink < 0 || c->n_sink > kMaxSink || c->n_sink >= c->capacity)
         return KVQ_ERR_UNSUPPORTED;
@@ -85,9 +85,10 @@ struct Plan {
     int tile_begin, tile_end, n_tiles, n_split, tiles_per_split;
 };
 
-// Split planner: enough workgroups to fill 256 CUs several times over while keeping at
-// least one 256-position tile per wave where the context allows it.
-Plan plan_splits(const kvq_cache *c, int len)
+// Split planner: one wave per split; enough splits that every resident wave slot of the
+// device holds one (slots = resident one-wave workgroups of the kernel instantiation), with
+// the context tiles divided evenly.
+Plan plan_splits(const kvq_cache *c, int len, int slots)
 {
     Plan pl;
     const int n_sink = c->n_sink < len ? c->n_sink : len;
@@ -104,11 +105,9 @@ Plan plan_splits(const kvq_cache *c, int len)
     const long long units = (long long)units_of(c);
     int tps = g_split_tiles.load();
     if (tps <= 0) {
-        const long long target_blocks = 2048; // 8 per CU
-        long long want_split = (target_blocks + units - 1) / units;
-        long long by_tiles = (pl.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock; // >= 4 tiles per split
-        if (want_split > by_tiles)
-            want_split = by_tiles;
+        long long want_split = (slots + units / 2) / units;
+        if (want_split > pl.n_tiles)
+            want_split = pl.n_tiles;
         if (want_split < 1)
             want_split = 1;
         tps = (int)((pl.n_tiles + want_split - 1) / want_split);
@@ -209,16 +208,17 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
     const size_t U = units_of(c);
     const size_t G = (size_t)(n_q_heads / c->n_kv_heads);
     const size_t part = U * (size_t)max_splits(c) * G * (size_t)(c->head_dim + 2) * sizeof(float);
-    const size_t part_aligned = (part + 255) & ~(size_t)255;
-    return part_aligned + ((U * sizeof(uint32_t) + 255) & ~(size_t)255);
+    return (part + 255) & ~(size_t)255;
 }
 
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
 {
-    (void)n_q_heads;
-    if (check_geometry(c) != KVQ_OK)
+    if (check_geometry(c) != KVQ_OK || n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
         return 0;
-    return plan_splits(c, c->len).n_split;
+    const int G = n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return 0;
+    return plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format)).n_split;
 }
 
 kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
@@ -245,9 +245,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     if (!aligned16(ws))
         return KVQ_ERR_ALIGN;
 
-    const Plan pl = plan_splits(c, c->len);
+    const Plan pl = plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format));
     const size_t U = units_of(c);
-    const size_t part = U * (size_t)max_splits(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float);
     DecodeParams p;
     p.k_codes = c->k_codes;
     p.k_sz = c->k_sz;
@@ -262,7 +261,6 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.out = out;
     p.mask_out = mask_out;
     p.part = static_cast<float *>(ws);
-    p.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + ((part + 255) & ~(size_t)255));
     p.n_kv_heads = c->n_kv_heads;
     p.cap = c->capacity;
     p.len = c->len;

@@ -12,8 +12,10 @@ constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
 
-// Decode tile: positions scored by one wave per pass (64 lanes x 4 positions).
-constexpr int kTile = 256;
+// Decode tile: positions scored by one wave per pass (64 lanes x 2 positions).
+constexpr int kTile = 128;
+// Cache capacity granule (public contract: capacity is a multiple of 256 positions).
+constexpr int kCapacityQuantum = 256;
 constexpr int kMaxSink = 64;
 
 struct AppendParams {
@@ -32,7 +34,6 @@ struct DecodeParams {
     float *out;
     uint8_t *mask_out;
     float *part;        // split partials [U][n_split][G][D + 2]
-    uint32_t *counters; // [U], zero between calls
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
     float sm_log2e;      // softmax scale times log2(e)
     int n_split, tile_begin, tile_end, tiles_per_split;
@@ -41,5 +42,7 @@ struct DecodeParams {
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
 hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
                          hipStream_t s);
+// Resident decode workgroups (one wave each) the device holds for this instantiation.
+int decode_slots(int head_dim, int group, int kfmt);
 
 } // namespace kvq

@@ -137,8 +137,8 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
                             int32_t n_new, void *stream);
 
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (any len up to capacity)
- * and n_q_heads.  The workspace holds split partials and one counter word per unit; it
- * must be zero-filled once before its first use and is left zeroed by every call.        */
+ * and n_q_heads.  The workspace holds the per-split partial softmax states; its contents
+ * need no initialisation and are scratch between calls.                                  */
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
 
 /* Decode attention for one query step per sequence over positions [0, len).
