@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -16,24 +17,35 @@ ARCH = "gfx950"
 
 SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip"]
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
+# Per-source extra flags (none at present).
+SOURCE_FLAGS: dict[str, list[str]] = {}
+BUILD_DIR = os.path.join(HERE, "_build")
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libkvq.so")
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    cmds = [[HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+            for src, obj in zip(SOURCES, objs)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -85,9 +85,12 @@ struct Plan {
     int tile_begin, tile_end, n_tiles, n_split, tiles_per_split;
 };
 
-// Split planner: one wave per split; enough splits that every resident wave slot of the
-// device holds one (slots = resident one-wave workgroups of the kernel instantiation), with
-// the context tiles divided evenly.
+// Split planner: one wave per split.  Enough splits that every resident wave slot of the
+// device holds one (slots = resident one-wave workgroups of the kernel instantiation), and
+// at most kSplitTiles tiles per split so long contexts keep more waves than slots (the
+// spare waves fill the gaps the finishing ones leave); the tiles are divided evenly.
+constexpr int kSplitTiles = 16;
+
 Plan plan_splits(const kvq_cache *c, int len, int slots)
 {
     Plan pl;
@@ -106,6 +109,9 @@ Plan plan_splits(const kvq_cache *c, int len, int slots)
     int tps = g_split_tiles.load();
     if (tps <= 0) {
         long long want_split = (slots + units / 2) / units;
+        const long long by_len = (pl.n_tiles + kSplitTiles - 1) / kSplitTiles;
+        if (want_split < by_len)
+            want_split = by_len;
         if (want_split > pl.n_tiles)
             want_split = pl.n_tiles;
         if (want_split < 1)
@@ -201,14 +207,22 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
     return KVQ_OK;
 }
 
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workspace: split partials [U][max splits][G][D + 2] fp32, then the query records
+static size_t part_region_bytes(const kvq_cache *c, int G)
+{
+    return round256(units_of(c) * (size_t)max_splits(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float));
+}
+
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
 {
     if (check_geometry(c) != KVQ_OK || n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
         return 0;
     const size_t U = units_of(c);
     const size_t G = (size_t)(n_q_heads / c->n_kv_heads);
-    const size_t part = U * (size_t)max_splits(c) * G * (size_t)(c->head_dim + 2) * sizeof(float);
-    return (part + 255) & ~(size_t)255;
+    return part_region_bytes(c, (int)G) +
+           round256(U * (size_t)decode_qrec_words(c->head_dim, (int)G, c->k_format) * sizeof(uint32_t));
 }
 
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
@@ -261,6 +275,7 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.out = out;
     p.mask_out = mask_out;
     p.part = static_cast<float *>(ws);
+    p.qprep = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + part_region_bytes(c, G));
     p.n_kv_heads = c->n_kv_heads;
     p.cap = c->capacity;
     p.len = c->len;

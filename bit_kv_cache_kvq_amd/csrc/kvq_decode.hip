@@ -13,25 +13,31 @@
 //     merged across splits by a small second kernel (no device-wide fences);
 //   * values from INT4 codes: o = sum_t p_t s_{t,g} code_{t,c} + sum_t p_t z_{t,g}.
 //
-// MI355X mapping (one workgroup = one wave = one context split of one unit; the host sizes
-// the splits so every SIMD slot the kernel's register use allows holds a wave):
-//   * score phase, lane per position: each lane scores 2 consecutive positions; a key row
-//     is one dwordx2 load per lane (64 lanes read 512 B contiguous).  Asymmetric codes are
-//     spread into bytes by shift+mask and multiplied with v_dot4_i32_i8 against the query
-//     held as a 16-bit integer in two signed-byte planes: exact int32 sums, and the
-//     zero-point term uses the same integer query, so code and zero terms together equal
-//     q_int . k^ with no cancellation between them (heavy-tailed keys make the group zero
-//     large).  The planes of one (row, head) come from LDS as a broadcast read straight into
-//     VGPR operands.  Lloyd-Max codes go through an LDS table of fp16 centroid pairs and
-//     v_dot2_f32_f16 against fp16 query pairs.
-//   * softmax: a running maximum per head; a wave-wide DPP reduction and a rescale happen
-//     only when a tile holds a logit above it (rare after the first tiles).
-//   * value phase, lane per 8 channels: v_dot2_f32_f16 over position pairs (value words
-//     interleave two positions); a 4-bit code masked into the low mantissa bits of a half
-//     is the subnormal integer code * 2^-24 (or * 2^-20), so no conversion is needed.  The
-//     fp16 weights p*s of each position pair come from LDS (conflict-free layout).
-//   * the next tile's key-side words are loaded before the value phase of the current one.
-//   * no MFMA: this is a bandwidth-bound scan.
+// Three kernels per decode call:
+//   qprep   one wave per (sequence, KV head): query in stored coordinates, pruning mask and
+//           the integer / fp16 query operands, written once to a small per-unit record.
+//   decode  one wave per (unit, context split); the host sizes the splits so every SIMD
+//           slot the kernel's register use allows holds a wave.  The query record is read
+//           with uniform loads, so its operands sit in scalar registers.
+//           * score phase, lane per position: each lane scores 2 consecutive positions; a
+//             key row is one dwordx2 load per lane (512 B contiguous per wave).  Asymmetric
+//             codes are spread into bytes by shift+mask and multiplied with v_dot4_i32_i8
+//             against the query held as a 16-bit integer in two signed-byte planes: exact
+//             int32 sums, and the zero-point term uses the same integer query, so code and
+//             zero terms together equal q_int . k^ with no cancellation between them
+//             (heavy-tailed keys make the group zero large).  Lloyd-Max codes go through an
+//             LDS table of fp16 centroid pairs and v_dot2_f32_f16 against fp16 query pairs.
+//           * softmax: a running maximum per head; a wave-wide DPP reduction and a rescale
+//             happen only when a tile holds a logit above it (rare after the first tiles).
+//           * value phase, lane per 8 channels: v_dot2_f32_f16 over position pairs (value
+//             words interleave two positions); a 4-bit code masked into the low mantissa
+//             bits of a half is the subnormal integer code * 2^-24 (or * 2^-20), so no
+//             conversion is needed.  The fp16 weights p*s of a position pair and scale
+//             group reach the value lanes through LDS, all heads in one 16-byte read.
+//           * the next tile's key-side words are loaded before the value phase of the
+//             current one; cache reads are non-temporal (each byte is read once).
+//   merge   combines the per-split partial softmax states (skipped for one split).
+// No MFMA: this is a bandwidth-bound scan.
 #include <atomic>
 
 #include "kvq_device.h"
@@ -58,8 +64,18 @@ struct Cfg {
     static constexpr int LPP = WPP / VW;           // value lanes per pair
     static constexpr int PPI = 64 / LPP;           // pairs per value iteration
     static constexpr int VIT = PAIRS / PPI;        // value iterations per tile
-    static constexpr int CPL = D / 64;             // channels per lane in the prologue
-    static constexpr int WROW = PAIRS + 1;         // padded LDS weight row (conflict-free)
+    static constexpr int CPL = D / 64;             // channels per lane in the query prep
+    static constexpr int WV = (G + 3) / 4;         // uint4 of fp16 weight pairs per (group, pair)
+    // query record, u32 words per unit: mask; per head the accumulator unit (log2-logit
+    // per accumulator step) and the channel-0 coefficient; zero-term sums [G][NG]; query
+    // operands [KROWS][G][QW]; scaled masked fp32 query [G][D] (sink positions)
+    static constexpr int OFF_MASK = 0;
+    static constexpr int OFF_QSC = 4;
+    static constexpr int OFF_Q0 = OFF_QSC + G;
+    static constexpr int OFF_QZ = OFF_Q0 + G;
+    static constexpr int OFF_QP = (OFF_QZ + G * NG + 7) / 8 * 8;
+    static constexpr int OFF_QF = OFF_QP + KROWS * G * QW;
+    static constexpr int QREC = (OFF_QF + G * D + 63) / 64 * 64;
     static_assert(TILE == kTile, "host and device tile must agree");
 };
 
@@ -101,20 +117,218 @@ __device__ __forceinline__ void fwht_wave(float (&y)[CPL], int lane)
     }
 }
 
+// Cache reads are raw buffer loads: one descriptor per (unit, array) holds the unit's slab
+// (base, byte size), the lane part of the offset is a VGPR and the position part an SGPR,
+// so no 64-bit address arithmetic runs on the VALU.  An access at or beyond the slab size
+// returns zero without touching memory; a descriptor of size 0 turns a prefetch past the
+// last tile into a no-op without a branch.  All of them are non-temporal (read once).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+constexpr int kBufWord3 = 0x00020000; // raw 32-bit access, no format conversion
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const u2v t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal);
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal);
+}
+
+// ===================================================================== query prep
+// One wave per unit: stored-coordinate query (FWHT when keys are rotated), 16-channel
+// group energies (fp32 stride-halving tree, the order the format fixes), mask, and the
+// query operands of the decode kernel.
+template <int D, int G, int KF>
+__global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
+{
+    using C = Cfg<D, G, KF>;
+    constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
+    constexpr int CPL = C::CPL, QW = C::QW;
+    __shared__ float sq_[G][D];
+    __shared__ float se[G][NP];
+    __shared__ float sam[G][NP];
+
+    const int lane = threadIdx.x;
+    const int unit = blockIdx.x;
+    const int b = unit / p.n_kv_heads;
+    const int kvh = unit % p.n_kv_heads;
+    const int n_q_heads = p.n_kv_heads * G;
+    uint32_t *rec = p.qprep + (size_t)unit * C::QREC;
+    float *recf = reinterpret_cast<float *>(rec);
+
+    for (int h = 0; h < G; h++) {
+        const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
+        float y[CPL];
+        if (p.q_bf16) {
+            const uint16_t *qb = static_cast<const uint16_t *>(p.q) + qoff;
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                y[s] = bf16_to_f32(qb[s]);
+        } else {
+            const float *qf = static_cast<const float *>(p.q) + qoff;
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                y[s] = qf[s];
+        }
+        if (p.rotate)
+            fwht_wave<CPL>(y, lane);
+        float sq[CPL], am = 0.0f;
+#pragma unroll
+        for (int s = 0; s < CPL; s++) {
+            sq_[h][lane * CPL + s] = y[s];
+            sq[s] = y[s] * y[s];
+            am = fmaxf(am, fabsf(y[s]));
+        }
+        // stride-halving tree over the 16 channels of a group: lanes of one group are
+        // 16/CPL consecutive lanes; the xor butterfly reproduces the tree's sums.
+#pragma unroll
+        for (int m = 8 / CPL; m >= 1; m >>= 1) {
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                sq[s] = sq[s] + __shfl_xor(sq[s], m);
+            am = fmaxf(am, __shfl_xor(am, m));
+        }
+        float e = sq[0];
+        if constexpr (CPL == 2)
+            e = sq[0] + sq[1];
+        if ((lane % (16 / CPL)) == 0) {
+            se[h][lane / (16 / CPL)] = e;
+            sam[h][lane / (16 / CPL)] = am;
+        }
+    }
+    __syncthreads();
+
+    // mask: keep the `keep` highest group energies summed over the heads in ascending
+    // head order, ties to the lower group
+    uint32_t mask = (1u << NP) - 1u;
+    if (p.keep > 0 && p.keep < NP) {
+        float E[NP];
+#pragma unroll
+        for (int g = 0; g < NP; g++) {
+            float acc = se[0][g];
+#pragma unroll
+            for (int h = 1; h < G; h++)
+                acc = acc + se[h][g];
+            E[g] = acc;
+        }
+        mask = 0;
+#pragma unroll
+        for (int g = 0; g < NP; g++) {
+            int rank = 0;
+#pragma unroll
+            for (int o = 0; o < NP; o++)
+                rank += (E[o] > E[g] || (E[o] == E[g] && o < g)) ? 1 : 0;
+            if (rank < p.keep)
+                mask |= 1u << g;
+        }
+    }
+    mask = uniform(mask);
+    if (lane == 0) {
+        rec[C::OFF_MASK] = mask;
+        if (p.mask_out)
+            p.mask_out[unit] = (uint8_t)mask;
+    }
+    const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
+
+    // scaled, masked fp32 query (the sink positions use it directly)
+    for (int h = 0; h < G; h++) {
+#pragma unroll
+        for (int s = 0; s < CPL; s++) {
+            const int c = lane * CPL + s;
+            const bool kept = (mask >> (c / 16)) & 1u;
+            const float v = kept ? sq_[h][c] * qscale : 0.0f;
+            sq_[h][c] = v;
+            recf[C::OFF_QF + h * D + c] = v;
+        }
+    }
+    __syncthreads();
+
+    if constexpr (KF == KVQ_K_LLOYD4) {
+        // fp16 pairs scaled so the largest kept |q| lands in [2^12, 2^13); byte j of key
+        // word r holds channels (8r + 2j, 8r + 2j + 1)
+        float amax = 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int g = 0; g < NP; g++)
+                if (mask >> g & 1u)
+                    amax = fmaxf(amax, sam[h][g]);
+        amax *= qscale;
+        int ex = 0;
+        (void)frexpf(amax, &ex);
+        const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
+        for (int h = 0; h < G; h++) {
+            if (lane < KROWS * PPW) {
+                const int r = lane / PPW, j = lane % PPW;
+                const int ca = 8 * r + 2 * j;
+                rec[C::OFF_QP + (r * G + h) * QW + j] = pack_f16x2(sq_[h][ca] * g2, sq_[h][ca + 1] * g2);
+            }
+            if (lane == 0) {
+                recf[C::OFF_QSC + h] = 1.0f / g2;
+                recf[C::OFF_Q0 + h] = 0.0f;
+            }
+        }
+    } else {
+        for (int h = 0; h < G; h++) {
+            // 16-bit integer query: q ~= qi * unit, |qi| <= 32639, written as 256*hi + lo
+            // with signed bytes hi, lo.  Channel 0 is scored from its BF16 copy instead.
+            float am = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < CPL; s2++) {
+                const int c = lane * CPL + s2;
+                if (!(p.ch0 && c == 0))
+                    am = fmaxf(am, fabsf(sq_[h][c]));
+            }
+            am = wave_max_dpp(am);
+            const float unit_q = am > 0.0f ? am / 32639.0f : 1.0f;
+            const float inv = 1.0f / unit_q;
+            // key word r, spread register k: byte m holds channel r*(32/KB) + m*(KB==2 ? 4 : 2) + k;
+            // words per (row, head): hi planes of registers 0..NREG-1, then the lo planes
+            if (lane < KROWS * C::NREG) {
+                const int r = lane / C::NREG, k = lane % C::NREG;
+                uint32_t hi = 0, lo = 0;
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    const int c = (KB == 2) ? 16 * r + 4 * m + k : 8 * r + 2 * m + k;
+                    const float qv = (p.ch0 && c == 0) ? 0.0f : sq_[h][c];
+                    const int qi = (int)__builtin_rintf(qv * inv);
+                    const int h8 = (qi + 128) >> 8;
+                    const int l8 = qi - 256 * h8;
+                    hi |= (uint32_t)(h8 & 0xFF) << (8 * m);
+                    lo |= (uint32_t)(l8 & 0xFF) << (8 * m);
+                }
+                rec[C::OFF_QP + (r * G + h) * QW + k] = hi;
+                rec[C::OFF_QP + (r * G + h) * QW + C::NREG + k] = lo;
+            }
+            if (lane < NG) {
+                float si = 0.0f;
+                for (int c = 32 * lane; c < 32 * lane + 32; c++)
+                    if (!(p.ch0 && c == 0))
+                        si += __builtin_rintf(sq_[h][c] * inv);
+                recf[C::OFF_QZ + h * NG + lane] = si;
+            }
+            if (lane == 0) {
+                recf[C::OFF_QSC + h] = unit_q;
+                recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv : 0.0f;
+            }
+        }
+    }
+}
+
+// ===================================================================== decode
 template <int D, int G, int KF>
 struct Smem {
     using C = Cfg<D, G, KF>;
-    float q[G][D];                                  // stored-coordinate query (scaled)
-    float e[G][C::NP];                              // group energies
-    float amax[G][C::NP];                           // group max |q~|
-    uint4 qp[C::KROWS][G][C::QW / 4];               // per (key row, head): int8 hi/lo query
-                                                    // planes (asym) or fp16 pairs (Lloyd-Max)
-    float qz[G][C::NG];                             // zero-term integer query sums
-    float q0[G];                                    // channel-0 coefficient (integer units)
-    float qsc[G];                                   // accumulator unit in log2-logit units
-    uint32_t lut[KF == KVQ_K_LLOYD4 ? 256 : 1];     // Lloyd-Max code-pair table (fp16x2)
+    uint32_t lut[KF == KVQ_K_LLOYD4 ? 256 : 1];      // Lloyd-Max code-pair table (fp16x2)
     float sink_p[G][kMaxSink];
-    uint32_t w[C::NG * G][C::WROW];                 // fp16 weight pairs of the current tile
+    uint4 w[C::NG][C::PAIRS + 1][C::WV];             // fp16 weight pairs: [group][pair][heads]
 };
 
 // Key-side words of one tile for this lane (TPL = 2 positions).
@@ -127,33 +341,35 @@ struct KTile {
     uint32_t kx; // channel-0 bf16 pair (asym + protection) or rho fp16 pair (Lloyd-Max)
 };
 
+// Descriptors of one unit's slabs.
+struct Slabs {
+    rsrc_t kc, ksz, kx, vsz, vc;
+};
+
 template <int D, int G, int KF>
-__device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const DecodeParams &p, int unit, int tl,
+__device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, uint32_t cap, int lane, int t0,
                                            uint32_t mask)
 {
     using C = Cfg<D, G, KF>;
-    const size_t cap = (size_t)p.cap;
-    const uint32_t *kc_base = p.k_codes + (size_t)unit * C::KROWS * cap + tl;
+    const uint32_t vo = (uint32_t)lane * C::TPL * 4u;  // lane's 2 positions of a u32 row
 #pragma unroll
     for (int r = 0; r < C::KROWS; r++)
         if (mask >> (r / C::RPP) & 1u)
-            k.kc[r] = *reinterpret_cast<const uint2 *>(kc_base + (size_t)r * cap);
+            k.kc[r] = bload2(sl.kc, vo, ((uint32_t)r * cap + (uint32_t)t0) * 4u);
     if constexpr (KF != KVQ_K_LLOYD4) {
-        const uint32_t *ksz_base = p.k_sz + (size_t)unit * C::NG * cap + tl;
 #pragma unroll
         for (int g = 0; g < C::NG; g++)
             if (mask >> (2 * g) & 3u)
-                k.ksz[g] = *reinterpret_cast<const uint2 *>(ksz_base + (size_t)g * cap);
+                k.ksz[g] = bload2(sl.ksz, vo, ((uint32_t)g * cap + (uint32_t)t0) * 4u);
         k.kx = 0;
-        if (p.ch0 && (mask & 1u))
-            k.kx = *reinterpret_cast<const uint32_t *>(p.k_ch0 + (size_t)unit * cap + tl);
+        if (mask & 1u)
+            k.kx = bload1(sl.kx, vo / 2u, (uint32_t)t0 * 2u);
     } else {
-        k.kx = *reinterpret_cast<const uint32_t *>(p.k_norm + (size_t)unit * cap + tl);
+        k.kx = bload1(sl.kx, vo / 2u, (uint32_t)t0 * 2u);
     }
-    const uint32_t *vsz_base = p.v_sz + (size_t)unit * C::NG * cap + tl;
 #pragma unroll
     for (int g = 0; g < C::NG; g++)
-        k.vsz[g] = *reinterpret_cast<const uint2 *>(vsz_base + (size_t)g * cap);
+        k.vsz[g] = bload2(sl.vsz, vo, ((uint32_t)g * cap + (uint32_t)t0) * 4u);
 }
 
 // Asymmetric-key logits of this lane's TPL positions in accumulator units:
@@ -161,13 +377,15 @@ __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const DecodeParam
 // ALL: every 16-channel row is kept (no pruning), so the row tests fold away.
 // Per (group, head, position) one int32 sum collects the hi-plane products, is shifted
 // by 8, then collects the lo-plane products: sum = 256 * hi.code + lo.code = q_int.code.
+// The query operands are uniform loads from the unit's record.
 template <int D, int G, int KF, bool ALL>
-__device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const Smem<D, G, KF> &sm, uint32_t mask,
-                                           int ch0, float (&lg)[Cfg<D, G, KF>::TPL][G])
+__device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const uint32_t *__restrict__ rec,
+                                           uint32_t mask, int ch0, float (&lg)[Cfg<D, G, KF>::TPL][G])
 {
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, NG = C::NG, TPL = C::TPL, NREG = C::NREG, QW = C::QW;
     constexpr int RPG = KROWS / NG; // key rows per scale group
+    const float *recf = reinterpret_cast<const float *>(rec);
 #pragma unroll
     for (int g = 0; g < NG; g++) {
         if (!ALL && !(mask >> (2 * g) & 3u))
@@ -208,20 +426,20 @@ __device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const Sme
                     const int r = g * RPG + rr;
                     if (!ALL && !(mask >> (r / C::RPP) & 1u))
                         continue;
-                    // broadcast LDS read of this (row, head)'s plane words into VGPRs
-                    const uint4 t4 = sm.qp[r][h][(plane * NREG) / 4];
-                    uint32_t qw[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-                    for (int i = 0; i < TPL; i++)
+                    for (int k = 0; k < NREG; k++) {
+                        const int qv = (int)rec[C::OFF_QP + (r * G + h) * QW + plane * NREG + k];
 #pragma unroll
-                        for (int k = 0; k < NREG; k++)
-                            acc[i] = __builtin_amdgcn_sdot4((int)qw[(plane * NREG) % 4 + k], (int)bsp[rr][i][k], acc[i], false);
+                        for (int i = 0; i < TPL; i++)
+                            acc[i] = __builtin_amdgcn_sdot4(qv, (int)bsp[rr][i][k], acc[i], false);
+                    }
                 }
             }
+            const float qz = recf[C::OFF_QZ + h * NG + g];
 #pragma unroll
             for (int i = 0; i < TPL; i++) {
                 const uint32_t szw = i == 0 ? cur.ksz[g].x : cur.ksz[g].y;
-                lg[i][h] = fmaf(hi_f16(szw), sm.qz[h][g], fmaf(lo_f16(szw), (float)acc[i], lg[i][h]));
+                lg[i][h] = fmaf(hi_f16(szw), qz, fmaf(lo_f16(szw), (float)acc[i], lg[i][h]));
             }
         }
     }
@@ -231,18 +449,22 @@ __device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const Sme
             const float k0 = bf16_to_f32(i == 0 ? (cur.kx & 0xFFFFu) : (cur.kx >> 16));
 #pragma unroll
             for (int h = 0; h < G; h++)
-                lg[i][h] = fmaf(k0, sm.q0[h], lg[i][h]);
+                lg[i][h] = fmaf(k0, recf[C::OFF_Q0 + h], lg[i][h]);
         }
     }
 }
 
+// Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
+// (twice the key words in flight) and 8 heads get 2.
 template <int D, int G, int KF>
-__global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kWave)
+__attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF == KVQ_K_ASYM2)) ? 3 : 2)))
+void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 {
     using C = Cfg<D, G, KF>;
-    constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
+    constexpr int KROWS = C::KROWS, NG = C::NG, NP = C::NP;
     constexpr int TPL = C::TPL, TILE = C::TILE, WPP = C::WPP, LPP = C::LPP, PPI = C::PPI;
-    constexpr int VIT = C::VIT, CPL = C::CPL, QW = C::QW, VW = C::VW;
+    constexpr int VIT = C::VIT, VW = C::VW, WV = C::WV;
     __shared__ Smem<D, G, KF> sm;
 
     const int lane = threadIdx.x;
@@ -252,169 +474,23 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
     const int kvh = unit % p.n_kv_heads;
     const size_t cap = (size_t)p.cap;
     const int n_q_heads = p.n_kv_heads * G;
+    const uint32_t *__restrict__ rec = qrec + (size_t)unit * C::QREC;
+    const float *__restrict__ recf = reinterpret_cast<const float *>(rec);
 
-    // ------------------------------------------------------------------ prologue
-    // phase 1: for each head: fp32 query in stored coordinates (FWHT when keys are
-    // rotated), 16-channel group energies and max |q|.
+    const uint32_t mask = rec[C::OFF_MASK];
+    const bool all_rows = mask == (1u << NP) - 1u;
+    float acc_to_logit[G], logit_to_acc[G];
+#pragma unroll
     for (int h = 0; h < G; h++) {
-        const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
-        float y[CPL];
-        if (p.q_bf16) {
-            const uint16_t *qb = static_cast<const uint16_t *>(p.q) + qoff;
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                y[s] = bf16_to_f32(qb[s]);
-        } else {
-            const float *qf = static_cast<const float *>(p.q) + qoff;
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                y[s] = qf[s];
-        }
-        if (p.rotate)
-            fwht_wave<CPL>(y, lane);
-        float sq[CPL], am = 0.0f;
-#pragma unroll
-        for (int s = 0; s < CPL; s++) {
-            sm.q[h][lane * CPL + s] = y[s];
-            sq[s] = y[s] * y[s];
-            am = fmaxf(am, fabsf(y[s]));
-        }
-        // stride-halving tree over the 16 channels of a group: lanes of one group are
-        // 16/CPL consecutive lanes; the xor butterfly reproduces the tree's sums.
-#pragma unroll
-        for (int m = 8 / CPL; m >= 1; m >>= 1) {
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                sq[s] = sq[s] + __shfl_xor(sq[s], m);
-            am = fmaxf(am, __shfl_xor(am, m));
-        }
-        float e = sq[0];
-        if constexpr (CPL == 2)
-            e = sq[0] + sq[1];
-        if ((lane % (16 / CPL)) == 0) {
-            sm.e[h][lane / (16 / CPL)] = e;
-            sm.amax[h][lane / (16 / CPL)] = am;
-        }
+        acc_to_logit[h] = recf[C::OFF_QSC + h];
+        logit_to_acc[h] = 1.0f / acc_to_logit[h];
     }
     if constexpr (KF == KVQ_K_LLOYD4) {
         // code-pair table: byte (lo nibble a, hi nibble b) -> fp16 (cent[a], cent[b])
         for (int e = lane; e < 256; e += kWave)
             sm.lut[e] = pack_f16x2(p.codebook[e & 15], p.codebook[e >> 4]);
+        __syncthreads();
     }
-    __syncthreads();
-
-    // phase 2 (every thread, uniform): mask, then the query scale.
-    uint32_t mask = (1u << NP) - 1u;
-    if (p.keep > 0 && p.keep < NP) {
-        float E[NP];
-#pragma unroll
-        for (int g = 0; g < NP; g++) {
-            float acc = sm.e[0][g];
-#pragma unroll
-            for (int h = 1; h < G; h++)
-                acc = acc + sm.e[h][g];
-            E[g] = acc;
-        }
-        mask = 0;
-#pragma unroll
-        for (int g = 0; g < NP; g++) {
-            int rank = 0;
-#pragma unroll
-            for (int o = 0; o < NP; o++)
-                rank += (E[o] > E[g] || (E[o] == E[g] && o < g)) ? 1 : 0;
-            if (rank < p.keep)
-                mask |= 1u << g;
-        }
-    }
-    mask = uniform(mask);
-    if (split == 0 && lane == 0 && p.mask_out)
-        p.mask_out[unit] = (uint8_t)mask;
-    const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
-    float amax = 0.0f;
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int g = 0; g < NP; g++)
-            if (mask >> g & 1u)
-                amax = fmaxf(amax, sm.amax[h][g]);
-    amax *= qscale;
-    // Lloyd-Max fp16 pair scale: the largest scaled |q| lands in [2^12, 2^13)
-    int ex = 0;
-    (void)frexpf(amax, &ex);
-    const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
-    __syncthreads();
-
-    // phase 3: scaled query, query operands and zero-term sums of every head.
-    for (int h = 0; h < G; h++) {
-#pragma unroll
-        for (int s = 0; s < CPL; s++) {
-            const int c = lane * CPL + s;
-            const bool kept = (mask >> (c / 16)) & 1u;
-            sm.q[h][c] = kept ? sm.q[h][c] * qscale : 0.0f;
-        }
-    }
-    __syncthreads();
-    for (int h = 0; h < G; h++) {
-        uint32_t *qpw = reinterpret_cast<uint32_t *>(&sm.qp[0][0][0]);
-        if constexpr (KF == KVQ_K_LLOYD4) {
-            // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
-            if (lane < KROWS * PPW) {
-                const int r = lane / PPW, j = lane % PPW;
-                const int ca = 8 * r + 2 * j;
-                qpw[(r * G + h) * QW + j] = pack_f16x2(sm.q[h][ca] * g2, sm.q[h][ca + 1] * g2);
-            }
-            if (lane == 0)
-                sm.qsc[h] = 1.0f / g2;
-        } else {
-            // 16-bit integer query: q ~= qi * unit, |qi| <= 32639, written as 256*hi + lo
-            // with signed bytes hi, lo.  Channel 0 is scored from its BF16 copy instead.
-            float am = 0.0f;
-#pragma unroll
-            for (int s2 = 0; s2 < CPL; s2++) {
-                const int c = lane * CPL + s2;
-                if (!(p.ch0 && c == 0))
-                    am = fmaxf(am, fabsf(sm.q[h][c]));
-            }
-            am = wave_max_dpp(am);
-            const float unit_q = am > 0.0f ? am / 32639.0f : 1.0f;
-            const float inv = 1.0f / unit_q;
-            // key word r, spread register k: byte m holds channel r*(32/KB) + m*(KB==2 ? 4 : 2) + k
-            if (lane < KROWS * C::NREG) {
-                const int r = lane / C::NREG, k = lane % C::NREG;
-                uint32_t hi = 0, lo = 0;
-#pragma unroll
-                for (int m = 0; m < 4; m++) {
-                    const int c = (KB == 2) ? 16 * r + 4 * m + k : 8 * r + 2 * m + k;
-                    const float qv = (p.ch0 && c == 0) ? 0.0f : sm.q[h][c];
-                    const int qi = (int)__builtin_rintf(qv * inv);
-                    const int h8 = (qi + 128) >> 8;
-                    const int l8 = qi - 256 * h8;
-                    hi |= (uint32_t)(h8 & 0xFF) << (8 * m);
-                    lo |= (uint32_t)(l8 & 0xFF) << (8 * m);
-                }
-                // word layout per (row, head): hi planes of regs 0..NREG-1, then lo planes
-                qpw[(r * G + h) * QW + k] = hi;
-                qpw[(r * G + h) * QW + C::NREG + k] = lo;
-            }
-            if (lane < NG) {
-                float si = 0.0f;
-                for (int c = 32 * lane; c < 32 * lane + 32; c++)
-                    if (!(p.ch0 && c == 0))
-                        si += __builtin_rintf(sm.q[h][c] * inv);
-                sm.qz[h][lane] = si;
-            }
-            if (lane == 0) {
-                sm.qsc[h] = unit_q;
-                sm.q0[h] = (p.ch0 && (mask & 1u)) ? sm.q[h][0] * inv : 0.0f;
-            }
-        }
-    }
-    __syncthreads();
-    float acc_to_logit[G];
-#pragma unroll
-    for (int h = 0; h < G; h++)
-        acc_to_logit[h] = sm.qsc[h];
-    const bool all_rows = mask == (1u << NP) - 1u;
 
     // ------------------------------------------------------------------ state
     const int vs = lane % LPP;         // value slot: channels 8*vs .. 8*vs+7
@@ -422,11 +498,12 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
     float acc[G][8];
     float zacc[G][NG];
     float lsum[G];
-    float mrun[G];
+    float mrun[G], mthr[G];
 #pragma unroll
     for (int h = 0; h < G; h++) {
         lsum[h] = 0.0f;
         mrun[h] = -__builtin_inff();
+        mthr[h] = -__builtin_inff();
 #pragma unroll
         for (int j = 0; j < 8; j++)
             acc[h][j] = 0.0f;
@@ -451,18 +528,19 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
                 const float k0 = bf16_to_f32(w & 0xFFFFu), k1 = bf16_to_f32(w >> 16);
 #pragma unroll
                 for (int h = 0; h < G; h++)
-                    sl[h] = fmaf(sm.q[h][c + 1], k1, fmaf(sm.q[h][c], k0, sl[h]));
+                    sl[h] = fmaf(recf[C::OFF_QF + h * D + c + 1], k1, fmaf(recf[C::OFF_QF + h * D + c], k0, sl[h]));
             }
         }
 #pragma unroll
         for (int h = 0; h < G; h++) {
             const float x = valid ? sl[h] : -__builtin_inff();
             mrun[h] = wave_max_dpp(x);
+            mthr[h] = mrun[h] * logit_to_acc[h];
             const float pr = valid ? __builtin_amdgcn_exp2f(x - mrun[h]) : 0.0f;
             lsum[h] += pr;
             sm.sink_p[h][lane] = pr;
         }
-        __builtin_amdgcn_wave_barrier();
+        __syncthreads();
         for (int t = lane / LPP; t < n_sink; t += PPI) {
             const uint16_t *sv = p.sink_v + ((size_t)unit * p.n_sink + t) * D + 8 * vs;
 #pragma unroll
@@ -481,19 +559,38 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
     if (t_last > p.tile_end)
         t_last = p.tile_end;
     const int q_lo = p.n_sink, q_hi = p.len; // quantized positions [q_lo, q_hi)
-    const uint32_t *vc_base = p.v_codes + (size_t)unit * (cap / 2) * WPP + VW * vs;
-    uint32_t(&wl)[NG * G][C::WROW] = sm.w;
+    const uint32_t ucap = (uint32_t)p.cap;
+    Slabs sl;
+    sl.kc = make_rsrc(p.k_codes + (size_t)unit * KROWS * cap, (uint32_t)KROWS * ucap * 4u);
+    sl.vsz = make_rsrc(p.v_sz + (size_t)unit * NG * cap, (uint32_t)NG * ucap * 4u);
+    sl.vc = make_rsrc(p.v_codes + (size_t)unit * (cap / 2) * WPP, (ucap / 2u) * WPP * 4u);
+    if constexpr (KF != KVQ_K_LLOYD4) {
+        sl.ksz = make_rsrc(p.k_sz + (size_t)unit * NG * cap, (uint32_t)NG * ucap * 4u);
+        sl.kx = p.ch0 ? make_rsrc(p.k_ch0 + (size_t)unit * cap, ucap * 2u) : make_rsrc(p.k_codes, 0u);
+    } else {
+        sl.ksz = make_rsrc(p.k_codes, 0u);
+        sl.kx = make_rsrc(p.k_norm + (size_t)unit * cap, ucap * 2u);
+    }
+    const Slabs none = {make_rsrc(p.k_codes, 0u), make_rsrc(p.k_codes, 0u), make_rsrc(p.k_codes, 0u),
+                        make_rsrc(p.k_codes, 0u), make_rsrc(p.k_codes, 0u)};
+    // value words: lane's pair row and channel slot
+    const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u;
 
+    // value words of the current tile: word pair `it` is reloaded with the next tile's
+    // right after its last use, so each load has a whole tile of work to arrive
+    uint2 vcur[VIT];
     KTile<D, G, KF> cur;
     int tile = t_first;
-    if (tile < t_last)
-        load_ktile<D, G, KF>(cur, p, unit, tile * TILE + lane * TPL, mask);
+    {
+        const Slabs &s0 = tile < t_last ? sl : none;
+        load_ktile<D, G, KF>(cur, s0, ucap, lane, tile * TILE, mask);
+#pragma unroll
+        for (int it = 0; it < VIT; it++)
+            vcur[it] = bload2(s0.vc, vvo, ((uint32_t)(tile * TILE / 2 + it * PPI) * WPP) * 4u);
+    }
     for (; tile < t_last; tile++) {
         const int t0 = tile * TILE;
         const int tl = t0 + lane * TPL;
-        // keep the per-(row, head) query reads inside the loop: hoisting all of them out
-        // would pin KROWS*G*QW registers for the whole loop
-        asm volatile("" ::: "memory");
 
         // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h])
         float lg[TPL][G];
@@ -504,9 +601,9 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
                 lg[i][h] = 0.0f;
         if constexpr (KF != KVQ_K_LLOYD4) {
             if (all_rows)
-                score_asym<D, G, KF, true>(cur, sm, mask, p.ch0, lg);
+                score_asym<D, G, KF, true>(cur, rec, mask, p.ch0, lg);
             else
-                score_asym<D, G, KF, false>(cur, sm, mask, p.ch0, lg);
+                score_asym<D, G, KF, false>(cur, rec, mask, p.ch0, lg);
         } else {
 #pragma unroll
             for (int r = 0; r < KROWS; r++) {
@@ -521,15 +618,14 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
                         pr[i][j] = sm.lut[(x >> (8 * j)) & 0xFFu];
                 }
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    const uint4 qv = sm.qp[r][h][0];
-                    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+                for (int h = 0; h < G; h++)
 #pragma unroll
-                    for (int i = 0; i < TPL; i++)
+                    for (int j = 0; j < 4; j++) {
+                        const uint32_t qv = rec[C::OFF_QP + (r * G + h) * C::QW + j];
 #pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            lg[i][h] = dot2(pr[i][j], qw[j], lg[i][h]);
-                }
+                        for (int i = 0; i < TPL; i++)
+                            lg[i][h] = dot2(pr[i][j], qv, lg[i][h]);
+                    }
             }
 #pragma unroll
             for (int i = 0; i < TPL; i++) {
@@ -540,17 +636,14 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
             }
         }
 
-        // ---- value scale/zero of this lane's positions; mask positions outside
-        // [q_lo, q_hi) (their slots may hold anything)
-        float vs_s[TPL][NG], vs_z[TPL][NG];
+        // ---- value scale/zero of this lane's positions; positions outside [q_lo, q_hi)
+        // get logit -inf and scale/zero 0 (their slots may hold anything)
+        uint32_t vsw[TPL][NG];
 #pragma unroll
-        for (int i = 0; i < TPL; i++)
-#pragma unroll
-            for (int g = 0; g < NG; g++) {
-                const uint32_t szw = i == 0 ? cur.vsz[g].x : cur.vsz[g].y;
-                vs_s[i][g] = lo_f16(szw);
-                vs_z[i][g] = hi_f16(szw);
-            }
+        for (int g = 0; g < NG; g++) {
+            vsw[0][g] = cur.vsz[g].x;
+            vsw[1][g] = cur.vsz[g].y;
+        }
         const bool full = (t0 >= q_lo) && (t0 + TILE <= q_hi);
         if (!full) {
 #pragma unroll
@@ -561,38 +654,38 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
                     for (int h = 0; h < G; h++)
                         lg[i][h] = -__builtin_inff();
 #pragma unroll
-                    for (int g = 0; g < NG; g++) {
-                        vs_s[i][g] = 0.0f;
-                        vs_z[i][g] = 0.0f;
-                    }
+                    for (int g = 0; g < NG; g++)
+                        vsw[i][g] = 0u;
                 }
             }
         }
 
         // ---- next tile's key-side words, into the registers this tile no longer needs:
         // in flight during the rest of this tile
-        if (tile + 1 < t_last)
-            load_ktile<D, G, KF>(cur, p, unit, (tile + 1) * TILE + lane * TPL, mask);
+        const Slabs &nx = tile + 1 < t_last ? sl : none;
+        load_ktile<D, G, KF>(cur, nx, ucap, lane, t0 + TILE, mask);
 
         // ---- online softmax (log2 units); wave-wide max only when some logit exceeds
         // the running maximum
-        float lmax[G];
-        bool above = false;
+        // (the test compares in accumulator units against mthr = mrun / acc_to_logit; a
+        // rounding miss only lets a weight exceed 1 by an ulp)
+        uint64_t above = 0;
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            float mt = lg[0][h];
+        for (int h = 0; h < G; h++)
 #pragma unroll
-            for (int i = 1; i < TPL; i++)
-                mt = fmaxf(mt, lg[i][h]);
-            lmax[h] = mt * acc_to_logit[h];
-            above |= lmax[h] > mrun[h];
-        }
-        if (__any(above)) {
+            for (int i = 0; i < TPL; i++)
+                above |= __ballot(lg[i][h] > mthr[h]);
+        if (above) {
 #pragma unroll
             for (int h = 0; h < G; h++) {
-                const float mnew = fmaxf(mrun[h], wave_max_dpp(lmax[h]));
+                float mt = lg[0][h];
+#pragma unroll
+                for (int i = 1; i < TPL; i++)
+                    mt = fmaxf(mt, lg[i][h]);
+                const float mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
                 const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);
                 mrun[h] = mnew;
+                mthr[h] = mnew * logit_to_acc[h];
                 lsum[h] *= alpha;
 #pragma unroll
                 for (int j = 0; j < 8; j++)
@@ -610,33 +703,50 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
                 pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -mrun[h]));
                 lsum[h] += pw[i][h];
             }
+        // zero-point term and the fp16 weights p*s of this lane's position pair (-> LDS),
+        // from the weights rounded to fp16 pairs: one packed product and one dot2 per
+        // (group, head)
+        uint32_t ph[G];
 #pragma unroll
         for (int h = 0; h < G; h++)
+            ph[h] = pack_f16x2(pw[0][h], pw[1][h]);
 #pragma unroll
-            for (int g = 0; g < NG; g++)
+        for (int g = 0; g < NG; g++) {
+            const uint32_t sp = __builtin_amdgcn_perm(vsw[1][g], vsw[0][g], 0x05040100u); // (s0, s1)
+            const uint32_t zp = __builtin_amdgcn_perm(vsw[1][g], vsw[0][g], 0x07060302u); // (z0, z1)
+            uint32_t wq[4 * WV];
 #pragma unroll
-                for (int i = 0; i < TPL; i++)
-                    zacc[h][g] = fmaf(pw[i][h], vs_z[i][g], zacc[h][g]);
-        // weights p*s as fp16 pairs over positions (2m, 2m+1) -> LDS row (g, h), column pair
+            for (int h = 0; h < G; h++) {
+                zacc[h][g] = dot2(ph[h], zp, zacc[h][g]);
+                wq[h] = mul_f16x2(ph[h], sp);
+            }
 #pragma unroll
-        for (int g = 0; g < NG; g++)
+            for (int h = G; h < 4 * WV; h++)
+                wq[h] = 0u;
 #pragma unroll
-            for (int h = 0; h < G; h++)
-                wl[g * G + h][lane] = pack_f16x2(pw[0][h] * vs_s[0][g], pw[1][h] * vs_s[1][g]);
+            for (int v4 = 0; v4 < WV; v4++)
+                sm.w[g][lane][v4] = make_uint4(wq[4 * v4], wq[4 * v4 + 1], wq[4 * v4 + 2], wq[4 * v4 + 3]);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // ---- values: lane owns channels 8*vs .. 8*vs+7 of one pair per iteration
-        const uint32_t *vrow = vc_base + (size_t)(t0 / 2 + lane / LPP) * WPP;
+        const uint32_t vnext = (uint32_t)((t0 + TILE) / 2) * WPP * 4u;
 #pragma unroll
         for (int it = 0; it < VIT; it++) {
-            const uint2 vv = *reinterpret_cast<const uint2 *>(vrow + (size_t)it * PPI * WPP);
+            const uint2 vv = vcur[it];
+            vcur[it] = bload2(nx.vc, vvo, vnext + (uint32_t)(it * PPI * WPP) * 4u);
             const int pl = it * PPI + lane / LPP;
-            uint32_t wv[G];
+            uint32_t wv[4 * WV];
 #pragma unroll
-            for (int h = 0; h < G; h++)
-                wv[h] = wl[vgrp * G + h][pl];
+            for (int v4 = 0; v4 < WV; v4++) {
+                const uint4 t4 = sm.w[vgrp][pl][v4];
+                wv[4 * v4 + 0] = t4.x;
+                wv[4 * v4 + 1] = t4.y;
+                wv[4 * v4 + 2] = t4.z;
+                wv[4 * v4 + 3] = t4.w;
+            }
 #pragma unroll
             for (int q2 = 0; q2 < 2; q2++) {
                 const uint32_t x = q2 == 0 ? vv.x : vv.y;
@@ -701,8 +811,9 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeParams p)
     }
 }
 
-// Split merge: one thread per (sequence, query head, channel) combines the per-split
-// (m, l, o) partials -- one global softmax over all positions (Dual-QK sec. 3.4).
+// ===================================================================== split merge
+// One thread per (sequence, query head, channel) combines the per-split (m, l, o) partials:
+// one global softmax over all positions (Dual-QK sec. 3.4).
 template <int D, int G>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
 {
@@ -727,16 +838,20 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
     p.out[oi] = L > 0.0f ? O / L : 0.0f;
 }
 
+// ===================================================================== launchers
 template <int D, int G, int KF>
 hipError_t launch_one(int units, const DecodeParams &p, hipStream_t s)
 {
-    dim3 grid((unsigned)p.n_split, (unsigned)units), block(kWave);
-    hipLaunchKernelGGL((decode_kernel<D, G, KF>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave), 0, s, p);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((decode_kernel<D, G, KF>), dim3((unsigned)p.n_split, (unsigned)units), dim3(kWave), 0, s,
+                       p, static_cast<const uint32_t *>(p.qprep));
+    e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1)
         return e;
-    dim3 mgrid((unsigned)G, (unsigned)units), mblock(D);
-    hipLaunchKernelGGL((merge_kernel<D, G>), mgrid, mblock, 0, s, p);
+    hipLaunchKernelGGL((merge_kernel<D, G>), dim3((unsigned)G, (unsigned)units), dim3(D), 0, s, p);
     return hipGetLastError();
 }
 
@@ -779,7 +894,27 @@ const void *kernel_g(int group, int kfmt)
            : group == 4 ? kernel_kf<D, 4>(kfmt) : kernel_kf<D, 8>(kfmt);
 }
 
+template <int D, int G>
+int qrec_kf(int kfmt)
+{
+    return kfmt == KVQ_K_ASYM2 ? Cfg<D, G, KVQ_K_ASYM2>::QREC
+           : kfmt == KVQ_K_ASYM4 ? Cfg<D, G, KVQ_K_ASYM4>::QREC
+                                 : Cfg<D, G, KVQ_K_LLOYD4>::QREC;
+}
+
+template <int D>
+int qrec_g(int group, int kfmt)
+{
+    return group == 1 ? qrec_kf<D, 1>(kfmt) : group == 2 ? qrec_kf<D, 2>(kfmt)
+           : group == 4 ? qrec_kf<D, 4>(kfmt) : qrec_kf<D, 8>(kfmt);
+}
+
 } // namespace
+
+int decode_qrec_words(int head_dim, int group, int kfmt)
+{
+    return head_dim == 128 ? qrec_g<128>(group, kfmt) : qrec_g<64>(group, kfmt);
+}
 
 int decode_slots(int head_dim, int group, int kfmt)
 {

@@ -44,6 +44,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// packed fp16 product of two pairs (round to nearest even per half)
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) * __builtin_bit_cast(h2, b));
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);

@@ -34,6 +34,7 @@ struct DecodeParams {
     float *out;
     uint8_t *mask_out;
     float *part;        // split partials [U][n_split][G][D + 2]
+    uint32_t *qprep;    // per-unit query record written by the query-prep kernel
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
     float sm_log2e;      // softmax scale times log2(e)
     int n_split, tile_begin, tile_end, tiles_per_split;
@@ -42,6 +43,8 @@ struct DecodeParams {
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
 hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
                          hipStream_t s);
+// u32 words of one unit's query record (query-prep output read by the decode kernel).
+int decode_qrec_words(int head_dim, int group, int kfmt);
 // Resident decode workgroups (one wave each) the device holds for this instantiation.
 int decode_slots(int head_dim, int group, int kfmt);
 
