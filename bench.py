@@ -77,6 +77,53 @@ def traffic_record():
         return None
 
 
+def _counter_per_dispatch(path, want):
+    """Per-dispatch totals (summed over dimensions) of the one counter in a rocprofv3
+    --pmc CSV, for dispatches whose kernel name satisfies want(name)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if want(r["Kernel_Name"]):
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{path}: no matching dispatch")
+    return list(per.values())
+
+
+def write_traffic(dec_fetch, dec_write, copy_fetch, copy_write, out_path, copy_bytes=1 << 30):
+    """Reduce FETCH_SIZE / WRITE_SIZE counter runs (KiB per dispatch) of the decode kernel
+    and of the --copy-probe copy (copy_bytes read and written per dispatch) to HBM bytes per
+    decode launch: each counter is scaled by what it reads for the copy of known size."""
+    is_dec = lambda n: "decode_kernel" in n
+    is_copy = lambda n: "copy" in n.lower() and "fill" not in n.lower()
+    f = _counter_per_dispatch(dec_fetch, is_dec)
+    wr = _counter_per_dispatch(dec_write, is_dec)
+    cf = _counter_per_dispatch(copy_fetch, is_copy)
+    cw = _counter_per_dispatch(copy_write, is_copy)
+    fetch_kib, write_kib = sum(f) / len(f), sum(wr) / len(wr)
+    cf_kib, cw_kib = sum(cf) / len(cf), sum(cw) / len(cw)
+    ff, wf = copy_bytes / (cf_kib * 1024), copy_bytes / (cw_kib * 1024)
+    hbm = fetch_kib * 1024 * ff + write_kib * 1024 * wf
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    lines = [
+        "# HBM traffic of one decode_kernel launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE counters",
+        "# (KiB per dispatch, each counter in its own run), scaled by the same counters on a copy of",
+        f"# {copy_bytes} bytes (python bench.py --copy-probe).  Valid only for the decode source whose",
+        "# sha256 is recorded below: bench.py ignores this file once the kernel changes.",
+        f"decode_source_sha256: {sha}",
+        f"decode_dispatches: {len(f)} fetch, {len(wr)} write",
+        f"fetch_kib_per_launch: {fetch_kib:.1f}",
+        f"write_kib_per_launch: {write_kib:.1f}",
+        f"copy_fetch_kib: {cf_kib:.1f}",
+        f"copy_write_kib: {cw_kib:.1f}",
+        f"fetch_scale: {ff:.4f}",
+        f"write_scale: {wf:.4f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+    ]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, length, budget_s):
     """The oracle (plain C, fp64 attention) on a bounded sample of the same workload:
     a few sequences at the bench's context length, timed over append + decode steps."""
@@ -128,7 +175,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--traffic-csv", nargs=4, metavar=("DEC_FETCH", "DEC_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="reduce rocprofv3 counter CSVs to the decode kernel's HBM bytes per launch, "
+                         "write the traffic record and exit (no GPU use)")
     args = ap.parse_args()
+    if args.traffic_csv:
+        write_traffic(*args.traffic_csv, out_path=TRAFFIC_FILE)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

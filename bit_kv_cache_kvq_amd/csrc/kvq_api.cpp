@@ -31,6 +31,11 @@ kvq_status check_geometry(const kvq_cache *c)
         return KVQ_ERR_UNSUPPORTED;
     if (c->capacity % kCapacityQuantum != 0)
         return KVQ_ERR_UNSUPPORTED;
+    // per-unit slabs are addressed with 32-bit byte offsets (at most 16 words per position)
+    // and the decode work split counts tiles of all units in 32 bits
+    if (c->capacity > kMaxCapacity ||
+        (long long)c->batch * c->n_kv_heads * (c->capacity / kTile) >= (1ll << 31))
+        return KVQ_ERR_UNSUPPORTED;
     if (c->n_sink < 0 || c->n_sink > kMaxSink || c->n_sink >= c->capacity)
         return KVQ_ERR_UNSUPPORTED;
     if (c->k_format < KVQ_K_ASYM2 || c->k_format > KVQ_K_LLOYD4)
@@ -82,53 +87,47 @@ kvq_status check_buffers(const kvq_cache *c)
 }
 
 struct Plan {
-    int tile_begin, tile_end, n_tiles, n_split, tiles_per_split;
+    int tiles_per_unit, n_waves;
+    bool merge; // some unit is shared by several waves
 };
 
-// Split planner: one wave per split.  Enough splits that every resident wave slot of the
-// device holds one (slots = resident one-wave workgroups of the kernel instantiation), and
-// at most kSplitTiles tiles per split so long contexts keep more waves than slots (the
-// spare waves fill the gaps the finishing ones leave); the tiles are divided evenly.
-constexpr int kSplitTiles = 16;
-
+// Work split of one decode call.  Every unit's positions [0, len) are cut into 128-position
+// tiles (at least one, so sink-only and empty contexts still produce their output); the
+// tiles of all units, unit after unit, are cut into n_waves contiguous ranges of equal
+// size (+-1 tile), one per decode wave.  n_waves = the resident one-wave workgroups of the
+// kernel instantiation (`slots`), so one pass of waves covers the device with no tail, or
+// fewer when there are fewer tiles.  kvq_set_split_tiles overrides it with a target
+// number of tiles per wave.
 Plan plan_splits(const kvq_cache *c, int len, int slots)
 {
     Plan pl;
-    const int n_sink = c->n_sink < len ? c->n_sink : len;
-    pl.tile_begin = n_sink / kTile;
-    pl.tile_end = (len + kTile - 1) / kTile;
-    if (len <= n_sink)
-        pl.tile_end = pl.tile_begin; // only sink positions
-    pl.n_tiles = pl.tile_end - pl.tile_begin;
-    if (pl.n_tiles <= 0) {
-        pl.n_split = 1;
-        pl.tiles_per_split = 0;
-        return pl;
-    }
-    const long long units = (long long)units_of(c);
-    int tps = g_split_tiles.load();
-    if (tps <= 0) {
-        long long want_split = (slots + units / 2) / units;
-        const long long by_len = (pl.n_tiles + kSplitTiles - 1) / kSplitTiles;
-        if (want_split < by_len)
-            want_split = by_len;
-        if (want_split > pl.n_tiles)
-            want_split = pl.n_tiles;
-        if (want_split < 1)
-            want_split = 1;
-        tps = (int)((pl.n_tiles + want_split - 1) / want_split);
-    }
-    if (tps > pl.n_tiles)
-        tps = pl.n_tiles;
-    pl.tiles_per_split = tps;
-    pl.n_split = (pl.n_tiles + tps - 1) / tps;
+    pl.tiles_per_unit = (len + kTile - 1) / kTile;
+    if (pl.tiles_per_unit < 1)
+        pl.tiles_per_unit = 1;
+    const long long total = (long long)units_of(c) * pl.tiles_per_unit;
+    long long W = slots > 0 ? slots : 1;
+    const int tps = g_split_tiles.load();
+    if (tps > 0)
+        W = (total + tps - 1) / tps;
+    if (W > total)
+        W = total;
+    if (W > kMaxWaves)
+        W = kMaxWaves;
+    if (W < 1)
+        W = 1;
+    pl.n_waves = (int)W;
+    // every unit sits whole in one wave when units are single tiles, or when the ranges are
+    // equal whole multiples of a unit
+    pl.merge = !(pl.tiles_per_unit == 1 || (total % W == 0 && (total / W) % pl.tiles_per_unit == 0));
     return pl;
 }
 
-int max_splits(const kvq_cache *c)
+// Partial-state slots: slot = wave + unit < max waves + units.
+size_t part_slots(const kvq_cache *c)
 {
-    // the planner never exceeds one split per tile of the full capacity
-    return c->capacity / kTile;
+    const long long max_tiles = (long long)units_of(c) * (c->capacity / kTile);
+    const long long w = max_tiles < kMaxWaves ? max_tiles : kMaxWaves;
+    return (size_t)w + units_of(c);
 }
 
 } // namespace
@@ -209,10 +208,10 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace: split partials [U][max splits][G][D + 2] fp32, then the query records
+// workspace: partial softmax states [slots][G][D + 2] fp32, then the query records
 static size_t part_region_bytes(const kvq_cache *c, int G)
 {
-    return round256(units_of(c) * (size_t)max_splits(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float));
+    return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float));
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
@@ -232,7 +231,7 @@ int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
     const int G = n_q_heads / c->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return 0;
-    return plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format)).n_split;
+    return plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format)).n_waves;
 }
 
 kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
@@ -285,11 +284,10 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.keep = keep_groups;
     p.q_bf16 = q_dtype == KVQ_BF16;
     p.sm_log2e = sm_scale * 1.4426950408889634f;
-    p.n_split = pl.n_split;
-    p.tile_begin = pl.tile_begin;
-    p.tile_end = pl.tile_end;
-    p.tiles_per_split = pl.tiles_per_split;
-    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, (hipStream_t)stream) != hipSuccess)
+    p.n_units = (int)U;
+    p.tiles_per_unit = pl.tiles_per_unit;
+    p.n_waves = pl.n_waves;
+    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, pl.merge, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
     return KVQ_OK;
 }

@@ -68,14 +68,15 @@ struct Cfg {
     static constexpr int WV = (G + 3) / 4;         // uint4 of fp16 weight pairs per (group, pair)
     // query record, u32 words per unit: mask; per head the accumulator unit (log2-logit
     // per accumulator step) and the channel-0 coefficient; zero-term sums [G][NG]; query
-    // operands [KROWS][G][QW]; scaled masked fp32 query [G][D] (sink positions)
+    // operands [KROWS][G][QW]; the softmax state (m, l, o[D]) of the BF16 sink positions
+    // per head [G][D + 2]
     static constexpr int OFF_MASK = 0;
     static constexpr int OFF_QSC = 4;
     static constexpr int OFF_Q0 = OFF_QSC + G;
     static constexpr int OFF_QZ = OFF_Q0 + G;
     static constexpr int OFF_QP = (OFF_QZ + G * NG + 7) / 8 * 8;
-    static constexpr int OFF_QF = OFF_QP + KROWS * G * QW;
-    static constexpr int QREC = (OFF_QF + G * D + 63) / 64 * 64;
+    static constexpr int OFF_SINK = OFF_QP + KROWS * G * QW;
+    static constexpr int QREC = (OFF_SINK + G * (D + 2) + 63) / 64 * 64;
     static_assert(TILE == kTile, "host and device tile must agree");
 };
 
@@ -95,6 +96,25 @@ __device__ __forceinline__ float wave_max_dpp(float v)
     v = dpp_max_step<0x118, 0xF>(v); // row_shr:8
     v = dpp_max_step<0x142, 0xA>(v); // row_bcast:15
     v = dpp_max_step<0x143, 0xC>(v); // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_add_step(float x)
+{
+    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xF, false);
+    return x + __int_as_float(o);
+}
+
+// sum over the wave, result uniform (DPP row shifts, then row broadcasts to lane 63)
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    v = dpp_add_step<0x111, 0xF>(v); // row_shr:1
+    v = dpp_add_step<0x112, 0xF>(v); // row_shr:2
+    v = dpp_add_step<0x114, 0xF>(v); // row_shr:4
+    v = dpp_add_step<0x118, 0xF>(v); // row_shr:8
+    v = dpp_add_step<0x142, 0xA>(v); // row_bcast:15
+    v = dpp_add_step<0x143, 0xC>(v); // row_bcast:31
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
@@ -118,14 +138,16 @@ __device__ __forceinline__ void fwht_wave(float (&y)[CPL], int lane)
 }
 
 // Cache reads are raw buffer loads: one descriptor per (unit, array) holds the unit's slab
-// (base, byte size), the lane part of the offset is a VGPR and the position part an SGPR,
-// so no 64-bit address arithmetic runs on the VALU.  An access at or beyond the slab size
-// returns zero without touching memory; a descriptor of size 0 turns a prefetch past the
-// last tile into a no-op without a branch.  All of them are non-temporal (read once).
+// (base, byte size below 2^30), the lane part of the offset is a VGPR and the position part
+// an SGPR, so no 64-bit address arithmetic runs on the VALU.  An access whose lane offset
+// is at or beyond the slab size returns zero without touching memory: adding kNoAccess to
+// the lane offset turns a prefetch past the last tile into a no-op without a branch.  All
+// of them are non-temporal (read once).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 constexpr int kBufWord3 = 0x00020000; // raw 32-bit access, no format conversion
 constexpr int kNonTemporal = 2;
+constexpr uint32_t kNoAccess = 0x80000000u;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -154,6 +176,7 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
     __shared__ float sq_[G][D];
     __shared__ float se[G][NP];
     __shared__ float sam[G][NP];
+    __shared__ float sp[G][kWave];
 
     const int lane = threadIdx.x;
     const int unit = blockIdx.x;
@@ -237,18 +260,84 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
     }
     const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
 
-    // scaled, masked fp32 query (the sink positions use it directly)
+    // scaled, masked fp32 query
     for (int h = 0; h < G; h++) {
 #pragma unroll
         for (int s = 0; s < CPL; s++) {
             const int c = lane * CPL + s;
             const bool kept = (mask >> (c / 16)) & 1u;
-            const float v = kept ? sq_[h][c] * qscale : 0.0f;
-            sq_[h][c] = v;
-            recf[C::OFF_QF + h * D + c] = v;
+            sq_[h][c] = kept ? sq_[h][c] * qscale : 0.0f;
         }
     }
     __syncthreads();
+
+    // BF16 sink positions (t < min(n_sink, len)): dense dot over the kept channels, then
+    // their softmax state per head -- log2 max m, sum l and o = sum_t 2^(l_t - m) v_t --
+    // which the decode and merge kernels fold into the unit's result.  Lanes own channels;
+    // one wave-wide sum per (sink, head) gives the logits, lane t keeps those of sink t.
+    {
+        const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
+        float qr[G][CPL], mine[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            mine[h] = -__builtin_inff();
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                qr[h][s] = sq_[h][lane * CPL + s];
+        }
+        for (int t = 0; t < n_sink; t++) {
+            const uint16_t *sk = p.sink_k + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
+            float kv[CPL];
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                kv[s] = bf16_to_f32(sk[s]);
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                float part = 0.0f;
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    part = fmaf(qr[h][s], kv[s], part);
+                const float tot = wave_sum_dpp(part);
+                mine[h] = lane == t ? tot : mine[h];
+            }
+        }
+        float l[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const float m = wave_max_dpp(mine[h]);
+            const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine[h] - m) : 0.0f;
+            sp[h][lane] = pr;
+            l[h] = wave_sum_dpp(pr);
+            if (lane == 0) {
+                recf[C::OFF_SINK + h * (D + 2)] = m;
+                recf[C::OFF_SINK + h * (D + 2) + 1] = l[h];
+            }
+        }
+        __syncthreads();
+        float o[G][CPL];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                o[h][s] = 0.0f;
+        for (int t = 0; t < n_sink; t++) {
+            const uint16_t *sv = p.sink_v + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
+            float vv[CPL];
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                vv[s] = bf16_to_f32(sv[s]);
+#pragma unroll
+            for (int h = 0; h < G; h++)
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    o[h][s] = fmaf(sp[h][t], vv[s], o[h][s]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                recf[C::OFF_SINK + h * (D + 2) + 2 + lane * CPL + s] = o[h][s];
+    }
 
     if constexpr (KF == KVQ_K_LLOYD4) {
         // fp16 pairs scaled so the largest kept |q| lands in [2^12, 2^13); byte j of key
@@ -346,12 +435,13 @@ struct Slabs {
     rsrc_t kc, ksz, kx, vsz, vc;
 };
 
+// off: 0, or kNoAccess to turn every load into a zero without a memory access
 template <int D, int G, int KF>
 __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, uint32_t cap, int lane, int t0,
-                                           uint32_t mask)
+                                           uint32_t mask, uint32_t off)
 {
     using C = Cfg<D, G, KF>;
-    const uint32_t vo = (uint32_t)lane * C::TPL * 4u;  // lane's 2 positions of a u32 row
+    const uint32_t vo = (uint32_t)lane * C::TPL * 4u + off;  // lane's 2 positions of a u32 row
 #pragma unroll
     for (int r = 0; r < C::KROWS; r++)
         if (mask >> (r / C::RPP) & 1u)
@@ -363,9 +453,9 @@ __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, 
                 k.ksz[g] = bload2(sl.ksz, vo, ((uint32_t)g * cap + (uint32_t)t0) * 4u);
         k.kx = 0;
         if (mask & 1u)
-            k.kx = bload1(sl.kx, vo / 2u, (uint32_t)t0 * 2u);
+            k.kx = bload1(sl.kx, (uint32_t)lane * C::TPL * 2u + off, (uint32_t)t0 * 2u);
     } else {
-        k.kx = bload1(sl.kx, vo / 2u, (uint32_t)t0 * 2u);
+        k.kx = bload1(sl.kx, (uint32_t)lane * C::TPL * 2u + off, (uint32_t)t0 * 2u);
     }
 #pragma unroll
     for (int g = 0; g < C::NG; g++)
@@ -454,8 +544,50 @@ __device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const uin
     }
 }
 
+// Descriptors of unit u's slabs.
+template <int D, int G, int KF>
+__device__ __forceinline__ Slabs unit_slabs(const DecodeParams &p, int u)
+{
+    using C = Cfg<D, G, KF>;
+    const size_t cap = (size_t)p.cap;
+    const uint32_t ucap = (uint32_t)p.cap;
+    Slabs sl;
+    sl.kc = make_rsrc(p.k_codes + (size_t)u * C::KROWS * cap, (uint32_t)C::KROWS * ucap * 4u);
+    sl.vsz = make_rsrc(p.v_sz + (size_t)u * C::NG * cap, (uint32_t)C::NG * ucap * 4u);
+    sl.vc = make_rsrc(p.v_codes + (size_t)u * (cap / 2) * C::WPP, (ucap / 2u) * C::WPP * 4u);
+    if constexpr (KF != KVQ_K_LLOYD4) {
+        sl.ksz = make_rsrc(p.k_sz + (size_t)u * C::NG * cap, (uint32_t)C::NG * ucap * 4u);
+        sl.kx = p.ch0 ? make_rsrc(p.k_ch0 + (size_t)u * cap, ucap * 2u) : make_rsrc(p.k_codes, 0u);
+    } else {
+        sl.ksz = make_rsrc(p.k_codes, 0u);
+        sl.kx = make_rsrc(p.k_norm + (size_t)u * cap, ucap * 2u);
+    }
+    return sl;
+}
+
+// First global tile of wave w when `total` tiles (unit-major: unit u owns tiles
+// u*Tu .. u*Tu+Tu-1) are cut into W contiguous, equal (+-1) ranges.
+__device__ __forceinline__ int wave_first_tile(int w, long long total, int W)
+{
+    return (int)((long long)w * total / W);
+}
+
+// Last wave whose range starts at or before global tile x.
+__device__ __forceinline__ int wave_of_tile(long long x, long long total, int W)
+{
+    return (int)(((x + 1) * W + total - 1) / total) - 1;
+}
+
 // Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
 // (twice the key words in flight) and 8 heads get 2.
+//
+// Work split: the grid holds one wave per resident slot of the device (or fewer for small
+// inputs).  The tiles of all units, unit after unit, are cut into one contiguous range per
+// wave, equal to within one tile, so every wave ends at the same time whatever the shape.
+// A wave whose range holds a whole unit writes that unit's normalised output; a unit
+// shared by several waves gets one partial softmax state (m, l, o) from each, in slot
+// wave + unit (unique: along the ranges the pair (wave, unit) only ever grows), combined
+// by the merge kernel.  The next tile is prefetched across unit boundaries.
 template <int D, int G, int KF>
 __global__ __launch_bounds__(kWave)
 __attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF == KVQ_K_ASYM2)) ? 3 : 2)))
@@ -468,23 +600,14 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     __shared__ Smem<D, G, KF> sm;
 
     const int lane = threadIdx.x;
-    const int split = blockIdx.x;
-    const int unit = blockIdx.y;
-    const int b = unit / p.n_kv_heads;
-    const int kvh = unit % p.n_kv_heads;
-    const size_t cap = (size_t)p.cap;
+    const int w = blockIdx.x;
+    const int Tu = p.tiles_per_unit;
+    const long long total = (long long)p.n_units * Tu;
+    const int g0 = wave_first_tile(w, total, p.n_waves);
+    const int g1 = wave_first_tile(w + 1, total, p.n_waves);
     const int n_q_heads = p.n_kv_heads * G;
-    const uint32_t *__restrict__ rec = qrec + (size_t)unit * C::QREC;
-    const float *__restrict__ recf = reinterpret_cast<const float *>(rec);
+    const uint32_t ucap = (uint32_t)p.cap;
 
-    const uint32_t mask = rec[C::OFF_MASK];
-    const bool all_rows = mask == (1u << NP) - 1u;
-    float acc_to_logit[G], logit_to_acc[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        acc_to_logit[h] = recf[C::OFF_QSC + h];
-        logit_to_acc[h] = 1.0f / acc_to_logit[h];
-    }
     if constexpr (KF == KVQ_K_LLOYD4) {
         // code-pair table: byte (lo nibble a, hi nibble b) -> fp16 (cent[a], cent[b])
         for (int e = lane; e < 256; e += kWave)
@@ -492,387 +615,414 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         __syncthreads();
     }
 
-    // ------------------------------------------------------------------ state
     const int vs = lane % LPP;         // value slot: channels 8*vs .. 8*vs+7
     const int vgrp = vs / 4;           // its scale group
+    const float chscale[2] = {5.9604644775390625e-08f, 9.5367431640625e-07f}; // 2^-24, 2^-20
+    const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u; // value word offset
+    const int q_lo = p.n_sink, q_hi = p.len; // quantized positions [q_lo, q_hi)
+
+    // ---- per-unit query scalars (uniform loads from the unit's record)
+    int u = g0 / Tu;
+    int t = g0 - u * Tu;
+    const uint32_t *__restrict__ rec = qrec + (size_t)u * C::QREC;
+    uint32_t mask = 0;
+    float acc_to_logit[G], logit_to_acc[G];
+    auto load_unit = [&]() {
+        rec = qrec + (size_t)u * C::QREC;
+        mask = rec[C::OFF_MASK];
+        const float *recf = reinterpret_cast<const float *>(rec);
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            acc_to_logit[h] = recf[C::OFF_QSC + h];
+            logit_to_acc[h] = 1.0f / acc_to_logit[h];
+        }
+    };
+
+    // ---- running softmax state of the current unit
     float acc[G][8];
     float zacc[G][NG];
     float lsum[G];
     float mrun[G], mthr[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        lsum[h] = 0.0f;
-        mrun[h] = -__builtin_inff();
-        mthr[h] = -__builtin_inff();
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-            acc[h][j] = 0.0f;
-#pragma unroll
-        for (int g = 0; g < NG; g++)
-            zacc[h][g] = 0.0f;
-    }
-    const float chscale[2] = {5.9604644775390625e-08f, 9.5367431640625e-07f}; // 2^-24, 2^-20
-
-    // ------------------------------------------------------------------ sink positions
-    const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
-    if (split == 0 && n_sink > 0) {
-        float sl[G];
-        const bool valid = lane < n_sink;
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            sl[h] = 0.0f;
-        if (valid) {
-            const uint16_t *sk = p.sink_k + ((size_t)unit * p.n_sink + lane) * D;
-            for (int c = 0; c < D; c += 2) {
-                const uint32_t w = *reinterpret_cast<const uint32_t *>(sk + c);
-                const float k0 = bf16_to_f32(w & 0xFFFFu), k1 = bf16_to_f32(w >> 16);
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    sl[h] = fmaf(recf[C::OFF_QF + h * D + c + 1], k1, fmaf(recf[C::OFF_QF + h * D + c], k0, sl[h]));
-            }
-        }
+    auto reset = [&]() {
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            const float x = valid ? sl[h] : -__builtin_inff();
-            mrun[h] = wave_max_dpp(x);
-            mthr[h] = mrun[h] * logit_to_acc[h];
-            const float pr = valid ? __builtin_amdgcn_exp2f(x - mrun[h]) : 0.0f;
-            lsum[h] += pr;
-            sm.sink_p[h][lane] = pr;
+            lsum[h] = 0.0f;
+            mrun[h] = -__builtin_inff();
+            mthr[h] = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                acc[h][j] = 0.0f;
+#pragma unroll
+            for (int g = 0; g < NG; g++)
+                zacc[h][g] = 0.0f;
         }
-        __syncthreads();
-        for (int t = lane / LPP; t < n_sink; t += PPI) {
-            const uint16_t *sv = p.sink_v + ((size_t)unit * p.n_sink + t) * D + 8 * vs;
+    };
+
+    // ---- end of the current unit's range in this wave: reduce over the wave, then write
+    // the normalised output (whole unit here) or this wave's partial state
+    auto flush = [&]() {
+        const bool whole = (long long)g0 <= (long long)u * Tu && (long long)(u + 1) * Tu <= (long long)g1;
+        const int b = u / p.n_kv_heads;
+        const int kvh = u % p.n_kv_heads;
+        float4 *red = reinterpret_cast<float4 *>(&sm.w[0][0][0]); // 64 lanes x 8 floats
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float v = bf16_to_f32(sv[j]) * chscale[j & 1];
+        for (int h = 0; h < G; h++) {
+            // lanes vs, vs + LPP, ... hold partial sums of the same 8 channels: add them
+            // through LDS (the weight buffer is free here)
+            red[2 * lane] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            red[2 * lane + 1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+            __syncthreads();
+            const float ls = wave_sum_dpp(lsum[h]);
+            float zs[NG];
 #pragma unroll
-                for (int h = 0; h < G; h++)
-                    acc[h][j] = fmaf(sm.sink_p[h][t], v, acc[h][j]);
+            for (int g = 0; g < NG; g++)
+                zs[g] = wave_sum_dpp(zacc[h][g]);
+            if (lane < LPP) {
+                float o[8] = {acc[h][0], acc[h][1], acc[h][2], acc[h][3], acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+#pragma unroll
+                for (int k = 1; k < 64 / LPP; k++) {
+                    const float4 a0 = red[2 * (lane + k * LPP)], a1 = red[2 * (lane + k * LPP) + 1];
+                    o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
+                    o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const float sc = (j & 1) ? 1048576.0f : 16777216.0f; // undo 2^-20 / 2^-24
+                    o[j] = o[j] * sc + zs[(8 * lane + j) / 32];
+                }
+                if (whole) {
+                    // fold in the sink positions' state, then normalise
+                    const float *sk = reinterpret_cast<const float *>(rec) + C::OFF_SINK + h * (D + 2);
+                    const float ms = sk[0];
+                    const float M = fmaxf(mrun[h], ms);
+                    const float fw = mrun[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mrun[h] - M);
+                    const float fs = ms == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+                    const float L = fmaf(ls, fw, sk[1] * fs);
+                    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; j++)
+                        o[j] = fmaf(o[j], fw, sk[2 + 8 * lane + j] * fs) * inv;
+                    float4 *dst = reinterpret_cast<float4 *>(p.out + ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + 8 * lane);
+                    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+                    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+                } else {
+                    float *part = p.part + ((size_t)(w + u) * G + h) * (D + 2);
+                    if (lane == 0) {
+                        part[0] = mrun[h];
+                        part[1] = ls;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; j++)
+                        part[2 + 8 * lane + j] = o[j];
+                }
             }
+            __syncthreads();
         }
-    }
+    };
 
-    // ------------------------------------------------------------------ position tiles
-    const int t_first = p.tile_begin + split * p.tiles_per_split;
-    int t_last = t_first + p.tiles_per_split;
-    if (t_last > p.tile_end)
-        t_last = p.tile_end;
-    const int q_lo = p.n_sink, q_hi = p.len; // quantized positions [q_lo, q_hi)
-    const uint32_t ucap = (uint32_t)p.cap;
-    Slabs sl;
-    sl.kc = make_rsrc(p.k_codes + (size_t)unit * KROWS * cap, (uint32_t)KROWS * ucap * 4u);
-    sl.vsz = make_rsrc(p.v_sz + (size_t)unit * NG * cap, (uint32_t)NG * ucap * 4u);
-    sl.vc = make_rsrc(p.v_codes + (size_t)unit * (cap / 2) * WPP, (ucap / 2u) * WPP * 4u);
-    if constexpr (KF != KVQ_K_LLOYD4) {
-        sl.ksz = make_rsrc(p.k_sz + (size_t)unit * NG * cap, (uint32_t)NG * ucap * 4u);
-        sl.kx = p.ch0 ? make_rsrc(p.k_ch0 + (size_t)unit * cap, ucap * 2u) : make_rsrc(p.k_codes, 0u);
-    } else {
-        sl.ksz = make_rsrc(p.k_codes, 0u);
-        sl.kx = make_rsrc(p.k_norm + (size_t)unit * cap, ucap * 2u);
-    }
-    const Slabs none = {make_rsrc(p.k_codes, 0u), make_rsrc(p.k_codes, 0u), make_rsrc(p.k_codes, 0u),
-                        make_rsrc(p.k_codes, 0u), make_rsrc(p.k_codes, 0u)};
-    // value words: lane's pair row and channel slot
-    const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u;
-
-    // value words of the current tile: word pair `it` is reloaded with the next tile's
-    // right after its last use, so each load has a whole tile of work to arrive
-    uint2 vcur[VIT];
+    // outer loop: the units this wave's range touches; inner loop: their tiles in the range
     KTile<D, G, KF> cur;
-    int tile = t_first;
-    {
-        const Slabs &s0 = tile < t_last ? sl : none;
-        load_ktile<D, G, KF>(cur, s0, ucap, lane, tile * TILE, mask);
+    uint2 vcur[VIT];
+    for (int g = g0; g < g1;) {
+        const int t_end = (g1 - g < Tu - t) ? t + (g1 - g) : Tu;
+        load_unit();
+        reset();
+        const Slabs sl = unit_slabs<D, G, KF>(p, u);
+        // key-side words and value words of the current tile; value word pair `it` is
+        // reloaded with the next tile's right after its last use, so each load has a whole
+        // tile of work to arrive
+        load_ktile<D, G, KF>(cur, sl, ucap, lane, t * TILE, mask, 0u);
 #pragma unroll
         for (int it = 0; it < VIT; it++)
-            vcur[it] = bload2(s0.vc, vvo, ((uint32_t)(tile * TILE / 2 + it * PPI) * WPP) * 4u);
-    }
-    for (; tile < t_last; tile++) {
-        const int t0 = tile * TILE;
-        const int tl = t0 + lane * TPL;
+            vcur[it] = bload2(sl.vc, vvo, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
+        for (; t < t_end; t++) {
+            const int t0 = t * TILE;
+            const int tl = t0 + lane * TPL;
+            const int tn = t + 1;
+            const bool more = tn < t_end;
 
-        // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h])
-        float lg[TPL][G];
-#pragma unroll
-        for (int i = 0; i < TPL; i++)
-#pragma unroll
-            for (int h = 0; h < G; h++)
-                lg[i][h] = 0.0f;
-        if constexpr (KF != KVQ_K_LLOYD4) {
-            if (all_rows)
-                score_asym<D, G, KF, true>(cur, rec, mask, p.ch0, lg);
-            else
-                score_asym<D, G, KF, false>(cur, rec, mask, p.ch0, lg);
-        } else {
-#pragma unroll
-            for (int r = 0; r < KROWS; r++) {
-                if (!(mask >> (r / C::RPP) & 1u))
-                    continue;
-                uint32_t pr[TPL][4];
-#pragma unroll
-                for (int i = 0; i < TPL; i++) {
-                    const uint32_t x = i == 0 ? cur.kc[r].x : cur.kc[r].y;
-#pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        pr[i][j] = sm.lut[(x >> (8 * j)) & 0xFFu];
-                }
-#pragma unroll
-                for (int h = 0; h < G; h++)
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const uint32_t qv = rec[C::OFF_QP + (r * G + h) * C::QW + j];
-#pragma unroll
-                        for (int i = 0; i < TPL; i++)
-                            lg[i][h] = dot2(pr[i][j], qv, lg[i][h]);
-                    }
-            }
-#pragma unroll
-            for (int i = 0; i < TPL; i++) {
-                const float rho = f16_to_f32(i == 0 ? (cur.kx & 0xFFFFu) : (cur.kx >> 16));
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    lg[i][h] *= rho;
-            }
-        }
-
-        // ---- value scale/zero of this lane's positions; positions outside [q_lo, q_hi)
-        // get logit -inf and scale/zero 0 (their slots may hold anything)
-        uint32_t vsw[TPL][NG];
-#pragma unroll
-        for (int g = 0; g < NG; g++) {
-            vsw[0][g] = cur.vsz[g].x;
-            vsw[1][g] = cur.vsz[g].y;
-        }
-        const bool full = (t0 >= q_lo) && (t0 + TILE <= q_hi);
-        if (!full) {
-#pragma unroll
-            for (int i = 0; i < TPL; i++) {
-                const int t = tl + i;
-                if (t < q_lo || t >= q_hi) {
-#pragma unroll
-                    for (int h = 0; h < G; h++)
-                        lg[i][h] = -__builtin_inff();
-#pragma unroll
-                    for (int g = 0; g < NG; g++)
-                        vsw[i][g] = 0u;
-                }
-            }
-        }
-
-        // ---- next tile's key-side words, into the registers this tile no longer needs:
-        // in flight during the rest of this tile
-        const Slabs &nx = tile + 1 < t_last ? sl : none;
-        load_ktile<D, G, KF>(cur, nx, ucap, lane, t0 + TILE, mask);
-
-        // ---- online softmax (log2 units); wave-wide max only when some logit exceeds
-        // the running maximum
-        // (the test compares in accumulator units against mthr = mrun / acc_to_logit; a
-        // rounding miss only lets a weight exceed 1 by an ulp)
-        uint64_t above = 0;
-#pragma unroll
-        for (int h = 0; h < G; h++)
+            // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h])
+            const bool all_rows = mask == (1u << NP) - 1u;
+            float lg[TPL][G];
 #pragma unroll
             for (int i = 0; i < TPL; i++)
-                above |= __ballot(lg[i][h] > mthr[h]);
-        if (above) {
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                float mt = lg[0][h];
+                for (int h = 0; h < G; h++)
+                    lg[i][h] = 0.0f;
+            if constexpr (KF != KVQ_K_LLOYD4) {
+                if (all_rows)
+                    score_asym<D, G, KF, true>(cur, rec, mask, p.ch0, lg);
+                else
+                    score_asym<D, G, KF, false>(cur, rec, mask, p.ch0, lg);
+            } else {
 #pragma unroll
-                for (int i = 1; i < TPL; i++)
-                    mt = fmaxf(mt, lg[i][h]);
-                const float mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
-                const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);
-                mrun[h] = mnew;
-                mthr[h] = mnew * logit_to_acc[h];
-                lsum[h] *= alpha;
+                for (int r = 0; r < KROWS; r++) {
+                    if (!(mask >> (r / C::RPP) & 1u))
+                        continue;
+                    uint32_t pr[TPL][4];
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    acc[h][j] *= alpha;
+                    for (int i = 0; i < TPL; i++) {
+                        const uint32_t x = i == 0 ? cur.kc[r].x : cur.kc[r].y;
 #pragma unroll
-                for (int g = 0; g < NG; g++)
-                    zacc[h][g] *= alpha;
+                        for (int j = 0; j < 4; j++)
+                            pr[i][j] = sm.lut[(x >> (8 * j)) & 0xFFu];
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            const uint32_t qv = rec[C::OFF_QP + (r * G + h) * C::QW + j];
+#pragma unroll
+                            for (int i = 0; i < TPL; i++)
+                                lg[i][h] = dot2(pr[i][j], qv, lg[i][h]);
+                        }
+                }
+#pragma unroll
+                for (int i = 0; i < TPL; i++) {
+                    const float rho = f16_to_f32(i == 0 ? (cur.kx & 0xFFFFu) : (cur.kx >> 16));
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        lg[i][h] *= rho;
+                }
             }
-        }
-        float pw[TPL][G];
-#pragma unroll
-        for (int i = 0; i < TPL; i++)
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -mrun[h]));
-                lsum[h] += pw[i][h];
-            }
-        // zero-point term and the fp16 weights p*s of this lane's position pair (-> LDS),
-        // from the weights rounded to fp16 pairs: one packed product and one dot2 per
-        // (group, head)
-        uint32_t ph[G];
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            ph[h] = pack_f16x2(pw[0][h], pw[1][h]);
-#pragma unroll
-        for (int g = 0; g < NG; g++) {
-            const uint32_t sp = __builtin_amdgcn_perm(vsw[1][g], vsw[0][g], 0x05040100u); // (s0, s1)
-            const uint32_t zp = __builtin_amdgcn_perm(vsw[1][g], vsw[0][g], 0x07060302u); // (z0, z1)
-            uint32_t wq[4 * WV];
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                zacc[h][g] = dot2(ph[h], zp, zacc[h][g]);
-                wq[h] = mul_f16x2(ph[h], sp);
-            }
-#pragma unroll
-            for (int h = G; h < 4 * WV; h++)
-                wq[h] = 0u;
-#pragma unroll
-            for (int v4 = 0; v4 < WV; v4++)
-                sm.w[g][lane][v4] = make_uint4(wq[4 * v4], wq[4 * v4 + 1], wq[4 * v4 + 2], wq[4 * v4 + 3]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- values: lane owns channels 8*vs .. 8*vs+7 of one pair per iteration
-        const uint32_t vnext = (uint32_t)((t0 + TILE) / 2) * WPP * 4u;
+            // ---- value scale/zero of this lane's positions; positions outside [q_lo, q_hi)
+            // get logit -inf and scale/zero 0 (their slots may hold anything)
+            uint32_t vsw[TPL][NG];
 #pragma unroll
-        for (int it = 0; it < VIT; it++) {
-            const uint2 vv = vcur[it];
-            vcur[it] = bload2(nx.vc, vvo, vnext + (uint32_t)(it * PPI * WPP) * 4u);
-            const int pl = it * PPI + lane / LPP;
-            uint32_t wv[4 * WV];
-#pragma unroll
-            for (int v4 = 0; v4 < WV; v4++) {
-                const uint4 t4 = sm.w[vgrp][pl][v4];
-                wv[4 * v4 + 0] = t4.x;
-                wv[4 * v4 + 1] = t4.y;
-                wv[4 * v4 + 2] = t4.z;
-                wv[4 * v4 + 3] = t4.w;
+            for (int gg = 0; gg < NG; gg++) {
+                vsw[0][gg] = cur.vsz[gg].x;
+                vsw[1][gg] = cur.vsz[gg].y;
             }
+            const bool full = (t0 >= q_lo) && (t0 + TILE <= q_hi);
+            if (!full) {
 #pragma unroll
-            for (int q2 = 0; q2 < 2; q2++) {
-                const uint32_t x = q2 == 0 ? vv.x : vv.y;
-                const uint32_t y = x >> 8;
-                const uint32_t c0 = x & 0x000F000Fu, c1 = x & 0x00F000F0u;
-                const uint32_t c2 = y & 0x000F000Fu, c3 = y & 0x00F000F0u;
+                for (int i = 0; i < TPL; i++) {
+                    const int tp = tl + i;
+                    if (tp < q_lo || tp >= q_hi) {
+#pragma unroll
+                        for (int h = 0; h < G; h++)
+                            lg[i][h] = -__builtin_inff();
+#pragma unroll
+                        for (int gg = 0; gg < NG; gg++)
+                            vsw[i][gg] = 0u;
+                    }
+                }
+            }
+
+            // ---- next tile's key-side words, into the registers this tile no longer needs:
+            // in flight during the rest of this tile.  After the last tile of the unit's range
+            // the loads access nothing: the next unit's first tile is loaded after the flush,
+            // outside the inner loop and its register peak.
+            const uint32_t noff = more ? 0u : kNoAccess;
+            load_ktile<D, G, KF>(cur, sl, ucap, lane, tn * TILE, mask, noff);
+
+            // ---- online softmax (log2 units); wave-wide max only when some logit exceeds
+            // the running maximum (the test compares in accumulator units against
+            // mthr = mrun / acc_to_logit; a rounding miss only lets a weight exceed 1 by an ulp)
+            uint64_t above = 0;
+#pragma unroll
+            for (int h = 0; h < G; h++)
+#pragma unroll
+                for (int i = 0; i < TPL; i++)
+                    above |= __ballot(lg[i][h] > mthr[h]);
+            if (above) {
 #pragma unroll
                 for (int h = 0; h < G; h++) {
-                    acc[h][4 * q2 + 0] = dot2(c0, wv[h], acc[h][4 * q2 + 0]);
-                    acc[h][4 * q2 + 1] = dot2(c1, wv[h], acc[h][4 * q2 + 1]);
-                    acc[h][4 * q2 + 2] = dot2(c2, wv[h], acc[h][4 * q2 + 2]);
-                    acc[h][4 * q2 + 3] = dot2(c3, wv[h], acc[h][4 * q2 + 3]);
+                    float mt = lg[0][h];
+#pragma unroll
+                    for (int i = 1; i < TPL; i++)
+                        mt = fmaxf(mt, lg[i][h]);
+                    const float mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
+                    const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);
+                    mrun[h] = mnew;
+                    mthr[h] = mnew * logit_to_acc[h];
+                    lsum[h] *= alpha;
+#pragma unroll
+                    for (int j = 0; j < 8; j++)
+                        acc[h][j] *= alpha;
+#pragma unroll
+                    for (int gg = 0; gg < NG; gg++)
+                        zacc[h][gg] *= alpha;
                 }
             }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+            // (a running maximum still at -inf means every logit so far, this tile's included,
+            // is -inf: subtract 0 instead so the weights come out 0, not NaN)
+            float pw[TPL][G];
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float msub = mrun[h] == -__builtin_inff() ? 0.0f : mrun[h];
+#pragma unroll
+                for (int i = 0; i < TPL; i++) {
+                    pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -msub));
+                    lsum[h] += pw[i][h];
+                }
+            }
+            // zero-point term and the fp16 weights p*s of this lane's position pair (-> LDS),
+            // from the weights rounded to fp16 pairs: one packed product and one dot2 per
+            // (group, head)
+            uint32_t ph[G];
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                ph[h] = pack_f16x2(pw[0][h], pw[1][h]);
+#pragma unroll
+            for (int gg = 0; gg < NG; gg++) {
+                const uint32_t sp = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x05040100u); // (s0, s1)
+                const uint32_t zp = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x07060302u); // (z0, z1)
+                uint32_t wq[4 * WV];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    zacc[h][gg] = dot2(ph[h], zp, zacc[h][gg]);
+                    wq[h] = mul_f16x2(ph[h], sp);
+                }
+#pragma unroll
+                for (int h = G; h < 4 * WV; h++)
+                    wq[h] = 0u;
+#pragma unroll
+                for (int v4 = 0; v4 < WV; v4++)
+                    sm.w[gg][lane][v4] = make_uint4(wq[4 * v4], wq[4 * v4 + 1], wq[4 * v4 + 2], wq[4 * v4 + 3]);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ------------------------------------------------------------------ wave reduction
+            // ---- values: lane owns channels 8*vs .. 8*vs+7 of one pair per iteration
+            const uint32_t vnext = (uint32_t)(tn * TILE / 2) * WPP * 4u;
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        lsum[h] = wave_sum(lsum[h]);
+            for (int it = 0; it < VIT; it++) {
+                const uint2 vv = vcur[it];
+                vcur[it] = bload2(sl.vc, vvo + noff, vnext + (uint32_t)(it * PPI * WPP) * 4u);
+                const int pl = it * PPI + lane / LPP;
+                uint32_t wv[4 * WV];
 #pragma unroll
-        for (int g = 0; g < NG; g++)
-            zacc[h][g] = wave_sum(zacc[h][g]);
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-#pragma unroll
-            for (int m = LPP; m < 64; m <<= 1)
-                acc[h][j] += __shfl_xor(acc[h][j], m);
-    }
-    // lanes 0..LPP-1 hold channels 8*lane .. 8*lane+7: the split's partial (m, l, o), or the
-    // normalised output when the whole context is one split
-    if (lane < LPP) {
-        const bool single = (p.n_split == 1);
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            float o[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float sc = (j & 1) ? 1048576.0f : 16777216.0f; // undo 2^-20 / 2^-24
-                o[j] = acc[h][j] * sc + zacc[h][(8 * lane + j) / 32];
-            }
-            if (single) {
-                const float inv = lsum[h] > 0.0f ? 1.0f / lsum[h] : 0.0f;
-                float4 *dst = reinterpret_cast<float4 *>(p.out + ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + 8 * lane);
-                dst[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-                dst[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
-            } else {
-                float *part = p.part + (((size_t)unit * p.n_split + split) * G + h) * (D + 2);
-                if (lane == 0) {
-                    part[0] = mrun[h];
-                    part[1] = lsum[h];
+                for (int v4 = 0; v4 < WV; v4++) {
+                    const uint4 t4 = sm.w[vgrp][pl][v4];
+                    wv[4 * v4 + 0] = t4.x;
+                    wv[4 * v4 + 1] = t4.y;
+                    wv[4 * v4 + 2] = t4.z;
+                    wv[4 * v4 + 3] = t4.w;
                 }
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    part[2 + 8 * lane + j] = o[j];
+                for (int q2 = 0; q2 < 2; q2++) {
+                    const uint32_t x = q2 == 0 ? vv.x : vv.y;
+                    const uint32_t y = x >> 8;
+                    const uint32_t c0 = x & 0x000F000Fu, c1 = x & 0x00F000F0u;
+                    const uint32_t c2 = y & 0x000F000Fu, c3 = y & 0x00F000F0u;
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        acc[h][4 * q2 + 0] = dot2(c0, wv[h], acc[h][4 * q2 + 0]);
+                        acc[h][4 * q2 + 1] = dot2(c1, wv[h], acc[h][4 * q2 + 1]);
+                        acc[h][4 * q2 + 2] = dot2(c2, wv[h], acc[h][4 * q2 + 2]);
+                        acc[h][4 * q2 + 3] = dot2(c3, wv[h], acc[h][4 * q2 + 3]);
+                    }
+                }
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+        flush();
+        g += t_end - (g - u * Tu);
+        u++;
+        t = 0;
     }
 }
 
 // ===================================================================== split merge
-// One thread per (sequence, query head, channel) combines the per-split (m, l, o) partials:
-// one global softmax over all positions (Dual-QK sec. 3.4).
-template <int D, int G>
+// One thread per (sequence, query head, channel) combines the partial (m, l, o) states of
+// the waves that shared a unit: one global softmax over all positions (Dual-QK sec. 3.4).
+// Units held whole by one wave were written by the decode kernel and are skipped.
+template <int D, int G, int QREC, int OFF_SINK>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
 {
     const int c = threadIdx.x;
     const int h = blockIdx.x;
-    const int unit = blockIdx.y;
-    const int b = unit / p.n_kv_heads;
-    const int kvh = unit % p.n_kv_heads;
-    const float *pbase = p.part + ((size_t)unit * p.n_split * G + h) * (D + 2);
+    const int u = blockIdx.y;
+    const long long total = (long long)p.n_units * p.tiles_per_unit;
+    const int w_lo = wave_of_tile((long long)u * p.tiles_per_unit, total, p.n_waves);
+    const int w_hi = wave_of_tile((long long)(u + 1) * p.tiles_per_unit - 1, total, p.n_waves);
+    if (w_lo == w_hi)
+        return;
+    const float *pb = p.part + ((size_t)(w_lo + u) * G + h) * (D + 2);
     const size_t stride = (size_t)G * (D + 2);
-    float M = -__builtin_inff();
-    for (int s = 0; s < p.n_split; s++)
-        M = fmaxf(M, pbase[s * stride]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < p.n_split; s++) {
-        const float *ps = pbase + s * stride;
-        const float f = (ps[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ps[0] - M);
-        L = fmaf(ps[1], f, L);
-        O = fmaf(ps[2 + c], f, O);
+    const int n = w_hi - w_lo + 1;
+    // the sink positions' state from the unit's query record
+    const float *sk = reinterpret_cast<const float *>(p.qprep + (size_t)u * QREC) + OFF_SINK + h * (D + 2);
+    // the partials are read in batches of 8 with independent loads (one memory latency per
+    // batch rather than per partial)
+    constexpr int NB = 8;
+    float M = sk[0];
+    for (int s0 = 0; s0 < n; s0 += NB) {
+        float mv[NB];
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+            mv[j] = s0 + j < n ? pb[(s0 + j) * stride] : -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+            M = fmaxf(M, mv[j]);
     }
+    const float fs = sk[0] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(sk[0] - M);
+    float L = sk[1] * fs, O = sk[2 + c] * fs;
+    for (int s0 = 0; s0 < n; s0 += NB) {
+        float mv[NB], lv[NB], ov[NB];
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const bool ok = s0 + j < n;
+            const float *ps = pb + (s0 + j) * stride;
+            mv[j] = ok ? ps[0] : -__builtin_inff();
+            lv[j] = ok ? ps[1] : 0.0f;
+            ov[j] = ok ? ps[2 + c] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const float f = mv[j] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mv[j] - M);
+            L = fmaf(lv[j], f, L);
+            O = fmaf(ov[j], f, O);
+        }
+    }
+    const int b = u / p.n_kv_heads;
+    const int kvh = u % p.n_kv_heads;
     const size_t oi = ((size_t)b * p.n_kv_heads * G + (size_t)kvh * G + h) * D + c;
     p.out[oi] = L > 0.0f ? O / L : 0.0f;
 }
 
 // ===================================================================== launchers
 template <int D, int G, int KF>
-hipError_t launch_one(int units, const DecodeParams &p, hipStream_t s)
+hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipStream_t s)
 {
     hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((decode_kernel<D, G, KF>), dim3((unsigned)p.n_split, (unsigned)units), dim3(kWave), 0, s,
-                       p, static_cast<const uint32_t *>(p.qprep));
+    hipLaunchKernelGGL((decode_kernel<D, G, KF>), dim3((unsigned)p.n_waves), dim3(kWave), 0, s, p,
+                       static_cast<const uint32_t *>(p.qprep));
     e = hipGetLastError();
-    if (e != hipSuccess || p.n_split == 1)
+    if (e != hipSuccess || !merge)
         return e;
-    hipLaunchKernelGGL((merge_kernel<D, G>), dim3((unsigned)G, (unsigned)units), dim3(D), 0, s, p);
+    using C = Cfg<D, G, KF>;
+    hipLaunchKernelGGL((merge_kernel<D, G, C::QREC, C::OFF_SINK>), dim3((unsigned)G, (unsigned)units), dim3(D), 0, s,
+                       p);
     return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t launch_kf(int kfmt, int units, const DecodeParams &p, hipStream_t s)
+hipError_t launch_kf(int kfmt, int units, const DecodeParams &p, bool merge, hipStream_t s)
 {
     switch (kfmt) {
-    case KVQ_K_ASYM2: return launch_one<D, G, KVQ_K_ASYM2>(units, p, s);
-    case KVQ_K_ASYM4: return launch_one<D, G, KVQ_K_ASYM4>(units, p, s);
-    default: return launch_one<D, G, KVQ_K_LLOYD4>(units, p, s);
+    case KVQ_K_ASYM2: return launch_one<D, G, KVQ_K_ASYM2>(units, p, merge, s);
+    case KVQ_K_ASYM4: return launch_one<D, G, KVQ_K_ASYM4>(units, p, merge, s);
+    default: return launch_one<D, G, KVQ_K_LLOYD4>(units, p, merge, s);
     }
 }
 
 template <int D>
-hipError_t launch_g(int group, int kfmt, int units, const DecodeParams &p, hipStream_t s)
+hipError_t launch_g(int group, int kfmt, int units, const DecodeParams &p, bool merge, hipStream_t s)
 {
     switch (group) {
-    case 1: return launch_kf<D, 1>(kfmt, units, p, s);
-    case 2: return launch_kf<D, 2>(kfmt, units, p, s);
-    case 4: return launch_kf<D, 4>(kfmt, units, p, s);
-    default: return launch_kf<D, 8>(kfmt, units, p, s);
+    case 1: return launch_kf<D, 1>(kfmt, units, p, merge, s);
+    case 2: return launch_kf<D, 2>(kfmt, units, p, merge, s);
+    case 4: return launch_kf<D, 4>(kfmt, units, p, merge, s);
+    default: return launch_kf<D, 8>(kfmt, units, p, merge, s);
     }
 }
 
@@ -942,12 +1092,12 @@ int decode_slots(int head_dim, int group, int kfmt)
     return v;
 }
 
-hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
+hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, bool merge,
                          hipStream_t s)
 {
     if (head_dim == 128)
-        return launch_g<128>(group, kfmt, units, p, s);
-    return launch_g<64>(group, kfmt, units, p, s);
+        return launch_g<128>(group, kfmt, units, p, merge, s);
+    return launch_g<64>(group, kfmt, units, p, merge, s);
 }
 
 } // namespace kvq

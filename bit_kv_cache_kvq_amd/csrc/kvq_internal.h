@@ -14,9 +14,13 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 
 // Decode tile: positions scored by one wave per pass (64 lanes x 2 positions).
 constexpr int kTile = 128;
+// Upper bound on decode waves per call (the grid is one wave per resident slot).
+constexpr int kMaxWaves = 16384;
 // Cache capacity granule (public contract: capacity is a multiple of 256 positions).
 constexpr int kCapacityQuantum = 256;
 constexpr int kMaxSink = 64;
+// Largest capacity (positions per sequence): keeps every per-unit slab under 1 GiB.
+constexpr int kMaxCapacity = 1 << 24;
 
 struct AppendParams {
     uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
@@ -33,15 +37,15 @@ struct DecodeParams {
     const void *q;
     float *out;
     uint8_t *mask_out;
-    float *part;        // split partials [U][n_split][G][D + 2]
+    float *part;        // partial softmax states [slot][G][D + 2], slot = wave + unit
     uint32_t *qprep;    // per-unit query record written by the query-prep kernel
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
     float sm_log2e;      // softmax scale times log2(e)
-    int n_split, tile_begin, tile_end, tiles_per_split;
+    int n_units, tiles_per_unit, n_waves; // work split: n_waves equal ranges of n_units * tiles_per_unit tiles
 };
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
-hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
+hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, bool merge,
                          hipStream_t s);
 // u32 words of one unit's query record (query-prep output read by the decode kernel).
 int decode_qrec_words(int head_dim, int group, int kfmt);

@@ -86,7 +86,7 @@ typedef enum { KVQ_K_ASYM2 = 0, KVQ_K_ASYM4 = 1, KVQ_K_LLOYD4 = 2 } kvq_kfmt;
 /* Cache descriptor.  Geometry and format fields are set once by the caller; `len` is the
  * number of positions stored per sequence (uniform across sequences) and is advanced by
  * kvq_quant_append.  Constraints: head_dim in {64, 128}; capacity a positive multiple of
- * 256; 0 <= n_sink <= 64 and n_sink < capacity; k_hadamard and k_ch0_bf16 in {0, 1};
+ * 256 and at most 2^24; batch * n_kv_heads <= 65535; 0 <= n_sink <= 64 and n_sink < capacity; k_hadamard and k_ch0_bf16 in {0, 1};
  * k_ch0_bf16 requires an asymmetric key format and k_hadamard = 0.  Pointers unused by
  * the chosen format may be NULL (see kvq_buffer_bytes).                                 */
 typedef struct kvq_cache {
@@ -137,8 +137,9 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
                             int32_t n_new, void *stream);
 
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (any len up to capacity)
- * and n_q_heads.  The workspace holds the per-split partial softmax states; its contents
- * need no initialisation and are scratch between calls.                                  */
+ * and n_q_heads.  The workspace holds the per-unit query records and the partial softmax
+ * states of units shared by several decode waves; its contents need no initialisation and
+ * are scratch between calls.                                                             */
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
 
 /* Decode attention for one query step per sequence over positions [0, len).
@@ -157,7 +158,10 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
                            float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* Number of context splits kvq_decode_attn uses for the current len (host-only).        */
+/* Number of decode waves kvq_decode_attn uses for the current len: the positions of all
+ * sequences and KV heads, in 128-position tiles, are cut into this many equal contiguous
+ * ranges (one per resident wave slot of the device, or fewer for small inputs).  Host-only
+ * apart from querying the device's occupancy once.                                       */
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads);
 
 /* Host helper: the 2^bits-level symmetric Lloyd-Max codebook of N(0,1) (fp64 iteration to
@@ -165,8 +169,9 @@ int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads);
  * Only bits = 4 is used by the key formats.                                               */
 kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *thresholds);
 
-/* Tuning override for the split planner: target tiles of 256 positions per split, 0 = the
- * built-in policy.  Process-wide; affects later decode calls only.                        */
+/* Tuning override for the work split: target number of 128-position tiles per decode wave,
+ * 0 = the built-in policy (one wave per resident slot).  Process-wide; affects later
+ * decode calls only.                                                                     */
 void kvq_set_split_tiles(int32_t tiles_per_split);
 
 const char *kvq_status_string(kvq_status s);

@@ -62,6 +62,7 @@ def test_buffer_bytes_follow_layout():
     (dict(batch=0), B.KVQ_ERR_ARG),
     (dict(len=513), B.KVQ_ERR_CAPACITY),
     (dict(batch=70000), B.KVQ_ERR_UNSUPPORTED),
+    (dict(capacity=(1 << 24) + 256), B.KVQ_ERR_UNSUPPORTED),
 ])
 def test_validate_rejects(kw, code):
     assert B.lib().kvq_validate(ctypes.byref(_cache(**kw))) == code
@@ -123,11 +124,18 @@ def test_split_planner_counts():
     L = B.lib()
     s = _cache(batch=64, n_kv_heads=8, capacity=16640, len=16385, n_sink=4)
     n = L.kvq_decode_splits(ctypes.byref(s), 32)
-    tiles = (16385 + 127) // 128  # 128-position tiles; position 0..3 are sinks in tile 0
-    assert -(-tiles // 16) <= n <= tiles  # at most 16 tiles per split
-    # a context of one tile is one split whatever the device
+    tiles = 64 * 8 * ((16385 + 127) // 128)  # 128-position tiles of all units
+    assert 1 <= n <= min(tiles, 16384)
+    # never more waves than tiles: 8 units of one tile each
     s = _cache(batch=1, n_kv_heads=8, capacity=256, len=100)
-    assert L.kvq_decode_splits(ctypes.byref(s), 32) == 1
+    assert 1 <= L.kvq_decode_splits(ctypes.byref(s), 32) <= 8
+    # the override sets tiles per wave
+    B.set_split_tiles(4)
+    try:
+        s = _cache(batch=2, n_kv_heads=2, capacity=4096, len=4096)  # 4 units x 32 tiles
+        assert L.kvq_decode_splits(ctypes.byref(s), 8) == 32
+    finally:
+        B.set_split_tiles(0)
     s = _cache(batch=1, n_kv_heads=1, capacity=256, len=0)
     assert L.kvq_decode_splits(ctypes.byref(s), 1) == 1
 

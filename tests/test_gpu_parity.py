@@ -132,6 +132,27 @@ def test_split_invariance_and_determinism(oracle_mod):
         B.set_split_tiles(0)
 
 
+@pytest.mark.parametrize("kfmt,rot,ch0,keep,G,d", [(0, 0, 0, 0, 2, 128), (2, 1, 0, 3, 4, 128),
+                                                   (1, 0, 1, 5, 1, 64), (0, 0, 1, 2, 8, 64)])
+def test_wave_ranges_across_units(oracle_mod, kfmt, rot, ch0, keep, G, d):
+    # 16 short sequences: with few tiles per wave the ranges start and end inside units,
+    # hold several whole units, or share one unit among several waves
+    c, oc, q, out0 = _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, keep=keep, ns=4, T=300, Bsz=4,
+                          Hkv=4, G=G, dist="t3")
+    qg = q.cuda()
+    sm = 1 / np.sqrt(d)
+    ref, _ = oc.decode(to_f32_np(q).reshape(16, G, d), sm, keep)
+    try:
+        for tps in (1, 2, 4, 5, 7, 13, 48, 1000):
+            B.set_split_tiles(tps)
+            note(f"  tiles per wave {tps}: {c.splits(4 * G)} waves")
+            o1, _ = c.decode(qg, sm, keep)
+            torch.cuda.synchronize()
+            compare_outputs(o1, ref, f"tiles per wave {tps}")
+    finally:
+        B.set_split_tiles(0)
+
+
 def test_keep_all_equals_no_pruning(oracle_mod):
     c, oc, q, out0 = _run(oracle_mod, kfmt=0, ch0=1, T=700, keep=0)
     o8, m8 = c.decode(q.cuda(), 1 / np.sqrt(128), 8)
