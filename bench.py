@@ -110,6 +110,14 @@ def write_traffic(dec_fetch, dec_write, copy_fetch, copy_write, out_path, copy_b
         "# (KiB per dispatch, each counter in its own run), scaled by the same counters on a copy of",
         f"# {copy_bytes} bytes (python bench.py --copy-probe).  Valid only for the decode source whose",
         "# sha256 is recorded below: bench.py ignores this file once the kernel changes.",
+        "# commands (from /tmp with TMPDIR=/tmp; each counter in a run of its own):",
+        "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex decode_kernel --output-format csv -d F -o decF"
+        " -- python3 <repo>/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex decode_kernel --output-format csv -d W -o decW"
+        " -- python3 <repo>/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d CF -o cpyF -- python3 <repo>/bench.py --copy-probe",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d CW -o cpyW -- python3 <repo>/bench.py --copy-probe",
+        "#   python3 bench.py --traffic-csv <decF csv> <decW csv> <cpyF csv> <cpyW csv>",
         f"decode_source_sha256: {sha}",
         f"decode_dispatches: {len(f)} fetch, {len(wr)} write",
         f"fetch_kib_per_launch: {fetch_kib:.1f}",
@@ -229,6 +237,9 @@ def main():
         if w.steps:
             c.append(*news[i])
         if ev is not None:
+            # call events around kvq_decode_attn; kernel events (recorded by the library on
+            # the same stream) around its main decode kernel alone
+            B.set_decode_events(ev[2], ev[3])
             ev[0].record(stream)
         c.decode(queries[i], w.sm_scale, w.keep_groups, out=out, mask_out=mask)
         if ev is not None:
@@ -237,7 +248,11 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+    for e in evs:  # torch creates an event's handle at its first record
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
     lens = []
     t0 = time.perf_counter()
     for j in range(args.steps):
@@ -245,8 +260,11 @@ def main():
         lens.append(c.len)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    B.set_decode_events()
     elapsed = t1 - t0
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    call_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    call_avg_s = sum(call_ms) / len(call_ms) / 1e3
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     full = (1 << (w.head_dim // 16)) - 1
     masks = mask.cpu().tolist() if w.keep_groups else [full] * w.units
@@ -257,8 +275,9 @@ def main():
     eff_gbps = sum(bytes_per) / elapsed / 1e9
     achieved = avg_bytes / dec_avg_s / 1e9
     traffic = traffic_record() if args.workload == 5 else None
-    log(f"decode kernel avg {dec_avg_s * 1e6:.1f} us, {avg_bytes / 1e9:.4f} GB/launch, {achieved:.0f} GB/s; "
-        f"step {elapsed / args.steps * 1e3:.3f} ms; splits {c.splits(w.n_q_heads)}")
+    log(f"decode kernel avg {dec_avg_s * 1e6:.1f} us ({call_avg_s * 1e6:.1f} us for the whole call), "
+        f"{avg_bytes / 1e9:.4f} GB/launch, {achieved:.0f} GB/s; step {elapsed / args.steps * 1e3:.3f} ms; "
+        f"waves {c.splits(w.n_q_heads)}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -289,8 +308,9 @@ def main():
         "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
         "decode_algorithmic_bytes_per_launch": avg_bytes,
         "decode_kernel_us": dec_avg_s * 1e6,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "decode_call_us": call_avg_s * 1e6,
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -22,6 +22,7 @@ BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", 
              "codebook", "thresholds"]
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles",
+           "kvq_set_decode_events",
            "kvq_status_string"]
 
 
@@ -64,6 +65,8 @@ def lib():
         L.kvq_codebook_gaussian.argtypes = [i32, P, P]
         L.kvq_set_split_tiles.restype = None
         L.kvq_set_split_tiles.argtypes = [i32]
+        L.kvq_set_decode_events.restype = None
+        L.kvq_set_decode_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [i32]
         _lib = L
@@ -87,6 +90,15 @@ def codebook_gaussian(bits: int = 4):
 
 def set_split_tiles(n: int) -> None:
     lib().kvq_set_split_tiles(int(n))
+
+
+def set_decode_events(start=None, stop=None) -> None:
+    """Record two torch.cuda.Event objects (timing enabled, already recorded once so that
+    they exist) around the main decode kernel of later decode calls; no arguments: off."""
+    if start is None or stop is None:
+        lib().kvq_set_decode_events(None, None)
+    else:
+        lib().kvq_set_decode_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
 
 
 def _ptr(t):

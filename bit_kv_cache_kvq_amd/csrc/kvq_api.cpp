@@ -14,6 +14,7 @@ using namespace kvq;
 namespace {
 
 std::atomic<int> g_split_tiles{0};
+std::atomic<void *> g_decode_ev[2] = {{nullptr}, {nullptr}};
 
 int key_bits(int kfmt) { return kfmt == KVQ_K_ASYM2 ? 2 : 4; }
 
@@ -287,12 +288,21 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.n_units = (int)U;
     p.tiles_per_unit = pl.tiles_per_unit;
     p.n_waves = pl.n_waves;
-    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, pl.merge, (hipStream_t)stream) != hipSuccess)
+    hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
+    if (!ev[0] || !ev[1])
+        ev[0] = ev[1] = nullptr;
+    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, pl.merge, ev, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
     return KVQ_OK;
 }
 
 void kvq_set_split_tiles(int32_t tiles_per_split) { g_split_tiles.store(tiles_per_split > 0 ? tiles_per_split : 0); }
+
+void kvq_set_decode_events(void *start_event, void *stop_event)
+{
+    g_decode_ev[0].store(start_event);
+    g_decode_ev[1].store(stop_event);
+}
 
 // Symmetric Lloyd-Max quantiser for N(0,1): iterate centroid = conditional mean of the
 // cell and threshold = midpoint on the positive half, then mirror.  Conditional mean of

@@ -988,15 +988,19 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
 
 // ===================================================================== launchers
 template <int D, int G, int KF>
-hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipStream_t s)
+hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2], hipStream_t s)
 {
     hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess)
+        return e;
     hipLaunchKernelGGL((decode_kernel<D, G, KF>), dim3((unsigned)p.n_waves), dim3(kWave), 0, s, p,
                        static_cast<const uint32_t *>(p.qprep));
     e = hipGetLastError();
+    if (e == hipSuccess && ev[1])
+        e = hipEventRecord(ev[1], s);
     if (e != hipSuccess || !merge)
         return e;
     using C = Cfg<D, G, KF>;
@@ -1006,23 +1010,24 @@ hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipStream_t 
 }
 
 template <int D, int G>
-hipError_t launch_kf(int kfmt, int units, const DecodeParams &p, bool merge, hipStream_t s)
+hipError_t launch_kf(int kfmt, int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2], hipStream_t s)
 {
     switch (kfmt) {
-    case KVQ_K_ASYM2: return launch_one<D, G, KVQ_K_ASYM2>(units, p, merge, s);
-    case KVQ_K_ASYM4: return launch_one<D, G, KVQ_K_ASYM4>(units, p, merge, s);
-    default: return launch_one<D, G, KVQ_K_LLOYD4>(units, p, merge, s);
+    case KVQ_K_ASYM2: return launch_one<D, G, KVQ_K_ASYM2>(units, p, merge, ev, s);
+    case KVQ_K_ASYM4: return launch_one<D, G, KVQ_K_ASYM4>(units, p, merge, ev, s);
+    default: return launch_one<D, G, KVQ_K_LLOYD4>(units, p, merge, ev, s);
     }
 }
 
 template <int D>
-hipError_t launch_g(int group, int kfmt, int units, const DecodeParams &p, bool merge, hipStream_t s)
+hipError_t launch_g(int group, int kfmt, int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2],
+                    hipStream_t s)
 {
     switch (group) {
-    case 1: return launch_kf<D, 1>(kfmt, units, p, merge, s);
-    case 2: return launch_kf<D, 2>(kfmt, units, p, merge, s);
-    case 4: return launch_kf<D, 4>(kfmt, units, p, merge, s);
-    default: return launch_kf<D, 8>(kfmt, units, p, merge, s);
+    case 1: return launch_kf<D, 1>(kfmt, units, p, merge, ev, s);
+    case 2: return launch_kf<D, 2>(kfmt, units, p, merge, ev, s);
+    case 4: return launch_kf<D, 4>(kfmt, units, p, merge, ev, s);
+    default: return launch_kf<D, 8>(kfmt, units, p, merge, ev, s);
     }
 }
 
@@ -1093,11 +1098,11 @@ int decode_slots(int head_dim, int group, int kfmt)
 }
 
 hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, bool merge,
-                         hipStream_t s)
+                         hipEvent_t const ev[2], hipStream_t s)
 {
     if (head_dim == 128)
-        return launch_g<128>(group, kfmt, units, p, merge, s);
-    return launch_g<64>(group, kfmt, units, p, merge, s);
+        return launch_g<128>(group, kfmt, units, p, merge, ev, s);
+    return launch_g<64>(group, kfmt, units, p, merge, ev, s);
 }
 
 } // namespace kvq

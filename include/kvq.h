@@ -174,6 +174,13 @@ kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *threshol
  * decode calls only.                                                                     */
 void kvq_set_split_tiles(int32_t tiles_per_split);
 
+/* Measurement hook: while both handles are non-NULL (hipEvent_t, created and owned by the
+ * caller), every kvq_decode_attn records start_event on its stream immediately before the
+ * main decode kernel and stop_event immediately after it, so hipEventElapsedTime gives that
+ * kernel's duration alone (the query-prep and merge kernels fall outside).  NULL, NULL
+ * turns it off.  Process-wide; meant for benchmarks, not for concurrent callers.          */
+void kvq_set_decode_events(void *start_event, void *stop_event);
+
 const char *kvq_status_string(kvq_status s);
 
 #ifdef __cplusplus

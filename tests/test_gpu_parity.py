@@ -170,3 +170,24 @@ def test_decode_leaves_cache_unchanged(oracle_mod):
     torch.cuda.synchronize()
     for k, v in c.buffers.items():
         assert torch.equal(before[k], v), k
+
+
+def test_decode_event_hook(oracle_mod):
+    # the library records the caller's events around the main decode kernel only
+    c, oc, q, out0 = _run(oracle_mod, kfmt=0, T=3000, Bsz=2, Hkv=2)
+    e0, e1, c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (e0, e1):
+        e.record()
+    torch.cuda.synchronize()
+    try:
+        B.set_decode_events(e0, e1)
+        c0.record()
+        out, _ = c.decode(q.cuda(), 1 / np.sqrt(128))
+        c1.record()
+        torch.cuda.synchronize()
+    finally:
+        B.set_decode_events()
+    kern, call = e0.elapsed_time(e1), c0.elapsed_time(c1)
+    note(f"  decode kernel {kern * 1e3:.1f} us of a {call * 1e3:.1f} us call")
+    assert 0 < kern <= call
+    assert torch.equal(out, out0)
