@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only time the streaming-read probe over 4 GiB (practical HBM read ceiling)")
     ap.add_argument("--traffic-csv", nargs=4, metavar=("DEC_FETCH", "DEC_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="reduce rocprofv3 counter CSVs to the decode kernel's HBM bytes per launch, "
                          "write the traffic record and exit (no GPU use)")
@@ -212,6 +214,27 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copy probe: 5 copies of 1073741824 bytes")
+        return
+    if args.read_probe:
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        props = torch.cuda.get_device_properties(dev)
+        best = None
+        for blocks in (props.multi_processor_count * 4, props.multi_processor_count * 8,
+                       props.multi_processor_count * 16):
+            o = torch.empty(blocks, dtype=torch.int32, device=dev)
+            for _ in range(2):
+                B.probe_stream_read(buf, o, blocks)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                B.probe_stream_read(buf, o, blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            gbps = 5 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+            log(f"read probe: {blocks} blocks x 256 threads, {gbps:.0f} GB/s")
+            best = max(best or 0.0, gbps)
+        print(json.dumps({"read_probe_GBps": best, "bytes": nbytes, "frac_of_8TBps": best / HBM_PEAK_GBPS}))
         return
     w = synth.WORKLOADS[args.workload]
     appends = args.warmup + args.steps if w.steps else 0

@@ -22,7 +22,7 @@ BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", 
              "codebook", "thresholds"]
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles",
-           "kvq_set_decode_events",
+           "kvq_set_decode_events", "kvq_probe_stream_read",
            "kvq_status_string"]
 
 
@@ -65,6 +65,8 @@ def lib():
         L.kvq_codebook_gaussian.argtypes = [i32, P, P]
         L.kvq_set_split_tiles.restype = None
         L.kvq_set_split_tiles.argtypes = [i32]
+        L.kvq_probe_stream_read.restype = i32
+        L.kvq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, i32, ctypes.c_void_p]
         L.kvq_set_decode_events.restype = None
         L.kvq_set_decode_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kvq_status_string.restype = ctypes.c_char_p
@@ -90,6 +92,17 @@ def codebook_gaussian(bits: int = 4):
 
 def set_split_tiles(n: int) -> None:
     lib().kvq_set_split_tiles(int(n))
+
+
+def probe_stream_read(buf, out, blocks: int) -> None:
+    """Read the whole uint8 device tensor `buf` once (see kvq_probe_stream_read)."""
+    import torch
+
+    st = lib().kvq_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                     ctypes.c_void_p(out.data_ptr()), int(blocks),
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise KvqError(st, "kvq_probe_stream_read")
 
 
 def set_decode_events(start=None, stop=None) -> None:

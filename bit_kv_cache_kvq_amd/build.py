@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_probe.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are disabled for all device code

@@ -298,6 +298,15 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
 
 void kvq_set_split_tiles(int32_t tiles_per_split) { g_split_tiles.store(tiles_per_split > 0 ? tiles_per_split : 0); }
 
+kvq_status kvq_probe_stream_read(const void *p, size_t bytes, uint32_t *out, int32_t blocks, void *stream)
+{
+    if (!p || !out || bytes == 0 || bytes % 16 != 0 || blocks < 1 || blocks > 65535)
+        return KVQ_ERR_ARG;
+    if (!aligned16(p) || !aligned16(out))
+        return KVQ_ERR_ALIGN;
+    return launch_stream_read(p, bytes, out, blocks, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
 void kvq_set_decode_events(void *start_event, void *stop_event)
 {
     g_decode_ev[0].store(start_event);

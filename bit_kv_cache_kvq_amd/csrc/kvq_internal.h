@@ -48,6 +48,8 @@ hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
 // ev[0], ev[1]: optional events recorded around the decode kernel (both non-null or unused)
 hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, bool merge,
                          hipEvent_t const ev[2], hipStream_t s);
+// Streaming-read probe over `bytes` (a multiple of 16) at p; out holds `blocks` words.
+hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *out, int blocks, hipStream_t s);
 // u32 words of one unit's query record (query-prep output read by the decode kernel).
 int decode_qrec_words(int head_dim, int group, int kfmt);
 // Resident decode workgroups (one wave each) the device holds for this instantiation.

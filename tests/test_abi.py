@@ -153,3 +153,12 @@ def test_library_codebook_equals_oracle_codebook(oracle_mod):
     oc, ot = oracle_mod.codebook_f32(16)
     np.testing.assert_array_equal(np.array(c, np.float32), oc)
     np.testing.assert_array_equal(np.array(t, np.float32), ot)
+
+
+def test_probe_argument_errors():
+    L = B.lib()
+    # checked on the host before anything is launched (no GPU needed)
+    assert L.kvq_probe_stream_read(None, 1024, FAKE, 4, None) == B.KVQ_ERR_ARG
+    assert L.kvq_probe_stream_read(FAKE, 1000, FAKE, 4, None) == B.KVQ_ERR_ARG
+    assert L.kvq_probe_stream_read(FAKE, 1024, FAKE, 0, None) == B.KVQ_ERR_ARG
+    assert L.kvq_probe_stream_read(FAKE + 8, 1024, FAKE, 4, None) == B.KVQ_ERR_ALIGN
