@@ -22,7 +22,8 @@
 //           * score phase, lane per position: each lane scores 2 consecutive positions; a
 //             key row is one dwordx2 load per lane (512 B contiguous per wave).  Asymmetric
 //             codes are spread into bytes by shift+mask and multiplied with v_dot4_i32_i8
-//             against the query held as a 16-bit integer in two signed-byte planes: exact
+//             against the query held as a 16-bit integer (14 bits of magnitude for INT2
+//             keys, whose spread bytes carry code or 4*code) in two signed-byte planes: exact
 //             int32 sums, and the zero-point term uses the same integer query, so code and
 //             zero terms together equal q_int . k^ with no cancellation between them
 //             (heavy-tailed keys make the group zero large).  Lloyd-Max codes go through an
@@ -148,6 +149,8 @@ typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 constexpr int kBufWord3 = 0x00020000; // raw 32-bit access, no format conversion
 constexpr int kNonTemporal = 2;
 constexpr uint32_t kNoAccess = 0x80000000u;
+// log2 slack of the lazily raised softmax maximum (weights stay below 2^kSlack)
+constexpr float kSlack = 2.0f;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -186,20 +189,30 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
     uint32_t *rec = p.qprep + (size_t)unit * C::QREC;
     float *recf = reinterpret_cast<float *>(rec);
 
+    // this wave is alone on its SIMD for most of its life: issue every global load of a
+    // phase before using any (one memory latency per phase, not per head or sink)
+    float yq[G][CPL];
+#pragma unroll
     for (int h = 0; h < G; h++) {
         const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
-        float y[CPL];
         if (p.q_bf16) {
             const uint16_t *qb = static_cast<const uint16_t *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                y[s] = bf16_to_f32(qb[s]);
+                yq[h][s] = bf16_to_f32(qb[s]);
         } else {
             const float *qf = static_cast<const float *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                y[s] = qf[s];
+                yq[h][s] = qf[s];
         }
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float y[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            y[s] = yq[h][s];
         if (p.rotate)
             fwht_wave<CPL>(y, lane);
         float sq[CPL], am = 0.0f;
@@ -285,20 +298,30 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
             for (int s = 0; s < CPL; s++)
                 qr[h][s] = sq_[h][lane * CPL + s];
         }
-        for (int t = 0; t < n_sink; t++) {
-            const uint16_t *sk = p.sink_k + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
-            float kv[CPL];
+        constexpr int SB = 8; // sinks per batch of loads
+        for (int t0 = 0; t0 < n_sink; t0 += SB) {
+            float kv[SB][CPL];
 #pragma unroll
-            for (int s = 0; s < CPL; s++)
-                kv[s] = bf16_to_f32(sk[s]);
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                float part = 0.0f;
+            for (int j = 0; j < SB; j++) {
+                const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
+                const uint16_t *sk = p.sink_k + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
 #pragma unroll
                 for (int s = 0; s < CPL; s++)
-                    part = fmaf(qr[h][s], kv[s], part);
-                const float tot = wave_sum_dpp(part);
-                mine[h] = lane == t ? tot : mine[h];
+                    kv[j][s] = bf16_to_f32(sk[s]);
+            }
+#pragma unroll
+            for (int j = 0; j < SB; j++) {
+                if (t0 + j >= n_sink)
+                    break;
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < CPL; s++)
+                        part = fmaf(qr[h][s], kv[j][s], part);
+                    const float tot = wave_sum_dpp(part);
+                    mine[h] = lane == t0 + j ? tot : mine[h];
+                }
             }
         }
         float l[G];
@@ -320,17 +343,26 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
 #pragma unroll
             for (int s = 0; s < CPL; s++)
                 o[h][s] = 0.0f;
-        for (int t = 0; t < n_sink; t++) {
-            const uint16_t *sv = p.sink_v + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
-            float vv[CPL];
+        for (int t0 = 0; t0 < n_sink; t0 += SB) {
+            float vv[SB][CPL];
 #pragma unroll
-            for (int s = 0; s < CPL; s++)
-                vv[s] = bf16_to_f32(sv[s]);
-#pragma unroll
-            for (int h = 0; h < G; h++)
+            for (int j = 0; j < SB; j++) {
+                const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
+                const uint16_t *sv = p.sink_v + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
 #pragma unroll
                 for (int s = 0; s < CPL; s++)
-                    o[h][s] = fmaf(sp[h][t], vv[s], o[h][s]);
+                    vv[j][s] = bf16_to_f32(sv[s]);
+            }
+#pragma unroll
+            for (int j = 0; j < SB; j++) {
+                if (t0 + j >= n_sink)
+                    break;
+#pragma unroll
+                for (int h = 0; h < G; h++)
+#pragma unroll
+                    for (int s = 0; s < CPL; s++)
+                        o[h][s] = fmaf(sp[h][t0 + j], vv[j][s], o[h][s]);
+            }
         }
 #pragma unroll
         for (int h = 0; h < G; h++)
@@ -366,8 +398,11 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
         }
     } else {
         for (int h = 0; h < G; h++) {
-            // 16-bit integer query: q ~= qi * unit, |qi| <= 32639, written as 256*hi + lo
-            // with signed bytes hi, lo.  Channel 0 is scored from its BF16 copy instead.
+            // Integer query: q ~= qi * unit, written as 256*hi + lo with signed bytes hi, lo.
+            // INT2 keys: the decode kernel spreads a code word into bytes holding code or
+            // 4*code (masks without shifts for half of them), so the plane entries of the
+            // unscaled codes carry 4*qi; every sum is then 4*(q_int . code), |qi| <= 8159.
+            // 4-bit keys: plain codes, |qi| <= 32639.  Channel 0 is scored from its BF16 copy.
             float am = 0.0f;
 #pragma unroll
             for (int s2 = 0; s2 < CPL; s2++) {
@@ -376,7 +411,8 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
                     am = fmaxf(am, fabsf(sq_[h][c]));
             }
             am = wave_max_dpp(am);
-            const float unit_q = am > 0.0f ? am / 32639.0f : 1.0f;
+            constexpr int F = KB == 2 ? 4 : 1;
+            const float unit_q = am > 0.0f ? am / (KB == 2 ? 8159.0f : 32639.0f) : 1.0f;
             const float inv = 1.0f / unit_q;
             // key word r, spread register k: byte m holds channel r*(32/KB) + m*(KB==2 ? 4 : 2) + k;
             // words per (row, head): hi planes of registers 0..NREG-1, then the lo planes
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
                 for (int m = 0; m < 4; m++) {
                     const int c = (KB == 2) ? 16 * r + 4 * m + k : 8 * r + 2 * m + k;
                     const float qv = (p.ch0 && c == 0) ? 0.0f : sq_[h][c];
-                    const int qi = (int)__builtin_rintf(qv * inv);
+                    const int qi = (int)__builtin_rintf(qv * inv) * ((KB == 2 && k % 2 == 0) ? 4 : 1);
                     const int h8 = (qi + 128) >> 8;
                     const int l8 = qi - 256 * h8;
                     hi |= (uint32_t)(h8 & 0xFF) << (8 * m);
@@ -396,16 +432,25 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
                 rec[C::OFF_QP + (r * G + h) * QW + k] = hi;
                 rec[C::OFF_QP + (r * G + h) * QW + C::NREG + k] = lo;
             }
-            if (lane < NG) {
+            // zero-term sums: integer query summed over each 32-channel group (lanes of a
+            // group: 32/CPL consecutive lanes; integer-valued floats below 2^24, exact)
+            {
                 float si = 0.0f;
-                for (int c = 32 * lane; c < 32 * lane + 32; c++)
+#pragma unroll
+                for (int s2 = 0; s2 < CPL; s2++) {
+                    const int c = lane * CPL + s2;
                     if (!(p.ch0 && c == 0))
                         si += __builtin_rintf(sq_[h][c] * inv);
-                recf[C::OFF_QZ + h * NG + lane] = si;
+                }
+#pragma unroll
+                for (int m = 16 / CPL; m >= 1; m >>= 1)
+                    si += __shfl_xor(si, m);
+                if (lane % (32 / CPL) == 0)
+                    recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si * F;
             }
             if (lane == 0) {
-                recf[C::OFF_QSC + h] = unit_q;
-                recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv : 0.0f;
+                recf[C::OFF_QSC + h] = unit_q / F;
+                recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv * F : 0.0f;
             }
         }
     }
@@ -438,7 +483,7 @@ struct Slabs {
 // off: 0, or kNoAccess to turn every load into a zero without a memory access
 template <int D, int G, int KF>
 __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, uint32_t cap, int lane, int t0,
-                                           uint32_t mask, uint32_t off)
+                                           uint32_t mask, uint32_t off, int ch0)
 {
     using C = Cfg<D, G, KF>;
     const uint32_t vo = (uint32_t)lane * C::TPL * 4u + off;  // lane's 2 positions of a u32 row
@@ -452,10 +497,10 @@ __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, 
             if (mask >> (2 * g) & 3u)
                 k.ksz[g] = bload2(sl.ksz, vo, ((uint32_t)g * cap + (uint32_t)t0) * 4u);
         k.kx = 0;
-        if (mask & 1u)
-            k.kx = bload1(sl.kx, (uint32_t)lane * C::TPL * 2u + off, (uint32_t)t0 * 2u);
+        if (ch0 && (mask & 1u))
+            k.kx = bload1(sl.kx, vo >> 1, (uint32_t)t0 * 2u); // u16 row: half the u32 offset
     } else {
-        k.kx = bload1(sl.kx, (uint32_t)lane * C::TPL * 2u + off, (uint32_t)t0 * 2u);
+        k.kx = bload1(sl.kx, vo >> 1, (uint32_t)t0 * 2u);
     }
 #pragma unroll
     for (int g = 0; g < C::NG; g++)
@@ -488,10 +533,13 @@ __device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const uin
             for (int i = 0; i < TPL; i++) {
                 const uint32_t x = i == 0 ? cur.kc[r].x : cur.kc[r].y;
                 if constexpr (KB == 2) {
+                    // bytes hold code (registers 0, 2) or 4*code (1, 3); the query planes
+                    // of registers 0 and 2 carry the matching factor 4
+                    const uint32_t y = x >> 4;
                     bsp[rr][i][0] = x & 0x03030303u;
-                    bsp[rr][i][1] = (x >> 2) & 0x03030303u;
-                    bsp[rr][i][2] = (x >> 4) & 0x03030303u;
-                    bsp[rr][i][3] = (x >> 6) & 0x03030303u;
+                    bsp[rr][i][1] = x & 0x0C0C0C0Cu;
+                    bsp[rr][i][2] = y & 0x03030303u;
+                    bsp[rr][i][3] = y & 0x0C0C0C0Cu;
                 } else {
                     bsp[rr][i][0] = x & 0x0F0F0F0Fu;
                     bsp[rr][i][1] = (x >> 4) & 0x0F0F0F0Fu;
@@ -731,7 +779,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         // key-side words and value words of the current tile; value word pair `it` is
         // reloaded with the next tile's right after its last use, so each load has a whole
         // tile of work to arrive
-        load_ktile<D, G, KF>(cur, sl, ucap, lane, t * TILE, mask, 0u);
+        load_ktile<D, G, KF>(cur, sl, ucap, lane, t * TILE, mask, 0u, p.ch0);
 #pragma unroll
         for (int it = 0; it < VIT; it++)
             vcur[it] = bload2(sl.vc, vvo, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
@@ -815,20 +863,21 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             // the loads access nothing: the next unit's first tile is loaded after the flush,
             // outside the inner loop and its register peak.
             const uint32_t noff = more ? 0u : kNoAccess;
-            load_ktile<D, G, KF>(cur, sl, ucap, lane, tn * TILE, mask, noff);
+            load_ktile<D, G, KF>(cur, sl, ucap, lane, tn * TILE, mask, noff, p.ch0);
 
-            // ---- online softmax (log2 units); wave-wide max only when some logit exceeds
-            // the running maximum (the test compares in accumulator units against
-            // mthr = mrun / acc_to_logit; a rounding miss only lets a weight exceed 1 by an ulp)
-            uint64_t above = 0;
+            // ---- online softmax (log2 units), per head.  The running maximum m is raised
+            // (wave-wide DPP max, rescale of that head's state) only when a logit exceeds
+            // m + kSlack; otherwise weights 2^(l - m) may reach 2^kSlack, which keeps every
+            // fp16 weight p*s finite (s < 2^14 for inputs below 65504) and makes the raise
+            // rare after the first tile.  The test runs in accumulator units against
+            // mthr = (m + kSlack) / acc_to_logit; a rounding miss is harmless.
 #pragma unroll
-            for (int h = 0; h < G; h++)
+            for (int h = 0; h < G; h++) {
+                uint64_t above = 0;
 #pragma unroll
                 for (int i = 0; i < TPL; i++)
                     above |= __ballot(lg[i][h] > mthr[h]);
-            if (above) {
-#pragma unroll
-                for (int h = 0; h < G; h++) {
+                if (above) {
                     float mt = lg[0][h];
 #pragma unroll
                     for (int i = 1; i < TPL; i++)
@@ -836,7 +885,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     const float mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
                     const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);
                     mrun[h] = mnew;
-                    mthr[h] = mnew * logit_to_acc[h];
+                    mthr[h] = (mnew + kSlack) * logit_to_acc[h];
                     lsum[h] *= alpha;
 #pragma unroll
                     for (int j = 0; j < 8; j++)
@@ -891,7 +940,6 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
             for (int it = 0; it < VIT; it++) {
                 const uint2 vv = vcur[it];
-                vcur[it] = bload2(sl.vc, vvo + noff, vnext + (uint32_t)(it * PPI * WPP) * 4u);
                 const int pl = it * PPI + lane / LPP;
                 uint32_t wv[4 * WV];
 #pragma unroll
@@ -916,6 +964,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                         acc[h][4 * q2 + 3] = dot2(c3, wv[h], acc[h][4 * q2 + 3]);
                     }
                 }
+                // reload after the last use, into the same registers
+                vcur[it] = bload2(sl.vc, vvo + noff, vnext + (uint32_t)(it * PPI * WPP) * 4u);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -948,21 +998,11 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
     const int n = w_hi - w_lo + 1;
     // the sink positions' state from the unit's query record
     const float *sk = reinterpret_cast<const float *>(p.qprep + (size_t)u * QREC) + OFF_SINK + h * (D + 2);
-    // the partials are read in batches of 8 with independent loads (one memory latency per
-    // batch rather than per partial)
+    // one pass, the partials read in batches of 8 with independent loads (one memory
+    // latency per batch): running maximum M, sum L and output O, rescaled as M grows
     constexpr int NB = 8;
     float M = sk[0];
-    for (int s0 = 0; s0 < n; s0 += NB) {
-        float mv[NB];
-#pragma unroll
-        for (int j = 0; j < NB; j++)
-            mv[j] = s0 + j < n ? pb[(s0 + j) * stride] : -__builtin_inff();
-#pragma unroll
-        for (int j = 0; j < NB; j++)
-            M = fmaxf(M, mv[j]);
-    }
-    const float fs = sk[0] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(sk[0] - M);
-    float L = sk[1] * fs, O = sk[2 + c] * fs;
+    float L = sk[1], O = sk[2 + c];
     for (int s0 = 0; s0 < n; s0 += NB) {
         float mv[NB], lv[NB], ov[NB];
 #pragma unroll
@@ -975,9 +1015,14 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
         }
 #pragma unroll
         for (int j = 0; j < NB; j++) {
-            const float f = mv[j] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mv[j] - M);
-            L = fmaf(lv[j], f, L);
-            O = fmaf(ov[j], f, O);
+            if (mv[j] == -__builtin_inff())
+                continue;
+            const float Mn = fmaxf(M, mv[j]);
+            const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+            const float fn = __builtin_amdgcn_exp2f(mv[j] - Mn);
+            L = fmaf(L, fo, lv[j] * fn);
+            O = fmaf(O, fo, ov[j] * fn);
+            M = Mn;
         }
     }
     const int b = u / p.n_kv_heads;
