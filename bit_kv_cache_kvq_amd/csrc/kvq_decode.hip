@@ -167,11 +167,11 @@ __device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t sof
 }
 
 // ===================================================================== query prep
-// One wave per unit: stored-coordinate query (FWHT when keys are rotated), 16-channel
-// group energies (fp32 stride-halving tree, the order the format fixes), mask, and the
-// query operands of the decode kernel.
+// One workgroup per unit, one wave per query head of the GQA group: stored-coordinate query
+// (FWHT when keys are rotated), 16-channel group energies (fp32 stride-halving tree, the
+// order the format fixes), the group's mask, and the head's query operands and sink state.
 template <int D, int G, int KF>
-__global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
+__global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
 {
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
     __shared__ float sam[G][NP];
     __shared__ float sp[G][kWave];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave;
+    const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
     const int unit = blockIdx.x;
     const int b = unit / p.n_kv_heads;
     const int kvh = unit % p.n_kv_heads;
@@ -189,30 +190,20 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
     uint32_t *rec = p.qprep + (size_t)unit * C::QREC;
     float *recf = reinterpret_cast<float *>(rec);
 
-    // this wave is alone on its SIMD for most of its life: issue every global load of a
-    // phase before using any (one memory latency per phase, not per head or sink)
-    float yq[G][CPL];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
+    {
         const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
+        float y[CPL];
         if (p.q_bf16) {
             const uint16_t *qb = static_cast<const uint16_t *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                yq[h][s] = bf16_to_f32(qb[s]);
+                y[s] = bf16_to_f32(qb[s]);
         } else {
             const float *qf = static_cast<const float *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                yq[h][s] = qf[s];
+                y[s] = qf[s];
         }
-    }
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        float y[CPL];
-#pragma unroll
-        for (int s = 0; s < CPL; s++)
-            y[s] = yq[h][s];
         if (p.rotate)
             fwht_wave<CPL>(y, lane);
         float sq[CPL], am = 0.0f;
@@ -241,8 +232,8 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
     }
     __syncthreads();
 
-    // mask: keep the `keep` highest group energies summed over the heads in ascending
-    // head order, ties to the lower group
+    // mask (every wave computes the same one): keep the `keep` highest group energies
+    // summed over the heads in ascending head order, ties to the lower group
     uint32_t mask = (1u << NP) - 1u;
     if (p.keep > 0 && p.keep < NP) {
         float E[NP];
@@ -250,8 +241,8 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
         for (int g = 0; g < NP; g++) {
             float acc = se[0][g];
 #pragma unroll
-            for (int h = 1; h < G; h++)
-                acc = acc + se[h][g];
+            for (int hh = 1; hh < G; hh++)
+                acc = acc + se[hh][g];
             E[g] = acc;
         }
         mask = 0;
@@ -266,38 +257,31 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
         }
     }
     mask = uniform(mask);
-    if (lane == 0) {
+    if (threadIdx.x == 0) {
         rec[C::OFF_MASK] = mask;
         if (p.mask_out)
             p.mask_out[unit] = (uint8_t)mask;
     }
     const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
 
-    // scaled, masked fp32 query
-    for (int h = 0; h < G; h++) {
+    // this head's scaled, masked fp32 query
+    float qr[CPL];
 #pragma unroll
-        for (int s = 0; s < CPL; s++) {
-            const int c = lane * CPL + s;
-            const bool kept = (mask >> (c / 16)) & 1u;
-            sq_[h][c] = kept ? sq_[h][c] * qscale : 0.0f;
-        }
+    for (int s = 0; s < CPL; s++) {
+        const int c = lane * CPL + s;
+        const bool kept = (mask >> (c / 16)) & 1u;
+        qr[s] = kept ? sq_[h][c] * qscale : 0.0f;
+        sq_[h][c] = qr[s];
     }
     __syncthreads();
 
     // BF16 sink positions (t < min(n_sink, len)): dense dot over the kept channels, then
-    // their softmax state per head -- log2 max m, sum l and o = sum_t 2^(l_t - m) v_t --
-    // which the decode and merge kernels fold into the unit's result.  Lanes own channels;
-    // one wave-wide sum per (sink, head) gives the logits, lane t keeps those of sink t.
+    // the head's softmax state over them -- log2 max m, sum l and o = sum_t 2^(l_t - m) v_t
+    // -- which the decode and merge kernels fold into the unit's result.  Lanes own
+    // channels; one wave-wide sum per sink gives its logit, lane t keeps that of sink t.
     {
         const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
-        float qr[G][CPL], mine[G];
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            mine[h] = -__builtin_inff();
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                qr[h][s] = sq_[h][lane * CPL + s];
-        }
+        float mine = -__builtin_inff();
         constexpr int SB = 8; // sinks per batch of loads
         for (int t0 = 0; t0 < n_sink; t0 += SB) {
             float kv[SB][CPL];
@@ -313,36 +297,27 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
             for (int j = 0; j < SB; j++) {
                 if (t0 + j >= n_sink)
                     break;
+                float part = 0.0f;
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    float part = 0.0f;
-#pragma unroll
-                    for (int s = 0; s < CPL; s++)
-                        part = fmaf(qr[h][s], kv[j][s], part);
-                    const float tot = wave_sum_dpp(part);
-                    mine[h] = lane == t0 + j ? tot : mine[h];
-                }
+                for (int s = 0; s < CPL; s++)
+                    part = fmaf(qr[s], kv[j][s], part);
+                const float tot = wave_sum_dpp(part);
+                mine = lane == t0 + j ? tot : mine;
             }
         }
-        float l[G];
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            const float m = wave_max_dpp(mine[h]);
-            const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine[h] - m) : 0.0f;
-            sp[h][lane] = pr;
-            l[h] = wave_sum_dpp(pr);
-            if (lane == 0) {
-                recf[C::OFF_SINK + h * (D + 2)] = m;
-                recf[C::OFF_SINK + h * (D + 2) + 1] = l[h];
-            }
+        const float m = wave_max_dpp(mine);
+        const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine - m) : 0.0f;
+        sp[h][lane] = pr;
+        const float l = wave_sum_dpp(pr);
+        if (lane == 0) {
+            recf[C::OFF_SINK + h * (D + 2)] = m;
+            recf[C::OFF_SINK + h * (D + 2) + 1] = l;
         }
         __syncthreads();
-        float o[G][CPL];
+        float o[CPL];
 #pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                o[h][s] = 0.0f;
+        for (int s = 0; s < CPL; s++)
+            o[s] = 0.0f;
         for (int t0 = 0; t0 < n_sink; t0 += SB) {
             float vv[SB][CPL];
 #pragma unroll
@@ -358,100 +333,92 @@ __global__ __launch_bounds__(kWave) void qprep_kernel(DecodeParams p)
                 if (t0 + j >= n_sink)
                     break;
 #pragma unroll
-                for (int h = 0; h < G; h++)
-#pragma unroll
-                    for (int s = 0; s < CPL; s++)
-                        o[h][s] = fmaf(sp[h][t0 + j], vv[j][s], o[h][s]);
+                for (int s = 0; s < CPL; s++)
+                    o[s] = fmaf(sp[h][t0 + j], vv[j][s], o[s]);
             }
         }
 #pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                recf[C::OFF_SINK + h * (D + 2) + 2 + lane * CPL + s] = o[h][s];
+        for (int s = 0; s < CPL; s++)
+            recf[C::OFF_SINK + h * (D + 2) + 2 + lane * CPL + s] = o[s];
     }
 
     if constexpr (KF == KVQ_K_LLOYD4) {
-        // fp16 pairs scaled so the largest kept |q| lands in [2^12, 2^13); byte j of key
-        // word r holds channels (8r + 2j, 8r + 2j + 1)
+        // fp16 pairs scaled so the largest kept |q| of the group lands in [2^12, 2^13);
+        // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
         float amax = 0.0f;
 #pragma unroll
-        for (int h = 0; h < G; h++)
+        for (int hh = 0; hh < G; hh++)
 #pragma unroll
             for (int g = 0; g < NP; g++)
                 if (mask >> g & 1u)
-                    amax = fmaxf(amax, sam[h][g]);
+                    amax = fmaxf(amax, sam[hh][g]);
         amax *= qscale;
         int ex = 0;
         (void)frexpf(amax, &ex);
         const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
-        for (int h = 0; h < G; h++) {
-            if (lane < KROWS * PPW) {
-                const int r = lane / PPW, j = lane % PPW;
-                const int ca = 8 * r + 2 * j;
-                rec[C::OFF_QP + (r * G + h) * QW + j] = pack_f16x2(sq_[h][ca] * g2, sq_[h][ca + 1] * g2);
-            }
-            if (lane == 0) {
-                recf[C::OFF_QSC + h] = 1.0f / g2;
-                recf[C::OFF_Q0 + h] = 0.0f;
-            }
+        if (lane < KROWS * PPW) {
+            const int r = lane / PPW, j = lane % PPW;
+            const int ca = 8 * r + 2 * j;
+            rec[C::OFF_QP + (r * G + h) * QW + j] = pack_f16x2(sq_[h][ca] * g2, sq_[h][ca + 1] * g2);
+        }
+        if (lane == 0) {
+            recf[C::OFF_QSC + h] = 1.0f / g2;
+            recf[C::OFF_Q0 + h] = 0.0f;
         }
     } else {
-        for (int h = 0; h < G; h++) {
-            // Integer query: q ~= qi * unit, written as 256*hi + lo with signed bytes hi, lo.
-            // INT2 keys: the decode kernel spreads a code word into bytes holding code or
-            // 4*code (masks without shifts for half of them), so the plane entries of the
-            // unscaled codes carry 4*qi; every sum is then 4*(q_int . code), |qi| <= 8159.
-            // 4-bit keys: plain codes, |qi| <= 32639.  Channel 0 is scored from its BF16 copy.
-            float am = 0.0f;
+        // Integer query: q ~= qi * unit, written as 256*hi + lo with signed bytes hi, lo.
+        // INT2 keys: the decode kernel spreads a code word into bytes holding code or
+        // 4*code (masks without shifts for half of them), so the plane entries of the
+        // unscaled codes carry 4*qi; every sum is then 4*(q_int . code), |qi| <= 8159.
+        // 4-bit keys: plain codes, |qi| <= 32639.  Channel 0 is scored from its BF16 copy.
+        float am = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < CPL; s2++) {
+            const int c = lane * CPL + s2;
+            if (!(p.ch0 && c == 0))
+                am = fmaxf(am, fabsf(qr[s2]));
+        }
+        am = wave_max_dpp(am);
+        constexpr int F = KB == 2 ? 4 : 1;
+        const float unit_q = am > 0.0f ? am / (KB == 2 ? 8159.0f : 32639.0f) : 1.0f;
+        const float inv = 1.0f / unit_q;
+        // key word r, spread register k: byte m holds channel r*(32/KB) + m*(KB==2 ? 4 : 2) + k;
+        // words per (row, head): hi planes of registers 0..NREG-1, then the lo planes
+        if (lane < KROWS * C::NREG) {
+            const int r = lane / C::NREG, k = lane % C::NREG;
+            uint32_t hi = 0, lo = 0;
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const int c = (KB == 2) ? 16 * r + 4 * m + k : 8 * r + 2 * m + k;
+                const float qv = (p.ch0 && c == 0) ? 0.0f : sq_[h][c];
+                const int qi = (int)__builtin_rintf(qv * inv) * ((KB == 2 && k % 2 == 0) ? 4 : 1);
+                const int h8 = (qi + 128) >> 8;
+                const int l8 = qi - 256 * h8;
+                hi |= (uint32_t)(h8 & 0xFF) << (8 * m);
+                lo |= (uint32_t)(l8 & 0xFF) << (8 * m);
+            }
+            rec[C::OFF_QP + (r * G + h) * QW + k] = hi;
+            rec[C::OFF_QP + (r * G + h) * QW + C::NREG + k] = lo;
+        }
+        // zero-term sums: integer query summed over each 32-channel group (lanes of a
+        // group: 32/CPL consecutive lanes; integer-valued floats below 2^24, exact)
+        {
+            float si = 0.0f;
 #pragma unroll
             for (int s2 = 0; s2 < CPL; s2++) {
                 const int c = lane * CPL + s2;
                 if (!(p.ch0 && c == 0))
-                    am = fmaxf(am, fabsf(sq_[h][c]));
+                    si += __builtin_rintf(qr[s2] * inv);
             }
-            am = wave_max_dpp(am);
-            constexpr int F = KB == 2 ? 4 : 1;
-            const float unit_q = am > 0.0f ? am / (KB == 2 ? 8159.0f : 32639.0f) : 1.0f;
-            const float inv = 1.0f / unit_q;
-            // key word r, spread register k: byte m holds channel r*(32/KB) + m*(KB==2 ? 4 : 2) + k;
-            // words per (row, head): hi planes of registers 0..NREG-1, then the lo planes
-            if (lane < KROWS * C::NREG) {
-                const int r = lane / C::NREG, k = lane % C::NREG;
-                uint32_t hi = 0, lo = 0;
 #pragma unroll
-                for (int m = 0; m < 4; m++) {
-                    const int c = (KB == 2) ? 16 * r + 4 * m + k : 8 * r + 2 * m + k;
-                    const float qv = (p.ch0 && c == 0) ? 0.0f : sq_[h][c];
-                    const int qi = (int)__builtin_rintf(qv * inv) * ((KB == 2 && k % 2 == 0) ? 4 : 1);
-                    const int h8 = (qi + 128) >> 8;
-                    const int l8 = qi - 256 * h8;
-                    hi |= (uint32_t)(h8 & 0xFF) << (8 * m);
-                    lo |= (uint32_t)(l8 & 0xFF) << (8 * m);
-                }
-                rec[C::OFF_QP + (r * G + h) * QW + k] = hi;
-                rec[C::OFF_QP + (r * G + h) * QW + C::NREG + k] = lo;
-            }
-            // zero-term sums: integer query summed over each 32-channel group (lanes of a
-            // group: 32/CPL consecutive lanes; integer-valued floats below 2^24, exact)
-            {
-                float si = 0.0f;
-#pragma unroll
-                for (int s2 = 0; s2 < CPL; s2++) {
-                    const int c = lane * CPL + s2;
-                    if (!(p.ch0 && c == 0))
-                        si += __builtin_rintf(sq_[h][c] * inv);
-                }
-#pragma unroll
-                for (int m = 16 / CPL; m >= 1; m >>= 1)
-                    si += __shfl_xor(si, m);
-                if (lane % (32 / CPL) == 0)
-                    recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si * F;
-            }
-            if (lane == 0) {
-                recf[C::OFF_QSC + h] = unit_q / F;
-                recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv * F : 0.0f;
-            }
+            for (int m = 16 / CPL; m >= 1; m >>= 1)
+                si += __shfl_xor(si, m);
+            if (lane % (32 / CPL) == 0)
+                recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si * F;
+        }
+        if (lane == 0) {
+            recf[C::OFF_QSC + h] = unit_q / F;
+            recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv * F : 0.0f;
         }
     }
 }
@@ -1035,7 +1002,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
 template <int D, int G, int KF>
 hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2], hipStream_t s)
 {
-    hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
