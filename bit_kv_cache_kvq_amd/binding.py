@@ -21,7 +21,7 @@ K_ASYM2, K_ASYM4, K_LLOYD4 = 0, 1, 2
 BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", "sink_v",
              "codebook", "thresholds"]
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles",
+           "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles", "kvq_set_deterministic",
            "kvq_set_decode_events", "kvq_probe_stream_read",
            "kvq_status_string"]
 
@@ -65,6 +65,8 @@ def lib():
         L.kvq_codebook_gaussian.argtypes = [i32, P, P]
         L.kvq_set_split_tiles.restype = None
         L.kvq_set_split_tiles.argtypes = [i32]
+        L.kvq_set_deterministic.restype = None
+        L.kvq_set_deterministic.argtypes = [i32]
         L.kvq_probe_stream_read.restype = i32
         L.kvq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, i32, ctypes.c_void_p]
         L.kvq_set_decode_events.restype = None
@@ -92,6 +94,11 @@ def codebook_gaussian(bits: int = 4):
 
 def set_split_tiles(n: int) -> None:
     lib().kvq_set_split_tiles(int(n))
+
+
+def set_deterministic(on: bool) -> None:
+    """Fixed tile-to-wave assignment (bit-identical repeat calls) instead of run-time draws."""
+    lib().kvq_set_deterministic(1 if on else 0)
 
 
 def probe_stream_read(buf, out, blocks: int) -> None:

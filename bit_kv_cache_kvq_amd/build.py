@@ -22,8 +22,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
-# Per-source extra flags (none at present).
-SOURCE_FLAGS: dict[str, list[str]] = {}
+# Per-source extra flags.  The decode kernel's tile-counter atomic is issued by one lane and
+# its return is read a tile later; the compiler's atomic optimizer would rewrite it as a
+# wave-wide atomic whose result is broadcast (and waited for) on the spot.
+SOURCE_FLAGS: dict[str, list[str]] = {
+    "kvq_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
 BUILD_DIR = os.path.join(HERE, "_build")
 
 

@@ -14,6 +14,7 @@ using namespace kvq;
 namespace {
 
 std::atomic<int> g_split_tiles{0};
+std::atomic<int> g_deterministic{0};
 std::atomic<void *> g_decode_ev[2] = {{nullptr}, {nullptr}};
 
 int key_bits(int kfmt) { return kfmt == KVQ_K_ASYM2 ? 2 : 4; }
@@ -89,23 +90,24 @@ kvq_status check_buffers(const kvq_cache *c)
 
 struct Plan {
     int tiles_per_unit, n_waves;
-    bool merge; // some unit is shared by several waves
+    bool merge; // some unit is served by several waves
 };
 
 // Work split of one decode call.  Every unit's positions [0, len) are cut into 128-position
-// tiles (at least one, so sink-only and empty contexts still produce their output); the
-// tiles of all units, unit after unit, are cut into n_waves contiguous ranges of equal
-// size (+-1 tile), one per decode wave.  n_waves = the resident one-wave workgroups of the
-// kernel instantiation (`slots`), so one pass of waves covers the device with no tail, or
-// fewer when there are fewer tiles.  kvq_set_split_tiles overrides it with a target
-// number of tiles per wave.
+// tiles (at least one, so sink-only and empty contexts still produce their output).  The
+// grid is n_waves one-wave workgroups, n_waves >= units: wave w serves unit w % units, and
+// the waves of one unit draw its tiles from a shared counter at run time.  n_waves = the
+// resident one-wave workgroups of the kernel instantiation (`slots`), so one pass of waves
+// covers the device, capped at one wave per tile; kvq_set_split_tiles overrides it with a
+// target number of tiles per wave.
 Plan plan_splits(const kvq_cache *c, int len, int slots)
 {
     Plan pl;
     pl.tiles_per_unit = (len + kTile - 1) / kTile;
     if (pl.tiles_per_unit < 1)
         pl.tiles_per_unit = 1;
-    const long long total = (long long)units_of(c) * pl.tiles_per_unit;
+    const long long U = units_of(c);
+    const long long total = U * pl.tiles_per_unit;
     long long W = slots > 0 ? slots : 1;
     const int tps = g_split_tiles.load();
     if (tps > 0)
@@ -114,21 +116,18 @@ Plan plan_splits(const kvq_cache *c, int len, int slots)
         W = total;
     if (W > kMaxWaves)
         W = kMaxWaves;
-    if (W < 1)
-        W = 1;
+    if (W < U)
+        W = U; // one wave per unit at least (more units than slots: the dispatcher balances)
     pl.n_waves = (int)W;
-    // every unit sits whole in one wave when units are single tiles, or when the ranges are
-    // equal whole multiples of a unit
-    pl.merge = !(pl.tiles_per_unit == 1 || (total % W == 0 && (total / W) % pl.tiles_per_unit == 0));
+    pl.merge = W > U;
     return pl;
 }
 
-// Partial-state slots: slot = wave + unit < max waves + units.
+// Partial-state slots: one per wave when units share waves (n_waves <= both bounds then).
 size_t part_slots(const kvq_cache *c)
 {
     const long long max_tiles = (long long)units_of(c) * (c->capacity / kTile);
-    const long long w = max_tiles < kMaxWaves ? max_tiles : kMaxWaves;
-    return (size_t)w + units_of(c);
+    return (size_t)(max_tiles < kMaxWaves ? max_tiles : kMaxWaves);
 }
 
 } // namespace
@@ -209,10 +208,15 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace: partial softmax states [slots][G][D + 2] fp32, then the query records
+// workspace: partial softmax states [slots][G][D + 2] fp32, the query records, the tile counters
 static size_t part_region_bytes(const kvq_cache *c, int G)
 {
     return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float));
+}
+
+static size_t qrec_region_bytes(const kvq_cache *c, int G)
+{
+    return round256(units_of(c) * (size_t)decode_qrec_words(c->head_dim, G, c->k_format) * sizeof(uint32_t));
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
@@ -221,8 +225,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
         return 0;
     const size_t U = units_of(c);
     const size_t G = (size_t)(n_q_heads / c->n_kv_heads);
-    return part_region_bytes(c, (int)G) +
-           round256(U * (size_t)decode_qrec_words(c->head_dim, (int)G, c->k_format) * sizeof(uint32_t));
+    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + round256(U * sizeof(uint32_t));
 }
 
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
@@ -276,6 +279,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.mask_out = mask_out;
     p.part = static_cast<float *>(ws);
     p.qprep = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + part_region_bytes(c, G));
+    p.tile_ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + part_region_bytes(c, G) +
+                                              qrec_region_bytes(c, G));
     p.n_kv_heads = c->n_kv_heads;
     p.cap = c->capacity;
     p.len = c->len;
@@ -288,6 +293,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.n_units = (int)U;
     p.tiles_per_unit = pl.tiles_per_unit;
     p.n_waves = pl.n_waves;
+    p.dynamic = !g_deterministic.load();
+    p.n_cu = device_cus();
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
     if (!ev[0] || !ev[1])
         ev[0] = ev[1] = nullptr;
@@ -297,6 +304,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
 }
 
 void kvq_set_split_tiles(int32_t tiles_per_split) { g_split_tiles.store(tiles_per_split > 0 ? tiles_per_split : 0); }
+
+void kvq_set_deterministic(int32_t on) { g_deterministic.store(on ? 1 : 0); }
 
 kvq_status kvq_probe_stream_read(const void *p, size_t bytes, uint32_t *out, int32_t blocks, void *stream)
 {

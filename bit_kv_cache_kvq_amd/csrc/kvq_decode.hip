@@ -258,6 +258,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     }
     mask = uniform(mask);
     if (threadIdx.x == 0) {
+        p.tile_ctr[unit] = 0u; // the decode kernel's tile counter of this unit
         rec[C::OFF_MASK] = mask;
         if (p.mask_out)
             p.mask_out[unit] = (uint8_t)mask;
@@ -580,29 +581,61 @@ __device__ __forceinline__ Slabs unit_slabs(const DecodeParams &p, int u)
     return sl;
 }
 
-// First global tile of wave w when `total` tiles (unit-major: unit u owns tiles
-// u*Tu .. u*Tu+Tu-1) are cut into W contiguous, equal (+-1) ranges.
-__device__ __forceinline__ int wave_first_tile(int w, long long total, int W)
+// Work split (one wave per workgroup, W waves, U units, W >= U).  Wave w takes the place
+// x = team_slot(w): it serves unit x mod U as member x / U of that unit's team; the team has
+// W / U members, one more for the first W mod U units.  Member k scores tile k first; every
+// further tile comes from the unit's counter (tiles team_size, team_size + 1, ... in the
+// order the members ask), so a member that gets more issue slots takes more tiles and the
+// whole team ends together.  In the deterministic mode member k takes tiles k, k + n, ...
+// of a team of n instead.
+__device__ __forceinline__ int team_size(int u, int U, int W) { return W / U + (u < W % U ? 1 : 0); }
+
+// Issue priority from a team's progress: the tile a wave is on (tiles are taken in
+// increasing order, so it tracks how far the whole team is), in the bands [0, 1/2),
+// [1/2, 3/4), [3/4, 7/8), [7/8, 1) of the unit.  The waves sharing a SIMD otherwise issue
+// oldest first, which lets whole teams fall behind others; a team in an earlier band now
+// goes first, so teams advance together, and the narrow last band bounds how far apart
+// they end.
+__device__ __forceinline__ void set_priority_for(int t, int Tu)
 {
-    return (int)((long long)w * total / W);
+    const int q = (int)(((long long)t * 8) / Tu); // 0..7, uniform
+    if (q < 4)
+        __builtin_amdgcn_s_setprio(3);
+    else if (q < 6)
+        __builtin_amdgcn_s_setprio(2);
+    else if (q < 7)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
 }
 
-// Last wave whose range starts at or before global tile x.
-__device__ __forceinline__ int wave_of_tile(long long x, long long total, int W)
+// Place of wave w.  Workgroups are dealt to compute units in turn, so waves w, w + n_cu,
+// w + 2 n_cu, ... share a CU, and the older of them get more of its issue slots.  When W is
+// a multiple of n_cu the places of one CU's waves are made consecutive (x = (w mod n_cu) *
+// (W / n_cu) + w / n_cu): the members of a team, U places apart, then sit on different CUs
+// at different ages, and no team gets a much larger or smaller share of the device.
+__device__ __forceinline__ int team_slot(int w, int W, int n_cu)
 {
-    return (int)(((x + 1) * W + total - 1) / total) - 1;
+    return (n_cu > 0 && W % n_cu == 0) ? (w % n_cu) * (W / n_cu) + w / n_cu : w;
+}
+
+// Next tile number from a unit's counter, called by lane 0 only; the return is read a tile
+// later (the library builds this file with the compiler's atomic optimizer off, which would
+// otherwise broadcast the result, and wait for it, on the spot).
+__device__ __forceinline__ uint32_t draw_tile(uint32_t *ctr)
+{
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
 // (twice the key words in flight) and 8 heads get 2.
 //
-// Work split: the grid holds one wave per resident slot of the device (or fewer for small
-// inputs).  The tiles of all units, unit after unit, are cut into one contiguous range per
-// wave, equal to within one tile, so every wave ends at the same time whatever the shape.
-// A wave whose range holds a whole unit writes that unit's normalised output; a unit
-// shared by several waves gets one partial softmax state (m, l, o) from each, in slot
-// wave + unit (unique: along the ranges the pair (wave, unit) only ever grows), combined
-// by the merge kernel.  The next tile is prefetched across unit boundaries.
+// Work split: the grid holds one wave per resident slot of the device, at least one per unit
+// (see team_size).  Waves resident on one SIMD get unequal shares of its issue slots (older
+// waves first), so tiles are handed out at run time: a unit's team draws them from a
+// per-unit counter that the query-prep kernel zeroes.  A unit served by one wave gets its
+// normalised output from it; otherwise each member writes one partial softmax state
+// (m, l, o) in the slot of its place, and the merge kernel combines them.
 template <int D, int G, int KF>
 __global__ __launch_bounds__(kWave)
 __attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF == KVQ_K_ASYM2)) ? 3 : 2)))
@@ -617,9 +650,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
     const int Tu = p.tiles_per_unit;
-    const long long total = (long long)p.n_units * Tu;
-    const int g0 = wave_first_tile(w, total, p.n_waves);
-    const int g1 = wave_first_tile(w + 1, total, p.n_waves);
+    const int x = team_slot(w, p.n_waves, p.n_cu);       // this wave's place
+    const int u = x % p.n_units;                          // its unit
+    const int team = team_size(u, p.n_units, p.n_waves); // waves serving it
     const int n_q_heads = p.n_kv_heads * G;
     const uint32_t ucap = (uint32_t)p.cap;
 
@@ -636,22 +669,18 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u; // value word offset
     const int q_lo = p.n_sink, q_hi = p.len; // quantized positions [q_lo, q_hi)
 
-    // ---- per-unit query scalars (uniform loads from the unit's record)
-    int u = g0 / Tu;
-    int t = g0 - u * Tu;
+    // ---- the unit's query scalars (uniform loads from its record)
     const uint32_t *__restrict__ rec = qrec + (size_t)u * C::QREC;
-    uint32_t mask = 0;
+    const uint32_t mask = rec[C::OFF_MASK];
     float acc_to_logit[G], logit_to_acc[G];
-    auto load_unit = [&]() {
-        rec = qrec + (size_t)u * C::QREC;
-        mask = rec[C::OFF_MASK];
+    {
         const float *recf = reinterpret_cast<const float *>(rec);
 #pragma unroll
         for (int h = 0; h < G; h++) {
             acc_to_logit[h] = recf[C::OFF_QSC + h];
             logit_to_acc[h] = 1.0f / acc_to_logit[h];
         }
-    };
+    }
 
     // ---- running softmax state of the current unit
     float acc[G][8];
@@ -676,7 +705,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     // ---- end of the current unit's range in this wave: reduce over the wave, then write
     // the normalised output (whole unit here) or this wave's partial state
     auto flush = [&]() {
-        const bool whole = (long long)g0 <= (long long)u * Tu && (long long)(u + 1) * Tu <= (long long)g1;
+        const bool whole = team == 1;
         const int b = u / p.n_kv_heads;
         const int kvh = u % p.n_kv_heads;
         float4 *red = reinterpret_cast<float4 *>(&sm.w[0][0][0]); // 64 lanes x 8 floats
@@ -721,7 +750,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     dst[0] = make_float4(o[0], o[1], o[2], o[3]);
                     dst[1] = make_float4(o[4], o[5], o[6], o[7]);
                 } else {
-                    float *part = p.part + ((size_t)(w + u) * G + h) * (D + 2);
+                    float *part = p.part + ((size_t)x * G + h) * (D + 2);
                     if (lane == 0) {
                         part[0] = mrun[h];
                         part[1] = ls;
@@ -735,26 +764,38 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         }
     };
 
-    // outer loop: the units this wave's range touches; inner loop: their tiles in the range
+    // this wave's tiles: tile `member` first, then those the unit's counter hands out.  The
+    // counter is asked one tile ahead of the answer's use (lane 0's atomic; its return
+    // travels with the tile loads), so the next tile's loads can still go out a whole tile
+    // before its scoring: key-side words and value words of the current tile are in
+    // registers, and value word pair `it` is reloaded with the next tile's right after its
+    // last use.
     KTile<D, G, KF> cur;
     uint2 vcur[VIT];
-    for (int g = g0; g < g1;) {
-        const int t_end = (g1 - g < Tu - t) ? t + (g1 - g) : Tu;
-        load_unit();
-        reset();
-        const Slabs sl = unit_slabs<D, G, KF>(p, u);
-        // key-side words and value words of the current tile; value word pair `it` is
-        // reloaded with the next tile's right after its last use, so each load has a whole
-        // tile of work to arrive
-        load_ktile<D, G, KF>(cur, sl, ucap, lane, t * TILE, mask, 0u, p.ch0);
+    reset();
+    const Slabs sl = unit_slabs<D, G, KF>(p, u);
+    uint32_t *const ctr = p.tile_ctr + u;
+    const bool dynamic = p.dynamic && team > 1;
+    uint32_t ask = 0;
+    if (dynamic && lane == 0)
+        ask = draw_tile(ctr);
+    {
+        const int t = x / p.n_units;
+        const uint32_t off = t < Tu ? 0u : kNoAccess;
+        load_ktile<D, G, KF>(cur, sl, ucap, lane, t * TILE, mask, off, p.ch0);
 #pragma unroll
         for (int it = 0; it < VIT; it++)
-            vcur[it] = bload2(sl.vc, vvo, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
-        for (; t < t_end; t++) {
+            vcur[it] = bload2(sl.vc, vvo + off, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
+    }
+    {
+        for (int t = x / p.n_units; t < Tu;) {
             const int t0 = t * TILE;
             const int tl = t0 + lane * TPL;
-            const int tn = t + 1;
-            const bool more = tn < t_end;
+            const int tn = dynamic ? team + (int)uniform(ask) : t + team; // the tile after this one
+            const bool more = tn < Tu;
+            if (dynamic && more && lane == 0)
+                ask = draw_tile(ctr);
+            set_priority_for(t, Tu);
 
             // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h])
             const bool all_rows = mask == (1u << NP) - 1u;
@@ -937,32 +978,28 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            t = tn;
         }
         flush();
-        g += t_end - (g - u * Tu);
-        u++;
-        t = 0;
     }
 }
 
 // ===================================================================== split merge
 // One thread per (sequence, query head, channel) combines the partial (m, l, o) states of
 // the waves that shared a unit: one global softmax over all positions (Dual-QK sec. 3.4).
-// Units held whole by one wave were written by the decode kernel and are skipped.
+// Units served by one wave were written by the decode kernel and are skipped.
 template <int D, int G, int QREC, int OFF_SINK>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
 {
     const int c = threadIdx.x;
     const int h = blockIdx.x;
     const int u = blockIdx.y;
-    const long long total = (long long)p.n_units * p.tiles_per_unit;
-    const int w_lo = wave_of_tile((long long)u * p.tiles_per_unit, total, p.n_waves);
-    const int w_hi = wave_of_tile((long long)(u + 1) * p.tiles_per_unit - 1, total, p.n_waves);
-    if (w_lo == w_hi)
+    const int n = team_size(u, p.n_units, p.n_waves);
+    if (n == 1)
         return;
-    const float *pb = p.part + ((size_t)(w_lo + u) * G + h) * (D + 2);
-    const size_t stride = (size_t)G * (D + 2);
-    const int n = w_hi - w_lo + 1;
+    // member k of the team has place u + k * n_units, its partial's slot
+    const float *pb = p.part + ((size_t)u * G + h) * (D + 2);
+    const size_t stride = (size_t)p.n_units * G * (D + 2);
     // the sink positions' state from the unit's query record
     const float *sk = reinterpret_cast<const float *>(p.qprep + (size_t)u * QREC) + OFF_SINK + h * (D + 2);
     // one pass, the partials read in batches of 8 with independent loads (one memory
@@ -1081,6 +1118,22 @@ int qrec_g(int group, int kfmt)
 int decode_qrec_words(int head_dim, int group, int kfmt)
 {
     return head_dim == 128 ? qrec_g<128>(group, kfmt) : qrec_g<64>(group, kfmt);
+}
+
+int device_cus()
+{
+    static std::atomic<int> cache{0};
+    int v = cache.load();
+    if (v > 0)
+        return v;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0) {
+        (void)hipGetLastError();
+        v = 256;
+    }
+    cache.store(v);
+    return v;
 }
 
 int decode_slots(int head_dim, int group, int kfmt)

@@ -14,7 +14,7 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 
 // Decode tile: positions scored by one wave per pass (64 lanes x 2 positions).
 constexpr int kTile = 128;
-// Upper bound on decode waves per call (the grid is one wave per resident slot).
+// Upper bound on decode waves per call when units share waves (one wave per resident slot).
 constexpr int kMaxWaves = 16384;
 // Cache capacity granule (public contract: capacity is a multiple of 256 positions).
 constexpr int kCapacityQuantum = 256;
@@ -37,11 +37,14 @@ struct DecodeParams {
     const void *q;
     float *out;
     uint8_t *mask_out;
-    float *part;        // partial softmax states [slot][G][D + 2], slot = wave + unit
+    float *part;        // partial softmax states [wave][G][D + 2]
     uint32_t *qprep;    // per-unit query record written by the query-prep kernel
+    uint32_t *tile_ctr; // per-unit tile counter: zeroed by the query-prep kernel, drawn by decode
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
     float sm_log2e;      // softmax scale times log2(e)
-    int n_units, tiles_per_unit, n_waves; // work split: n_waves equal ranges of n_units * tiles_per_unit tiles
+    int n_units, tiles_per_unit, n_waves; // work split: n_waves >= n_units waves, wave w serves unit w % n_units
+    int dynamic;        // 1: tiles from the unit counters; 0: member k of n takes k, k + n, ...
+    int n_cu;           // compute units of the device (places of waves, see the decode kernel)
 };
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
@@ -54,5 +57,7 @@ hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *out, int bl
 int decode_qrec_words(int head_dim, int group, int kfmt);
 // Resident decode workgroups (one wave each) the device holds for this instantiation.
 int decode_slots(int head_dim, int group, int kfmt);
+// Compute units of the current device (256 when the runtime cannot be asked).
+int device_cus();
 
 } // namespace kvq

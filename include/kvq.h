@@ -137,9 +137,9 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
                             int32_t n_new, void *stream);
 
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (any len up to capacity)
- * and n_q_heads.  The workspace holds the per-unit query records and the partial softmax
- * states of units shared by several decode waves; its contents need no initialisation and
- * are scratch between calls.                                                             */
+ * and n_q_heads.  The workspace holds the per-unit query records, the partial softmax
+ * states of units shared by several decode waves and one tile counter per unit; its
+ * contents need no initialisation and are scratch between calls.                          */
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
 
 /* Decode attention for one query step per sequence over positions [0, len).
@@ -153,14 +153,16 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
  *   out      [batch][n_q_heads][head_dim] fp32, device.
  *   mask_out nullable, [batch * n_kv_heads] bytes, bit p set = group p was read.
  *   ws       workspace of ws_bytes >= kvq_decode_workspace_bytes(c, n_q_heads).
- * len = 0 writes zeros.                                                                   */
+ * len = 0 writes zeros.  By default the waves serving one sequence and KV head take its
+ * 128-position tiles in the order they ask for them, so the fp32 summation order, and the
+ * last bits of out, can differ between calls; kvq_set_deterministic(1) fixes the order.   */
 kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
                            float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* Number of decode waves kvq_decode_attn uses for the current len: the positions of all
- * sequences and KV heads, in 128-position tiles, are cut into this many equal contiguous
- * ranges (one per resident wave slot of the device, or fewer for small inputs).  Host-only
+/* Number of decode waves kvq_decode_attn uses for the current len: one per resident wave
+ * slot of the device, at most one per 128-position tile and at least one per (sequence,
+ * KV head); wave w serves (sequence, KV head) number w mod (batch * n_kv_heads).  Host-only
  * apart from querying the device's occupancy once.                                       */
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads);
 
@@ -173,6 +175,12 @@ kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *threshol
  * 0 = the built-in policy (one wave per resident slot).  Process-wide; affects later
  * decode calls only.                                                                     */
 void kvq_set_split_tiles(int32_t tiles_per_split);
+
+/* 1: every decode wave takes a fixed set of tiles (member k of a team of n waves takes tiles
+ * k, k + n, k + 2n, ...), so kvq_decode_attn gives bit-identical outputs for identical
+ * inputs; 0 (default): tiles go to whichever wave of the team asks first, which balances
+ * waves that get unequal shares of their SIMD.  Process-wide; affects later calls only.    */
+void kvq_set_deterministic(int32_t on);
 
 /* Measurement hook: while both handles are non-NULL (hipEvent_t, created and owned by the
  * caller), every kvq_decode_attn records start_event on its stream immediately before the

@@ -117,26 +117,30 @@ def test_split_invariance_and_determinism(oracle_mod):
     c, oc, q, out0 = _run(oracle_mod, kfmt=0, ch0=1, T=5000, Bsz=1, Hkv=2, G=4)
     qg = q.cuda()
     ref, _ = oc.decode(to_f32_np(q).reshape(2, 4, 128), 1 / np.sqrt(128))
-    outs = []
     try:
-        for tps in (1, 2, 3, 7, 20):
-            B.set_split_tiles(tps)
-            note(f"  split tiles {tps}: {c.splits(8)} splits")
-            o1, _ = c.decode(qg, 1 / np.sqrt(128))
-            o2, _ = c.decode(qg, 1 / np.sqrt(128))
-            torch.cuda.synchronize()
-            assert torch.equal(o1, o2), "run-to-run difference"
-            compare_outputs(o1, ref, f"split tiles {tps}")
-            outs.append(o1)
+        for det in (True, False):
+            B.set_deterministic(det)
+            for tps in (1, 2, 3, 7, 20):
+                B.set_split_tiles(tps)
+                note(f"  deterministic {det}, split tiles {tps}: {c.splits(8)} waves")
+                o1, _ = c.decode(qg, 1 / np.sqrt(128))
+                o2, _ = c.decode(qg, 1 / np.sqrt(128))
+                torch.cuda.synchronize()
+                if det:
+                    assert torch.equal(o1, o2), "run-to-run difference"
+                compare_outputs(o1, ref, f"split tiles {tps}")
+                compare_outputs(o2, ref, f"split tiles {tps}")
     finally:
         B.set_split_tiles(0)
+        B.set_deterministic(False)
 
 
 @pytest.mark.parametrize("kfmt,rot,ch0,keep,G,d", [(0, 0, 0, 0, 2, 128), (2, 1, 0, 3, 4, 128),
                                                    (1, 0, 1, 5, 1, 64), (0, 0, 1, 2, 8, 64)])
-def test_wave_ranges_across_units(oracle_mod, kfmt, rot, ch0, keep, G, d):
-    # 16 short sequences: with few tiles per wave the ranges start and end inside units,
-    # hold several whole units, or share one unit among several waves
+def test_wave_teams_across_units(oracle_mod, kfmt, rot, ch0, keep, G, d):
+    # 16 short sequences (3 tiles each): from one wave per tile (every tile a member's
+    # first) down to one wave per unit; in between, teams of 1-2 waves where the unit's
+    # counter hands out the third tile
     c, oc, q, out0 = _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, keep=keep, ns=4, T=300, Bsz=4,
                           Hkv=4, G=G, dist="t3")
     qg = q.cuda()
@@ -149,6 +153,25 @@ def test_wave_ranges_across_units(oracle_mod, kfmt, rot, ch0, keep, G, d):
             o1, _ = c.decode(qg, sm, keep)
             torch.cuda.synchronize()
             compare_outputs(o1, ref, f"tiles per wave {tps}")
+    finally:
+        B.set_split_tiles(0)
+
+
+def test_teams_drawing_many_tiles(oracle_mod):
+    # 4 sequences of 40 tiles: teams of 2..40 waves draw most tiles from the unit counters
+    # in whatever order the waves ask; every order gives the oracle's output
+    c, oc, q, _ = _run(oracle_mod, kfmt=0, ch0=1, ns=4, T=5000, Bsz=2, Hkv=2, G=4, dist="t3")
+    qg = q.cuda()
+    sm = 1 / np.sqrt(128)
+    ref, _ = oc.decode(to_f32_np(q).reshape(4, 4, 128), sm, 0)
+    try:
+        for tps in (1, 2, 3, 7, 20):
+            B.set_split_tiles(tps)
+            note(f"  tiles per wave {tps}: {c.splits(16)} waves")
+            for _ in range(3):
+                o1, _ = c.decode(qg, sm, 0)
+                torch.cuda.synchronize()
+                compare_outputs(o1, ref, f"tiles per wave {tps}")
     finally:
         B.set_split_tiles(0)
 
