@@ -90,7 +90,6 @@ kvq_status check_buffers(const kvq_cache *c)
 
 struct Plan {
     int tiles_per_unit, n_waves;
-    bool merge; // some unit is served by several waves
 };
 
 // Work split of one decode call.  Every unit's positions [0, len) are cut into 128-position
@@ -119,7 +118,6 @@ Plan plan_splits(const kvq_cache *c, int len, int slots)
     if (W < U)
         W = U; // one wave per unit at least (more units than slots: the dispatcher balances)
     pl.n_waves = (int)W;
-    pl.merge = W > U;
     return pl;
 }
 
@@ -208,7 +206,7 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace: partial softmax states [slots][G][D + 2] fp32, the query records, the tile counters
+// workspace: partial softmax states [slots][G][D + 2] fp32, the query records, two counters per unit
 static size_t part_region_bytes(const kvq_cache *c, int G)
 {
     return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float));
@@ -225,7 +223,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
         return 0;
     const size_t U = units_of(c);
     const size_t G = (size_t)(n_q_heads / c->n_kv_heads);
-    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + round256(U * sizeof(uint32_t));
+    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + round256(2 * U * sizeof(uint32_t));
 }
 
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
@@ -298,7 +296,7 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
     if (!ev[0] || !ev[1])
         ev[0] = ev[1] = nullptr;
-    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, pl.merge, ev, (hipStream_t)stream) != hipSuccess)
+    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, ev, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
     return KVQ_OK;
 }

@@ -9,15 +9,17 @@
 //     query in the keys' rotated coordinates (Walsh-Hadamard, TurboQuant topic list);
 //   * an optional per-GQA-group channel mask from the current queries (Dual-QK sec. 3.2,
 //     C.2): only the kept 16-channel key rows are loaded (channel-major rows, sec. 3.3);
-//   * one softmax over all positions (Dual-QK sec. 3.4), computed online per split and
-//     merged across splits by a small second kernel (no device-wide fences);
+//   * one softmax over all positions (Dual-QK sec. 3.4), computed online by each wave over
+//     its tiles; the waves sharing a unit combine their states at the end (the last one to
+//     finish does it, after an agent-scope release / acquire on a per-unit counter);
 //   * values from INT4 codes: o = sum_t p_t s_{t,g} code_{t,c} + sum_t p_t z_{t,g}.
 //
-// Three kernels per decode call:
-//   qprep   one wave per (sequence, KV head): query in stored coordinates, pruning mask and
-//           the integer / fp16 query operands, written once to a small per-unit record.
-//   decode  one wave per (unit, context split); the host sizes the splits so every SIMD
-//           slot the kernel's register use allows holds a wave.  The query record is read
+// Two kernels per decode call:
+//   qprep   one workgroup per (sequence, KV head), one wave per query head: query in stored
+//           coordinates, pruning mask, the integer / fp16 query operands and the sink
+//           positions' softmax state, written once to a small per-unit record.
+//   decode  one wave per resident SIMD slot (at least one per unit); the waves serving a
+//           unit draw its 128-position tiles from a counter.  The query record is read
 //           with uniform loads, so its operands sit in scalar registers.
 //           * score phase, lane per position: each lane scores 2 consecutive positions; a
 //             key row is one dwordx2 load per lane (512 B contiguous per wave).  Asymmetric
@@ -29,7 +31,8 @@
 //             (heavy-tailed keys make the group zero large).  Lloyd-Max codes go through an
 //             LDS table of fp16 centroid pairs and v_dot2_f32_f16 against fp16 query pairs.
 //           * softmax: a running maximum per head; a wave-wide DPP reduction and a rescale
-//             happen only when a tile holds a logit above it (rare after the first tiles).
+//             happen only when a tile holds a logit well above it (rare after the first
+//             tiles).
 //           * value phase, lane per 8 channels: v_dot2_f32_f16 over position pairs (value
 //             words interleave two positions); a 4-bit code masked into the low mantissa
 //             bits of a half is the subnormal integer code * 2^-24 (or * 2^-20), so no
@@ -37,7 +40,6 @@
 //             group reach the value lanes through LDS, all heads in one 16-byte read.
 //           * the next tile's key-side words are loaded before the value phase of the
 //             current one; cache reads are non-temporal (each byte is read once).
-//   merge   combines the per-split partial softmax states (skipped for one split).
 // No MFMA: this is a bandwidth-bound scan.
 #include <atomic>
 
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     }
     mask = uniform(mask);
     if (threadIdx.x == 0) {
-        p.tile_ctr[unit] = 0u; // the decode kernel's tile counter of this unit
+        p.tile_ctr[unit] = 0u;             // the decode kernel's tile counter of this unit
+        p.tile_ctr[p.n_units + unit] = 0u; // and its count of members done
         rec[C::OFF_MASK] = mask;
         if (p.mask_out)
             p.mask_out[unit] = (uint8_t)mask;
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
 
     // BF16 sink positions (t < min(n_sink, len)): dense dot over the kept channels, then
     // the head's softmax state over them -- log2 max m, sum l and o = sum_t 2^(l_t - m) v_t
-    // -- which the decode and merge kernels fold into the unit's result.  Lanes own
+    // -- which the decode kernel folds into the unit's result.  Lanes own
     // channels; one wave-wide sum per sink gives its logit, lane t keeps that of sink t.
     {
         const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
@@ -627,6 +630,77 @@ __device__ __forceinline__ uint32_t draw_tile(uint32_t *ctr)
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Partial softmax states pass between the waves of a team (on any compute unit) within the
+// kernel.  They are written as agent-scope atomic stores and read back with the same
+// device-coherence cache policy (sc1), so both go to the device-coherent level rather than
+// a compute unit's or XCD's own caches, and the writer counts itself in on the unit's
+// counter only after its stores have completed.  No cache-wide write-back or invalidation
+// is needed.
+constexpr int kCoherent = 16; // sc1
+__device__ __forceinline__ void store_shared(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(rsrc_t r, uint32_t byte_off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherent));
+}
+
+// Combine the partial softmax states (m, l, o) of a unit's team, member k in slot u + k * U,
+// with the sink positions' state: one global softmax over all positions (Dual-QK sec. 3.4),
+// normalised into out_u[h][D].  Run by one wave; lane j holds channels j, j + 64.  Members'
+// m and l are read by one lane each and passed on with readlane.
+template <int D, int G>
+__device__ __forceinline__ void combine_team(const DecodeParams &p, const float *sink, int u, int team, int lane,
+                                          float *out_u)
+{
+    constexpr int CPL = D / 64;
+    constexpr int NB = 8;
+    const uint32_t stride = (uint32_t)p.n_units * G * (D + 2) * 4u; // bytes between members
+    // the team's slots: u + k * U for k < team, all below the number of waves
+    const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * (D + 2) * 4u);
+    for (int h = 0; h < G; h++) {
+        const float *sk = sink + h * (D + 2);
+        float M = sk[0], L = sk[1], O[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            O[s] = sk[2 + lane + 64 * s];
+        const uint32_t hb = (((uint32_t)u * G + h) * (D + 2)) * 4u; // member 0, head h
+        for (int k0 = 0; k0 < team; k0 += NB) {
+            // lane j < NB fetches member k0 + j's (m, l); every lane its channels of each o
+            const bool mine = lane < NB && k0 + lane < team;
+            const uint32_t pm = hb + (uint32_t)(k0 + (mine ? lane : 0)) * stride;
+            const float mlane = mine ? load_shared(r, pm) : -__builtin_inff();
+            const float llane = mine ? load_shared(r, pm + 4u) : 0.0f;
+            float ov[NB][CPL];
+#pragma unroll
+            for (int j = 0; j < NB; j++)
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    ov[j][s] = k0 + j < team ? load_shared(r, hb + (uint32_t)(k0 + j) * stride + (2u + lane + 64u * s) * 4u)
+                                             : 0.0f;
+#pragma unroll
+            for (int j = 0; j < NB; j++) {
+                const float mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlane), j));
+                const float lj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(llane), j));
+                if (mj == -__builtin_inff())
+                    continue;
+                const float Mn = fmaxf(M, mj);
+                const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+                const float fn = __builtin_amdgcn_exp2f(mj - Mn);
+                L = fmaf(L, fo, lj * fn);
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    O[s] = fmaf(O[s], fo, ov[j][s] * fn);
+                M = Mn;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            out_u[h * D + lane + 64 * s] = L > 0.0f ? O[s] / L : 0.0f;
+    }
+}
+
 // Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
 // (twice the key words in flight) and 8 heads get 2.
 //
@@ -635,7 +709,7 @@ __device__ __forceinline__ uint32_t draw_tile(uint32_t *ctr)
 // waves first), so tiles are handed out at run time: a unit's team draws them from a
 // per-unit counter that the query-prep kernel zeroes.  A unit served by one wave gets its
 // normalised output from it; otherwise each member writes one partial softmax state
-// (m, l, o) in the slot of its place, and the merge kernel combines them.
+// (m, l, o) in the slot of its place, and the last member to finish combines them.
 template <int D, int G, int KF>
 __global__ __launch_bounds__(kWave)
 __attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF == KVQ_K_ASYM2)) ? 3 : 2)))
@@ -752,15 +826,28 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 } else {
                     float *part = p.part + ((size_t)x * G + h) * (D + 2);
                     if (lane == 0) {
-                        part[0] = mrun[h];
-                        part[1] = ls;
+                        store_shared(part, mrun[h]);
+                        store_shared(part + 1, ls);
                     }
 #pragma unroll
                     for (int j = 0; j < 8; j++)
-                        part[2 + 8 * lane + j] = o[j];
+                        store_shared(part + 2 + 8 * lane + j, o[j]);
                 }
             }
             __syncthreads();
+        }
+        if (!whole) {
+            // count this member in once its states are stored (all of the wave's memory
+            // operations complete); the member that arrives last combines the team's
+            // states (in member order, so the result does not depend on which member that
+            // is) with the sink positions' state
+            __builtin_amdgcn_s_waitcnt(0);
+            uint32_t arrived = 0;
+            if (lane == 0)
+                arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_units + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((int)uniform(arrived) == team - 1)
+                combine_team<D, G>(p, reinterpret_cast<const float *>(rec) + C::OFF_SINK, u, team, lane,
+                                   p.out + ((size_t)b * n_q_heads + (size_t)kvh * G) * D);
         }
     };
 
@@ -984,60 +1071,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     }
 }
 
-// ===================================================================== split merge
-// One thread per (sequence, query head, channel) combines the partial (m, l, o) states of
-// the waves that shared a unit: one global softmax over all positions (Dual-QK sec. 3.4).
-// Units served by one wave were written by the decode kernel and are skipped.
-template <int D, int G, int QREC, int OFF_SINK>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p)
-{
-    const int c = threadIdx.x;
-    const int h = blockIdx.x;
-    const int u = blockIdx.y;
-    const int n = team_size(u, p.n_units, p.n_waves);
-    if (n == 1)
-        return;
-    // member k of the team has place u + k * n_units, its partial's slot
-    const float *pb = p.part + ((size_t)u * G + h) * (D + 2);
-    const size_t stride = (size_t)p.n_units * G * (D + 2);
-    // the sink positions' state from the unit's query record
-    const float *sk = reinterpret_cast<const float *>(p.qprep + (size_t)u * QREC) + OFF_SINK + h * (D + 2);
-    // one pass, the partials read in batches of 8 with independent loads (one memory
-    // latency per batch): running maximum M, sum L and output O, rescaled as M grows
-    constexpr int NB = 8;
-    float M = sk[0];
-    float L = sk[1], O = sk[2 + c];
-    for (int s0 = 0; s0 < n; s0 += NB) {
-        float mv[NB], lv[NB], ov[NB];
-#pragma unroll
-        for (int j = 0; j < NB; j++) {
-            const bool ok = s0 + j < n;
-            const float *ps = pb + (s0 + j) * stride;
-            mv[j] = ok ? ps[0] : -__builtin_inff();
-            lv[j] = ok ? ps[1] : 0.0f;
-            ov[j] = ok ? ps[2 + c] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < NB; j++) {
-            if (mv[j] == -__builtin_inff())
-                continue;
-            const float Mn = fmaxf(M, mv[j]);
-            const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-            const float fn = __builtin_amdgcn_exp2f(mv[j] - Mn);
-            L = fmaf(L, fo, lv[j] * fn);
-            O = fmaf(O, fo, ov[j] * fn);
-            M = Mn;
-        }
-    }
-    const int b = u / p.n_kv_heads;
-    const int kvh = u % p.n_kv_heads;
-    const size_t oi = ((size_t)b * p.n_kv_heads * G + (size_t)kvh * G + h) * D + c;
-    p.out[oi] = L > 0.0f ? O / L : 0.0f;
-}
-
 // ===================================================================== launchers
 template <int D, int G, int KF>
-hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2], hipStream_t s)
+hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
     hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
@@ -1050,33 +1086,28 @@ hipError_t launch_one(int units, const DecodeParams &p, bool merge, hipEvent_t c
     e = hipGetLastError();
     if (e == hipSuccess && ev[1])
         e = hipEventRecord(ev[1], s);
-    if (e != hipSuccess || !merge)
-        return e;
-    using C = Cfg<D, G, KF>;
-    hipLaunchKernelGGL((merge_kernel<D, G, C::QREC, C::OFF_SINK>), dim3((unsigned)G, (unsigned)units), dim3(D), 0, s,
-                       p);
-    return hipGetLastError();
+    return e;
 }
 
 template <int D, int G>
-hipError_t launch_kf(int kfmt, int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2], hipStream_t s)
+hipError_t launch_kf(int kfmt, int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
     switch (kfmt) {
-    case KVQ_K_ASYM2: return launch_one<D, G, KVQ_K_ASYM2>(units, p, merge, ev, s);
-    case KVQ_K_ASYM4: return launch_one<D, G, KVQ_K_ASYM4>(units, p, merge, ev, s);
-    default: return launch_one<D, G, KVQ_K_LLOYD4>(units, p, merge, ev, s);
+    case KVQ_K_ASYM2: return launch_one<D, G, KVQ_K_ASYM2>(units, p, ev, s);
+    case KVQ_K_ASYM4: return launch_one<D, G, KVQ_K_ASYM4>(units, p, ev, s);
+    default: return launch_one<D, G, KVQ_K_LLOYD4>(units, p, ev, s);
     }
 }
 
 template <int D>
-hipError_t launch_g(int group, int kfmt, int units, const DecodeParams &p, bool merge, hipEvent_t const ev[2],
+hipError_t launch_g(int group, int kfmt, int units, const DecodeParams &p, hipEvent_t const ev[2],
                     hipStream_t s)
 {
     switch (group) {
-    case 1: return launch_kf<D, 1>(kfmt, units, p, merge, ev, s);
-    case 2: return launch_kf<D, 2>(kfmt, units, p, merge, ev, s);
-    case 4: return launch_kf<D, 4>(kfmt, units, p, merge, ev, s);
-    default: return launch_kf<D, 8>(kfmt, units, p, merge, ev, s);
+    case 1: return launch_kf<D, 1>(kfmt, units, p, ev, s);
+    case 2: return launch_kf<D, 2>(kfmt, units, p, ev, s);
+    case 4: return launch_kf<D, 4>(kfmt, units, p, ev, s);
+    default: return launch_kf<D, 8>(kfmt, units, p, ev, s);
     }
 }
 
@@ -1162,12 +1193,12 @@ int decode_slots(int head_dim, int group, int kfmt)
     return v;
 }
 
-hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, bool merge,
-                         hipEvent_t const ev[2], hipStream_t s)
+hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, hipEvent_t const ev[2],
+                         hipStream_t s)
 {
     if (head_dim == 128)
-        return launch_g<128>(group, kfmt, units, p, merge, ev, s);
-    return launch_g<64>(group, kfmt, units, p, merge, ev, s);
+        return launch_g<128>(group, kfmt, units, p, ev, s);
+    return launch_g<64>(group, kfmt, units, p, ev, s);
 }
 
 } // namespace kvq

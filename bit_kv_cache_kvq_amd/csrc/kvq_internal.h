@@ -39,7 +39,7 @@ struct DecodeParams {
     uint8_t *mask_out;
     float *part;        // partial softmax states [wave][G][D + 2]
     uint32_t *qprep;    // per-unit query record written by the query-prep kernel
-    uint32_t *tile_ctr; // per-unit tile counter: zeroed by the query-prep kernel, drawn by decode
+    uint32_t *tile_ctr; // [2][units]: tiles drawn, members done; zeroed by the query-prep kernel
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
     float sm_log2e;      // softmax scale times log2(e)
     int n_units, tiles_per_unit, n_waves; // work split: n_waves >= n_units waves, wave w serves unit w % n_units
@@ -49,8 +49,8 @@ struct DecodeParams {
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
 // ev[0], ev[1]: optional events recorded around the decode kernel (both non-null or unused)
-hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, bool merge,
-                         hipEvent_t const ev[2], hipStream_t s);
+hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, hipEvent_t const ev[2],
+                         hipStream_t s);
 // Streaming-read probe over `bytes` (a multiple of 16) at p; out holds `blocks` words.
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *out, int blocks, hipStream_t s);
 // u32 words of one unit's query record (query-prep output read by the decode kernel).

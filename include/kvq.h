@@ -185,7 +185,7 @@ void kvq_set_deterministic(int32_t on);
 /* Measurement hook: while both handles are non-NULL (hipEvent_t, created and owned by the
  * caller), every kvq_decode_attn records start_event on its stream immediately before the
  * main decode kernel and stop_event immediately after it, so hipEventElapsedTime gives that
- * kernel's duration alone (the query-prep and merge kernels fall outside).  NULL, NULL
+ * kernel's duration alone (the query-prep kernel falls outside).  NULL, NULL
  * turns it off.  Process-wide; meant for benchmarks, not for concurrent callers.          */
 void kvq_set_decode_events(void *start_event, void *stop_event);
 
