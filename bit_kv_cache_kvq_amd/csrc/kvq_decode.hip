@@ -192,6 +192,26 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     uint32_t *rec = p.qprep + (size_t)unit * C::QREC;
     float *recf = reinterpret_cast<float *>(rec);
 
+    // BF16 sink rows, SB at a time (the last row repeated past n_sink); the first batch of
+    // keys and values is loaded here, with the query, so its latency overlaps the query's
+    const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
+    constexpr int SB = 8; // sinks per batch of loads
+    auto load_sinks = [&](const uint16_t *base, int t0, float (&dst)[SB][CPL]) {
+#pragma unroll
+        for (int j = 0; j < SB; j++) {
+            const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
+            const uint16_t *row = base + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                dst[j][s] = bf16_to_f32(row[s]);
+        }
+    };
+    float kv[SB][CPL], vv[SB][CPL];
+    if (n_sink > 0) {
+        load_sinks(p.sink_k, 0, kv);
+        load_sinks(p.sink_v, 0, vv);
+    }
+
     {
         const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
         float y[CPL];
@@ -284,19 +304,10 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     // -- which the decode kernel folds into the unit's result.  Lanes own
     // channels; one wave-wide sum per sink gives its logit, lane t keeps that of sink t.
     {
-        const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
         float mine = -__builtin_inff();
-        constexpr int SB = 8; // sinks per batch of loads
         for (int t0 = 0; t0 < n_sink; t0 += SB) {
-            float kv[SB][CPL];
-#pragma unroll
-            for (int j = 0; j < SB; j++) {
-                const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
-                const uint16_t *sk = p.sink_k + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    kv[j][s] = bf16_to_f32(sk[s]);
-            }
+            if (t0 > 0)
+                load_sinks(p.sink_k, t0, kv);
 #pragma unroll
             for (int j = 0; j < SB; j++) {
                 if (t0 + j >= n_sink)
@@ -323,15 +334,8 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         for (int s = 0; s < CPL; s++)
             o[s] = 0.0f;
         for (int t0 = 0; t0 < n_sink; t0 += SB) {
-            float vv[SB][CPL];
-#pragma unroll
-            for (int j = 0; j < SB; j++) {
-                const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
-                const uint16_t *sv = p.sink_v + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    vv[j][s] = bf16_to_f32(sv[s]);
-            }
+            if (t0 > 0)
+                load_sinks(p.sink_v, t0, vv);
 #pragma unroll
             for (int j = 0; j < SB; j++) {
                 if (t0 + j >= n_sink)
