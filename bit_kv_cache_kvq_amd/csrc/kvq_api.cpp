@@ -206,10 +206,11 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace: partial softmax states [slots][G][D + 2] fp32, the query records, two counters per unit
+// workspace: partial softmax states [slots][G][D + 4] fp32 (m, l, 2 unused, o), the query records,
+// two counters per unit
 static size_t part_region_bytes(const kvq_cache *c, int G)
 {
-    return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 2) * sizeof(float));
+    return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 4) * sizeof(float));
 }
 
 static size_t qrec_region_bytes(const kvq_cache *c, int G)

@@ -635,20 +635,30 @@ __device__ __forceinline__ uint32_t draw_tile(uint32_t *ctr)
 }
 
 // Partial softmax states pass between the waves of a team (on any compute unit) within the
-// kernel.  They are written as agent-scope atomic stores and read back with the same
-// device-coherence cache policy (sc1), so both go to the device-coherent level rather than
-// a compute unit's or XCD's own caches, and the writer counts itself in on the unit's
-// counter only after its stores have completed.  No cache-wide write-back or invalidation
-// is needed.
+// kernel.  They are written and read back with the device-coherence cache policy (sc1, as
+// the compiler gives agent-scope atomic accesses), so both go to the device-coherent level
+// rather than a compute unit's or XCD's own caches, and the writer counts itself in on the
+// unit's counter only after its stores have completed.  No cache-wide write-back or
+// invalidation is needed.  Stores are 16 bytes per lane, whole lines per wave.
 constexpr int kCoherent = 16; // sc1
-__device__ __forceinline__ void store_shared(float *p, float v)
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_shared2(rsrc_t r, uint32_t byte_off, float a, float b)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const u2v v = {__float_as_uint(a), __float_as_uint(b)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_shared4(rsrc_t r, uint32_t byte_off, float a, float b, float c, float d)
+{
+    const u4v v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kCoherent);
 }
 __device__ __forceinline__ float load_shared(rsrc_t r, uint32_t byte_off)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherent));
 }
+// Partial state record of one (wave, head): m, l, two unused words, o[D] (16-byte aligned).
+template <int D>
+constexpr int part_rec() { return D + 4; }
 
 // Combine the partial softmax states (m, l, o) of a unit's team, member k in slot u + k * U,
 // with the sink positions' state: one global softmax over all positions (Dual-QK sec. 3.4),
@@ -660,16 +670,17 @@ __device__ __forceinline__ void combine_team(const DecodeParams &p, const float 
 {
     constexpr int CPL = D / 64;
     constexpr int NB = 8;
-    const uint32_t stride = (uint32_t)p.n_units * G * (D + 2) * 4u; // bytes between members
+    constexpr int PR = part_rec<D>();
+    const uint32_t stride = (uint32_t)p.n_units * G * PR * 4u; // bytes between members
     // the team's slots: u + k * U for k < team, all below the number of waves
-    const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * (D + 2) * 4u);
+    const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
     for (int h = 0; h < G; h++) {
         const float *sk = sink + h * (D + 2);
         float M = sk[0], L = sk[1], O[CPL];
 #pragma unroll
         for (int s = 0; s < CPL; s++)
             O[s] = sk[2 + lane + 64 * s];
-        const uint32_t hb = (((uint32_t)u * G + h) * (D + 2)) * 4u; // member 0, head h
+        const uint32_t hb = (((uint32_t)u * G + h) * PR) * 4u; // member 0, head h
         for (int k0 = 0; k0 < team; k0 += NB) {
             // lane j < NB fetches member k0 + j's (m, l); every lane its channels of each o
             const bool mine = lane < NB && k0 + lane < team;
@@ -681,7 +692,7 @@ __device__ __forceinline__ void combine_team(const DecodeParams &p, const float 
             for (int j = 0; j < NB; j++)
 #pragma unroll
                 for (int s = 0; s < CPL; s++)
-                    ov[j][s] = k0 + j < team ? load_shared(r, hb + (uint32_t)(k0 + j) * stride + (2u + lane + 64u * s) * 4u)
+                    ov[j][s] = k0 + j < team ? load_shared(r, hb + (uint32_t)(k0 + j) * stride + (4u + lane + 64u * s) * 4u)
                                              : 0.0f;
 #pragma unroll
             for (int j = 0; j < NB; j++) {
@@ -828,14 +839,12 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     dst[0] = make_float4(o[0], o[1], o[2], o[3]);
                     dst[1] = make_float4(o[4], o[5], o[6], o[7]);
                 } else {
-                    float *part = p.part + ((size_t)x * G + h) * (D + 2);
-                    if (lane == 0) {
-                        store_shared(part, mrun[h]);
-                        store_shared(part + 1, ls);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; j++)
-                        store_shared(part + 2 + 8 * lane + j, o[j]);
+                    const rsrc_t pr = make_rsrc(p.part, (uint32_t)p.n_waves * G * part_rec<D>() * 4u);
+                    const uint32_t rb = ((uint32_t)x * G + h) * part_rec<D>() * 4u;
+                    if (lane == 0)
+                        store_shared2(pr, rb, mrun[h], ls);
+                    store_shared4(pr, rb + (4u + 8u * lane) * 4u, o[0], o[1], o[2], o[3]);
+                    store_shared4(pr, rb + (8u + 8u * lane) * 4u, o[4], o[5], o[6], o[7]);
                 }
             }
             __syncthreads();

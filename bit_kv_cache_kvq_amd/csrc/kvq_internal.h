@@ -37,7 +37,7 @@ struct DecodeParams {
     const void *q;
     float *out;
     uint8_t *mask_out;
-    float *part;        // partial softmax states [wave][G][D + 2]
+    float *part;        // partial softmax states [wave][G][D + 4]: m, l, unused x2, o[D]
     uint32_t *qprep;    // per-unit query record written by the query-prep kernel
     uint32_t *tile_ctr; // [2][units]: tiles drawn, members done; zeroed by the query-prep kernel
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
