@@ -140,6 +140,11 @@ __device__ __forceinline__ void fwht_wave(float (&y)[CPL], int lane)
     }
 }
 
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 // Cache reads are raw buffer loads: one descriptor per (unit, array) holds the unit's slab
 // (base, byte size below 2^30), the lane part of the offset is a VGPR and the position part
 // an SGPR, so no 64-bit address arithmetic runs on the VALU.  An access whose lane offset
@@ -455,25 +460,26 @@ struct Slabs {
     rsrc_t kc, ksz, kx, vsz, vc;
 };
 
-// off: 0, or kNoAccess to turn every load into a zero without a memory access
-template <int D, int G, int KF>
+// off: 0, or kNoAccess to turn every load into a zero without a memory access.  ALL: every
+// row is kept; otherwise the rows of pruned groups get kNoAccess too (zeros, no traffic, and
+// no branch).  CH0: channel 0 is stored apart in BF16.
+template <int D, int G, int KF, bool ALL, bool CH0>
 __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, uint32_t cap, int lane, int t0,
-                                           uint32_t mask, uint32_t off, int ch0)
+                                           uint32_t mask, uint32_t off)
 {
     using C = Cfg<D, G, KF>;
     const uint32_t vo = (uint32_t)lane * C::TPL * 4u + off;  // lane's 2 positions of a u32 row
+    auto gate = [&](uint32_t bits) { return (ALL || (mask & bits)) ? vo : (vo | kNoAccess); };
 #pragma unroll
     for (int r = 0; r < C::KROWS; r++)
-        if (mask >> (r / C::RPP) & 1u)
-            k.kc[r] = bload2(sl.kc, vo, ((uint32_t)r * cap + (uint32_t)t0) * 4u);
+        k.kc[r] = bload2(sl.kc, gate(1u << (r / C::RPP)), ((uint32_t)r * cap + (uint32_t)t0) * 4u);
     if constexpr (KF != KVQ_K_LLOYD4) {
 #pragma unroll
         for (int g = 0; g < C::NG; g++)
-            if (mask >> (2 * g) & 3u)
-                k.ksz[g] = bload2(sl.ksz, vo, ((uint32_t)g * cap + (uint32_t)t0) * 4u);
+            k.ksz[g] = bload2(sl.ksz, gate(3u << (2 * g)), ((uint32_t)g * cap + (uint32_t)t0) * 4u);
         k.kx = 0;
-        if (ch0 && (mask & 1u))
-            k.kx = bload1(sl.kx, vo >> 1, (uint32_t)t0 * 2u); // u16 row: half the u32 offset
+        if constexpr (CH0)
+            k.kx = bload1(sl.kx, ((ALL || (mask & 1u)) ? (vo >> 1) : ((vo >> 1) | kNoAccess)), (uint32_t)t0 * 2u); // u16 row
     } else {
         k.kx = bload1(sl.kx, vo >> 1, (uint32_t)t0 * 2u);
     }
@@ -488,9 +494,9 @@ __device__ __forceinline__ void load_ktile(KTile<D, G, KF> &k, const Slabs &sl, 
 // Per (group, head, position) one int32 sum collects the hi-plane products, is shifted
 // by 8, then collects the lo-plane products: sum = 256 * hi.code + lo.code = q_int.code.
 // The query operands are uniform loads from the unit's record.
-template <int D, int G, int KF, bool ALL>
+template <int D, int G, int KF, bool ALL, bool CH0>
 __device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const uint32_t *__restrict__ rec,
-                                           uint32_t mask, int ch0, float (&lg)[Cfg<D, G, KF>::TPL][G])
+                                           uint32_t mask, float (&lg)[Cfg<D, G, KF>::TPL][G])
 {
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, NG = C::NG, TPL = C::TPL, NREG = C::NREG, QW = C::QW;
@@ -556,7 +562,7 @@ __device__ __forceinline__ void score_asym(const KTile<D, G, KF> &cur, const uin
             }
         }
     }
-    if (ch0 && (mask & 1u)) {
+    if (CH0 && (ALL || (mask & 1u))) {
 #pragma unroll
         for (int i = 0; i < TPL; i++) {
             const float k0 = bf16_to_f32(i == 0 ? (cur.kx & 0xFFFFu) : (cur.kx >> 16));
@@ -879,15 +885,19 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     uint32_t ask = 0;
     if (dynamic && lane == 0)
         ask = draw_tile(ctr);
-    {
-        const int t = x / p.n_units;
-        const uint32_t off = t < Tu ? 0u : kNoAccess;
-        load_ktile<D, G, KF>(cur, sl, ucap, lane, t * TILE, mask, off, p.ch0);
+    // the tile loop, compiled for every-row-kept or not (ALL) and channel 0 apart or not
+    // (CH0), so that neither costs a branch per tile
+    auto tiles = [&](auto all_c, auto ch0_c) {
+        constexpr bool ALL = decltype(all_c)::value;
+        constexpr bool CH0 = decltype(ch0_c)::value;
+        {
+            const int t = x / p.n_units;
+            const uint32_t off = t < Tu ? 0u : kNoAccess;
+            load_ktile<D, G, KF, ALL, CH0>(cur, sl, ucap, lane, t * TILE, mask, off);
 #pragma unroll
-        for (int it = 0; it < VIT; it++)
-            vcur[it] = bload2(sl.vc, vvo + off, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
-    }
-    {
+            for (int it = 0; it < VIT; it++)
+                vcur[it] = bload2(sl.vc, vvo + off, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
+        }
         for (int t = x / p.n_units; t < Tu;) {
             const int t0 = t * TILE;
             const int tl = t0 + lane * TPL;
@@ -897,8 +907,11 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 ask = draw_tile(ctr);
             set_priority_for(t, Tu);
 
-            // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h])
-            const bool all_rows = mask == (1u << NP) - 1u;
+            // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h]).  The query
+            // operands are read through an address that depends on the tile number (the
+            // added term is always 0: t >= 0), so they are reloaded per tile from the scalar
+            // cache rather than hoisted out of the loop into more scalar registers than exist.
+            const uint32_t *__restrict__ rq = rec + ((uint32_t)t >> 31);
             float lg[TPL][G];
 #pragma unroll
             for (int i = 0; i < TPL; i++)
@@ -906,14 +919,11 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 for (int h = 0; h < G; h++)
                     lg[i][h] = 0.0f;
             if constexpr (KF != KVQ_K_LLOYD4) {
-                if (all_rows)
-                    score_asym<D, G, KF, true>(cur, rec, mask, p.ch0, lg);
-                else
-                    score_asym<D, G, KF, false>(cur, rec, mask, p.ch0, lg);
+                score_asym<D, G, KF, ALL, CH0>(cur, rq, mask, lg);
             } else {
 #pragma unroll
                 for (int r = 0; r < KROWS; r++) {
-                    if (!(mask >> (r / C::RPP) & 1u))
+                    if (!ALL && !(mask >> (r / C::RPP) & 1u))
                         continue;
                     uint32_t pr[TPL][4];
 #pragma unroll
@@ -927,7 +937,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     for (int h = 0; h < G; h++)
 #pragma unroll
                         for (int j = 0; j < 4; j++) {
-                            const uint32_t qv = rec[C::OFF_QP + (r * G + h) * C::QW + j];
+                            const uint32_t qv = rq[C::OFF_QP + (r * G + h) * C::QW + j];
 #pragma unroll
                             for (int i = 0; i < TPL; i++)
                                 lg[i][h] = dot2(pr[i][j], qv, lg[i][h]);
@@ -971,7 +981,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             // the loads access nothing: the next unit's first tile is loaded after the flush,
             // outside the inner loop and its register peak.
             const uint32_t noff = more ? 0u : kNoAccess;
-            load_ktile<D, G, KF>(cur, sl, ucap, lane, tn * TILE, mask, noff, p.ch0);
+            load_ktile<D, G, KF, ALL, CH0>(cur, sl, ucap, lane, tn * TILE, mask, noff);
 
             // ---- online softmax (log2 units), per head.  The running maximum m is raised
             // (wave-wide DPP max, rescale of that head's state) only when a logit exceeds
@@ -1080,8 +1090,19 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             t = tn;
         }
-        flush();
+    };
+    if (mask == (1u << NP) - 1u) {
+        if (KF != KVQ_K_LLOYD4 && p.ch0)
+            tiles(BoolC<true>(), BoolC<KF != KVQ_K_LLOYD4>());
+        else
+            tiles(BoolC<true>(), BoolC<false>());
+    } else {
+        if (KF != KVQ_K_LLOYD4 && p.ch0)
+            tiles(BoolC<false>(), BoolC<KF != KVQ_K_LLOYD4>());
+        else
+            tiles(BoolC<false>(), BoolC<false>());
     }
+    flush();
 }
 
 // ===================================================================== launchers
