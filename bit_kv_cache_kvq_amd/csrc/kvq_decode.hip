@@ -977,9 +977,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             }
 
             // ---- next tile's key-side words, into the registers this tile no longer needs:
-            // in flight during the rest of this tile.  After the last tile of the unit's range
-            // the loads access nothing: the next unit's first tile is loaded after the flush,
-            // outside the inner loop and its register peak.
+            // in flight during the rest of this tile.  After the wave's last tile the loads
+            // access nothing.
             const uint32_t noff = more ? 0u : kNoAccess;
             load_ktile<D, G, KF, ALL, CH0>(cur, sl, ucap, lane, tn * TILE, mask, noff);
 
@@ -989,13 +988,24 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             // fp16 weight p*s finite (s < 2^14 for inputs below 65504) and makes the raise
             // rare after the first tile.  The test runs in accumulator units against
             // mthr = (m + kSlack) / acc_to_logit; a rounding miss is harmless.
+            // One branch per tile covers all heads: one per head splits the tile's code into
+            // blocks the compiler cannot schedule across, which costs far more than the
+            // raises themselves (about one per two tiles over all heads).
+            uint64_t above[G];
+            uint64_t any_above = 0;
 #pragma unroll
             for (int h = 0; h < G; h++) {
-                uint64_t above = 0;
+                above[h] = 0;
 #pragma unroll
                 for (int i = 0; i < TPL; i++)
-                    above |= __ballot(lg[i][h] > mthr[h]);
-                if (above) {
+                    above[h] |= __ballot(lg[i][h] > mthr[h]);
+                any_above |= above[h];
+            }
+            if (any_above) {
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    if (!above[h])
+                        continue;
                     float mt = lg[0][h];
 #pragma unroll
                     for (int i = 1; i < TPL; i++)
