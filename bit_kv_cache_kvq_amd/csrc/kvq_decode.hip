@@ -284,9 +284,12 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         }
     }
     mask = uniform(mask);
+    // the decode kernel's tile counters of this unit's stripes, at the places u + k * units
+    for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
+        if (unit + k * p.n_units < p.n_waves)
+            p.tile_ctr[unit + k * p.n_units] = 0u;
     if (threadIdx.x == 0) {
-        p.tile_ctr[unit] = 0u;             // the decode kernel's tile counter of this unit
-        p.tile_ctr[p.n_units + unit] = 0u; // and its count of members done
+        p.tile_ctr[p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
         rec[C::OFF_MASK] = mask;
         if (p.mask_out)
             p.mask_out[unit] = (uint8_t)mask;
@@ -599,12 +602,17 @@ __device__ __forceinline__ Slabs unit_slabs(const DecodeParams &p, int u)
 // W / U members, one more for the first W mod U units.  Member k scores tile k first; every
 // further tile comes from the unit's counter (tiles team_size, team_size + 1, ... in the
 // order the members ask), so a member that gets more issue slots takes more tiles and the
-// whole team ends together.  In the deterministic mode member k takes tiles k, k + n, ...
-// of a team of n instead.
+// whole team ends together.  Teams of more than kStripe members work the same way on
+// stripes of the unit (see the decode kernel).  In the deterministic mode member k takes
+// tiles k, k + n, ... of a team (stripe) of n instead.
 __device__ __forceinline__ int team_size(int u, int U, int W) { return W / U + (u < W % U ? 1 : 0); }
 
+// Most waves drawing from one counter: draws on one address are serialized where the atomic
+// executes, so a large team (few units, long contexts) is cut into stripes of this many.
+constexpr int kStripe = 8;
+
 // Issue priority from a team's progress: the tile a wave is on (tiles are taken in
-// increasing order, so it tracks how far the whole team is), in the bands [0, 1/2),
+// increasing order, so it tracks how far the whole team or stripe is), in the bands [0, 1/2),
 // [1/2, 3/4), [3/4, 7/8), [7/8, 1) of the unit.  The waves sharing a SIMD otherwise issue
 // oldest first, which lets whole teams fall behind others; a team in an earlier band now
 // goes first, so teams advance together, and the narrow last band bounds how far apart
@@ -668,58 +676,91 @@ constexpr int part_rec() { return D + 4; }
 
 // Combine the partial softmax states (m, l, o) of a unit's team, member k in slot u + k * U,
 // with the sink positions' state: one global softmax over all positions (Dual-QK sec. 3.4),
-// normalised into out_u[h][D].  Run by one wave; lane j holds channels j, j + 64.  Members'
-// m and l are read by one lane each and passed on with readlane.
+// normalised into out_u[h][D].  Run by one wave; lane j holds channels j, j + 64 of every
+// head.  Members go in batches of NB, all heads at once (32 o loads per lane per batch),
+// and the next batch's loads are issued before the current batch is folded in, so a team
+// of n members costs about one memory latency plus n / NB load rounds.  Lane j < G * NB
+// reads (m, l) of head j / NB, member j % NB of the batch; readlane passes them on.
+template <int D, int G>
+struct CombineBatch {
+    static constexpr int CPL = D / 64;
+    static constexpr int NB = 32 / (G * CPL);
+    float m, l;
+    float o[G][NB][CPL];
+};
+
+template <int D, int G>
+__device__ __forceinline__ void load_batch(CombineBatch<D, G> &b, rsrc_t r, uint32_t ub, uint32_t stride, int k0,
+                                           int team, int lane)
+{
+    using CB = CombineBatch<D, G>;
+    constexpr int CPL = CB::CPL, NB = CB::NB, PR = part_rec<D>();
+    const int jm = lane % NB, hm = lane / NB;
+    const bool mine = hm < G && k0 + jm < team;
+    const uint32_t pm = ub + (uint32_t)(k0 + (mine ? jm : 0)) * stride + (uint32_t)(mine ? hm : 0) * PR * 4u;
+    b.m = mine ? load_shared(r, pm) : -__builtin_inff();
+    b.l = mine ? load_shared(r, pm + 4u) : 0.0f;
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                b.o[h][j][s] = k0 + j < team ? load_shared(r, ub + (uint32_t)(k0 + j) * stride +
+                                                                  ((uint32_t)h * PR + 4u + lane + 64u * s) * 4u)
+                                             : 0.0f;
+}
+
 template <int D, int G>
 __device__ __forceinline__ void combine_team(const DecodeParams &p, const float *sink, int u, int team, int lane,
                                           float *out_u)
 {
-    constexpr int CPL = D / 64;
-    constexpr int NB = 8;
-    constexpr int PR = part_rec<D>();
+    using CB = CombineBatch<D, G>;
+    constexpr int CPL = CB::CPL, NB = CB::NB, PR = part_rec<D>();
     const uint32_t stride = (uint32_t)p.n_units * G * PR * 4u; // bytes between members
     // the team's slots: u + k * U for k < team, all below the number of waves
     const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
+    const uint32_t ub = (uint32_t)u * G * PR * 4u; // member 0, head 0
+    float M[G], L[G], O[G][CPL];
+#pragma unroll
     for (int h = 0; h < G; h++) {
         const float *sk = sink + h * (D + 2);
-        float M = sk[0], L = sk[1], O[CPL];
+        M[h] = sk[0];
+        L[h] = sk[1];
 #pragma unroll
         for (int s = 0; s < CPL; s++)
-            O[s] = sk[2 + lane + 64 * s];
-        const uint32_t hb = (((uint32_t)u * G + h) * PR) * 4u; // member 0, head h
-        for (int k0 = 0; k0 < team; k0 += NB) {
-            // lane j < NB fetches member k0 + j's (m, l); every lane its channels of each o
-            const bool mine = lane < NB && k0 + lane < team;
-            const uint32_t pm = hb + (uint32_t)(k0 + (mine ? lane : 0)) * stride;
-            const float mlane = mine ? load_shared(r, pm) : -__builtin_inff();
-            const float llane = mine ? load_shared(r, pm + 4u) : 0.0f;
-            float ov[NB][CPL];
+            O[h][s] = sk[2 + lane + 64 * s];
+    }
+    CB cur, nxt;
+    load_batch<D, G>(cur, r, ub, stride, 0, team, lane);
+    for (int k0 = 0; k0 < team; k0 += NB) {
+        if (k0 + NB < team)
+            load_batch<D, G>(nxt, r, ub, stride, k0 + NB, team, lane);
 #pragma unroll
-            for (int j = 0; j < NB; j++)
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    ov[j][s] = k0 + j < team ? load_shared(r, hb + (uint32_t)(k0 + j) * stride + (4u + lane + 64u * s) * 4u)
-                                             : 0.0f;
+        for (int h = 0; h < G; h++) {
 #pragma unroll
             for (int j = 0; j < NB; j++) {
-                const float mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlane), j));
-                const float lj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(llane), j));
+                const float mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.m), h * NB + j));
+                const float lj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cur.l), h * NB + j));
                 if (mj == -__builtin_inff())
                     continue;
-                const float Mn = fmaxf(M, mj);
-                const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+                const float Mn = fmaxf(M[h], mj);
+                const float fo = M[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M[h] - Mn);
                 const float fn = __builtin_amdgcn_exp2f(mj - Mn);
-                L = fmaf(L, fo, lj * fn);
+                L[h] = fmaf(L[h], fo, lj * fn);
 #pragma unroll
                 for (int s = 0; s < CPL; s++)
-                    O[s] = fmaf(O[s], fo, ov[j][s] * fn);
-                M = Mn;
+                    O[h][s] = fmaf(O[h][s], fo, cur.o[h][j][s] * fn);
+                M[h] = Mn;
             }
         }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++)
 #pragma unroll
         for (int s = 0; s < CPL; s++)
-            out_u[h * D + lane + 64 * s] = L > 0.0f ? O[s] / L : 0.0f;
-    }
+            out_u[h * D + lane + 64 * s] = L[h] > 0.0f ? O[h][s] / L[h] : 0.0f;
 }
 
 // Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
@@ -863,7 +904,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             __builtin_amdgcn_s_waitcnt(0);
             uint32_t arrived = 0;
             if (lane == 0)
-                arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_units + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_waves + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((int)uniform(arrived) == team - 1)
                 combine_team<D, G>(p, reinterpret_cast<const float *>(rec) + C::OFF_SINK, u, team, lane,
                                    p.out + ((size_t)b * n_q_heads + (size_t)kvh * G) * D);
@@ -880,8 +921,18 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     uint2 vcur[VIT];
     reset();
     const Slabs sl = unit_slabs<D, G, KF>(p, u);
-    uint32_t *const ctr = p.tile_ctr + u;
-    const bool dynamic = p.dynamic && team > 1;
+    // stripes: a team of more than kStripe waves splits the unit's tiles into S contiguous
+    // stripes, stripe s served by members s, s + S, ... with a counter of its own (at the
+    // place of member s), so no counter takes more than kStripe waves' draws
+    const int member = x / p.n_units;
+    const int S = (team + kStripe - 1) / kStripe;
+    const int stripe = member % S;
+    const int smem = member / S;                        // index within the stripe
+    const int nst = (team - stripe + S - 1) / S;        // members of the stripe
+    const int ts0 = (int)((long long)stripe * Tu / S);  // its tiles [ts0, ts1)
+    const int ts1 = (int)((long long)(stripe + 1) * Tu / S);
+    uint32_t *const ctr = p.tile_ctr + (u + stripe * p.n_units);
+    const bool dynamic = p.dynamic && nst > 1;
     uint32_t ask = 0;
     if (dynamic && lane == 0)
         ask = draw_tile(ctr);
@@ -891,21 +942,21 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         constexpr bool ALL = decltype(all_c)::value;
         constexpr bool CH0 = decltype(ch0_c)::value;
         {
-            const int t = x / p.n_units;
-            const uint32_t off = t < Tu ? 0u : kNoAccess;
+            const int t = ts0 + smem;
+            const uint32_t off = t < ts1 ? 0u : kNoAccess;
             load_ktile<D, G, KF, ALL, CH0>(cur, sl, ucap, lane, t * TILE, mask, off);
 #pragma unroll
             for (int it = 0; it < VIT; it++)
                 vcur[it] = bload2(sl.vc, vvo + off, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
         }
-        for (int t = x / p.n_units; t < Tu;) {
+        for (int t = ts0 + smem; t < ts1;) {
             const int t0 = t * TILE;
             const int tl = t0 + lane * TPL;
-            const int tn = dynamic ? team + (int)uniform(ask) : t + team; // the tile after this one
-            const bool more = tn < Tu;
+            const int tn = dynamic ? ts0 + nst + (int)uniform(ask) : t + nst; // the tile after this one
+            const bool more = tn < ts1;
             if (dynamic && more && lane == 0)
                 ask = draw_tile(ctr);
-            set_priority_for(t, Tu);
+            set_priority_for(t - ts0, ts1 - ts0);
 
             // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h]).  The query
             // operands are read through an address that depends on the tile number (the
