@@ -865,6 +865,10 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
                     o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
                 }
+                // even slots summed code_even + 16 code_odd: take out the odd slot's sums
+#pragma unroll
+                for (int j = 0; j < 8; j += 2)
+                    o[j] -= o[j + 1];
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
                     const float sc = (j & 1) ? 1048576.0f : 16777216.0f; // undo 2^-20 / 2^-24
@@ -1081,18 +1085,19 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             for (int h = 0; h < G; h++) {
                 const float msub = mrun[h] == -__builtin_inff() ? 0.0f : mrun[h];
 #pragma unroll
-                for (int i = 0; i < TPL; i++) {
+                for (int i = 0; i < TPL; i++)
                     pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -msub));
-                    lsum[h] += pw[i][h];
-                }
             }
             // zero-point term and the fp16 weights p*s of this lane's position pair (-> LDS),
             // from the weights rounded to fp16 pairs: one packed product and one dot2 per
             // (group, head)
+            // (the softmax sum takes the same fp16-rounded weights the values get: one dot2)
             uint32_t ph[G];
 #pragma unroll
-            for (int h = 0; h < G; h++)
+            for (int h = 0; h < G; h++) {
                 ph[h] = pack_f16x2(pw[0][h], pw[1][h]);
+                lsum[h] = dot2(ph[h], 0x3C003C00u, lsum[h]); // (1.0, 1.0)
+            }
 #pragma unroll
             for (int gg = 0; gg < NG; gg++) {
                 const uint32_t sp = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x05040100u); // (s0, s1)
@@ -1131,10 +1136,13 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 }
 #pragma unroll
                 for (int q2 = 0; q2 < 2; q2++) {
+                    // c0 holds both nibbles of bytes 0 and 2 (code0 + 16 code1, still a
+                    // subnormal half), c1 code1 alone; the flush subtracts c1's sums from c0's.
+                    // Bytes 1 and 3 likewise, moved down by one byte permute.
                     const uint32_t x = q2 == 0 ? vv.x : vv.y;
-                    const uint32_t y = x >> 8;
-                    const uint32_t c0 = x & 0x000F000Fu, c1 = x & 0x00F000F0u;
-                    const uint32_t c2 = y & 0x000F000Fu, c3 = y & 0x00F000F0u;
+                    const uint32_t y = __builtin_amdgcn_perm(0u, x, 0x0c030c01u); // bytes 1, 3 -> 0, 2
+                    const uint32_t c0 = x & 0x00FF00FFu, c1 = x & 0x00F000F0u;
+                    const uint32_t c2 = y, c3 = y & 0x00F000F0u;
 #pragma unroll
                     for (int h = 0; h < G; h++) {
                         acc[h][4 * q2 + 0] = dot2(c0, wv[h], acc[h][4 * q2 + 0]);
