@@ -176,6 +176,26 @@ def cpu_baseline(w, length, budget_s):
                       f"append+decode steps, {t_used:.1f} s of oracle time"}
 
 
+def trace_summary(path: str, last: int) -> None:
+    """Per-kernel durations (us) of this library's kernels in a rocprofv3 kernel-trace CSV, in
+    dispatch order: count, mean over all dispatches, mean over the last `last`."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if "kvq::" not in name:
+            continue
+        short = name.split("(anonymous namespace)::")[-1].split("(")[0]
+        per.setdefault(short, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    print("| kernel | dispatches | mean us (all) | mean us (last %d) |" % last)
+    print("|---|---|---|---|")
+    for k, v in sorted(per.items()):
+        v.sort()
+        d = [(e - b) / 1e3 for b, e in v]
+        tail = d[-last:]
+        print(f"| `{k}` | {len(d)} | {sum(d) / len(d):.1f} | {sum(tail) / len(tail):.1f} |")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,9 +211,15 @@ def main():
     ap.add_argument("--traffic-csv", nargs=4, metavar=("DEC_FETCH", "DEC_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="reduce rocprofv3 counter CSVs to the decode kernel's HBM bytes per launch, "
                          "write the traffic record and exit (no GPU use)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "LAST"),
+                    help="average duration of this library's kernels in a rocprofv3 kernel-trace CSV, "
+                         "over all dispatches and over the last LAST of each (no GPU use)")
     args = ap.parse_args()
     if args.traffic_csv:
         write_traffic(*args.traffic_csv, out_path=TRAFFIC_FILE)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], int(args.trace_summary[1]))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
