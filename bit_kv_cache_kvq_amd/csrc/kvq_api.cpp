@@ -207,7 +207,7 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace: partial softmax states [slots][G][D + 4] fp32 (m, l, 2 unused, o), the query records,
-// the counters (one per wave place, one per unit)
+// the counters (two per wave place, one per unit)
 static size_t part_region_bytes(const kvq_cache *c, int G)
 {
     return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 4) * sizeof(float));
@@ -224,9 +224,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
         return 0;
     const size_t U = units_of(c);
     const size_t G = (size_t)(n_q_heads / c->n_kv_heads);
-    // counters: one per wave place (stripe tile counters), then one per unit (members done)
+    // counters: two per wave place (a stripe's tiles drawn and members done, at the place of
+    // its first member), then one per unit (members or stripes done)
     const size_t places = part_slots(c) > U ? part_slots(c) : U;
-    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + round256((places + U) * sizeof(uint32_t));
+    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + round256((2 * places + U) * sizeof(uint32_t));
 }
 
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)

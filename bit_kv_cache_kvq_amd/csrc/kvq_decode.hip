@@ -284,12 +284,15 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         }
     }
     mask = uniform(mask);
-    // the decode kernel's tile counters of this unit's stripes, at the places u + k * units
+    // the decode kernel's tile and arrival counters of this unit's stripes, at the places
+    // u + k * units
     for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
-        if (unit + k * p.n_units < p.n_waves)
+        if (unit + k * p.n_units < p.n_waves) {
             p.tile_ctr[unit + k * p.n_units] = 0u;
+            p.tile_ctr[p.n_waves + unit + k * p.n_units] = 0u;
+        }
     if (threadIdx.x == 0) {
-        p.tile_ctr[p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
+        p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
         rec[C::OFF_MASK] = mask;
         if (p.mask_out)
             p.mask_out[unit] = (uint8_t)mask;
@@ -711,31 +714,23 @@ __device__ __forceinline__ void load_batch(CombineBatch<D, G> &b, rsrc_t r, uint
                                              : 0.0f;
 }
 
+// Fold `count` partial states (slots first, first + step, ... in units of records) into the
+// state (M, L, O), which holds the sink state or an empty one on entry.
 template <int D, int G>
-__device__ __forceinline__ void combine_team(const DecodeParams &p, const float *sink, int u, int team, int lane,
-                                          float *out_u)
+__device__ __forceinline__ void fold_states(const DecodeParams &p, int first, int step, int count, int lane,
+                                            float (&M)[G], float (&L)[G], float (&O)[G][D / 64])
 {
     using CB = CombineBatch<D, G>;
     constexpr int CPL = CB::CPL, NB = CB::NB, PR = part_rec<D>();
-    const uint32_t stride = (uint32_t)p.n_units * G * PR * 4u; // bytes between members
-    // the team's slots: u + k * U for k < team, all below the number of waves
+    const uint32_t stride = (uint32_t)step * G * PR * 4u; // bytes between the states
+    // all slots are below the number of waves
     const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
-    const uint32_t ub = (uint32_t)u * G * PR * 4u; // member 0, head 0
-    float M[G], L[G], O[G][CPL];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        const float *sk = sink + h * (D + 2);
-        M[h] = sk[0];
-        L[h] = sk[1];
-#pragma unroll
-        for (int s = 0; s < CPL; s++)
-            O[h][s] = sk[2 + lane + 64 * s];
-    }
+    const uint32_t ub = (uint32_t)first * G * PR * 4u;    // first state, head 0
     CB cur, nxt;
-    load_batch<D, G>(cur, r, ub, stride, 0, team, lane);
-    for (int k0 = 0; k0 < team; k0 += NB) {
-        if (k0 + NB < team)
-            load_batch<D, G>(nxt, r, ub, stride, k0 + NB, team, lane);
+    load_batch<D, G>(cur, r, ub, stride, 0, count, lane);
+    for (int k0 = 0; k0 < count; k0 += NB) {
+        if (k0 + NB < count)
+            load_batch<D, G>(nxt, r, ub, stride, k0 + NB, count, lane);
 #pragma unroll
         for (int h = 0; h < G; h++) {
 #pragma unroll
@@ -756,11 +751,60 @@ __device__ __forceinline__ void combine_team(const DecodeParams &p, const float 
         }
         cur = nxt;
     }
+}
+
+// The unit's team, last step: fold `count` states (stripe or member states) into the sink
+// positions' state and write the normalised output out_u[h][D].
+template <int D, int G>
+__device__ __forceinline__ void combine_unit(const DecodeParams &p, const float *sink, int first, int step, int count,
+                                             int lane, float *out_u)
+{
+    constexpr int CPL = D / 64;
+    float M[G], L[G], O[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const float *sk = sink + h * (D + 2);
+        M[h] = sk[0];
+        L[h] = sk[1];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            O[h][s] = sk[2 + lane + 64 * s];
+    }
+    fold_states<D, G>(p, first, step, count, lane, M, L, O);
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
         for (int s = 0; s < CPL; s++)
             out_u[h * D + lane + 64 * s] = L[h] > 0.0f ? O[h][s] / L[h] : 0.0f;
+}
+
+// A stripe's last member: fold the stripe's member states into one state, stored (not
+// normalised) in the slot of the stripe's first member.
+template <int D, int G>
+__device__ __forceinline__ void combine_stripe(const DecodeParams &p, int first, int step, int count, int lane)
+{
+    constexpr int CPL = D / 64, PR = part_rec<D>();
+    float M[G], L[G], O[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        M[h] = -__builtin_inff();
+        L[h] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            O[h][s] = 0.0f;
+    }
+    fold_states<D, G>(p, first, step, count, lane, M, L, O);
+    const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const uint32_t rb = ((uint32_t)first * G + h) * PR * 4u;
+        if (lane == 0)
+            store_shared2(r, rb, M[h], L[h]);
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[h][s]), r, rb + (4u + lane + 64u * s) * 4u, 0,
+                                                  kCoherent);
+    }
 }
 
 // Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
@@ -838,6 +882,17 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         }
     };
 
+    // stripes: a team of more than kStripe waves splits the unit's tiles into S contiguous
+    // stripes, stripe s served by members s, s + S, ... with a counter of its own (at the
+    // place of member s), so no counter takes more than kStripe waves' draws
+    const int member = x / p.n_units;
+    const int S = (team + kStripe - 1) / kStripe;
+    const int stripe = member % S;
+    const int smem = member / S;                        // index within the stripe
+    const int nst = (team - stripe + S - 1) / S;        // members of the stripe
+    const int ts0 = (int)((long long)stripe * Tu / S);  // its tiles [ts0, ts1)
+    const int ts1 = (int)((long long)(stripe + 1) * Tu / S);
+
     // ---- end of the current unit's range in this wave: reduce over the wave, then write
     // the normalised output (whole unit here) or this wave's partial state
     auto flush = [&]() {
@@ -902,16 +957,37 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         }
         if (!whole) {
             // count this member in once its states are stored (all of the wave's memory
-            // operations complete); the member that arrives last combines the team's
-            // states (in member order, so the result does not depend on which member that
-            // is) with the sink positions' state
+            // operations complete); the member that arrives last combines the states (in
+            // member order, so the result does not depend on which member that is) with the
+            // sink positions' state.  A striped team does it in two steps: the last member of
+            // each stripe folds the stripe's states into its first member's slot and then
+            // counts the stripe in; the last stripe folds the stripes' states.
+            const float *sink = reinterpret_cast<const float *>(rec) + C::OFF_SINK;
+            float *out_u = p.out + ((size_t)b * n_q_heads + (size_t)kvh * G) * D;
             __builtin_amdgcn_s_waitcnt(0);
             uint32_t arrived = 0;
-            if (lane == 0)
-                arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_waves + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((int)uniform(arrived) == team - 1)
-                combine_team<D, G>(p, reinterpret_cast<const float *>(rec) + C::OFF_SINK, u, team, lane,
-                                   p.out + ((size_t)b * n_q_heads + (size_t)kvh * G) * D);
+            if (S == 1) {
+                if (lane == 0)
+                    arrived = __hip_atomic_fetch_add(p.tile_ctr + 2 * p.n_waves + u, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                if ((int)uniform(arrived) == team - 1)
+                    combine_unit<D, G>(p, sink, u, p.n_units, team, lane, out_u);
+            } else {
+                const int sfirst = u + stripe * p.n_units; // place of the stripe's first member
+                if (lane == 0)
+                    arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_waves + sfirst, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                if ((int)uniform(arrived) == nst - 1) {
+                    combine_stripe<D, G>(p, sfirst, S * p.n_units, nst, lane);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    uint32_t done = 0;
+                    if (lane == 0)
+                        done = __hip_atomic_fetch_add(p.tile_ctr + 2 * p.n_waves + u, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                    if ((int)uniform(done) == S - 1)
+                        combine_unit<D, G>(p, sink, u, p.n_units, S, lane, out_u);
+                }
+            }
         }
     };
 
@@ -925,16 +1001,6 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     uint2 vcur[VIT];
     reset();
     const Slabs sl = unit_slabs<D, G, KF>(p, u);
-    // stripes: a team of more than kStripe waves splits the unit's tiles into S contiguous
-    // stripes, stripe s served by members s, s + S, ... with a counter of its own (at the
-    // place of member s), so no counter takes more than kStripe waves' draws
-    const int member = x / p.n_units;
-    const int S = (team + kStripe - 1) / kStripe;
-    const int stripe = member % S;
-    const int smem = member / S;                        // index within the stripe
-    const int nst = (team - stripe + S - 1) / S;        // members of the stripe
-    const int ts0 = (int)((long long)stripe * Tu / S);  // its tiles [ts0, ts1)
-    const int ts1 = (int)((long long)(stripe + 1) * Tu / S);
     uint32_t *const ctr = p.tile_ctr + (u + stripe * p.n_units);
     const bool dynamic = p.dynamic && nst > 1;
     uint32_t ask = 0;

@@ -39,8 +39,9 @@ struct DecodeParams {
     uint8_t *mask_out;
     float *part;        // partial softmax states [wave][G][D + 4]: m, l, unused x2, o[D]
     uint32_t *qprep;    // per-unit query record written by the query-prep kernel
-    uint32_t *tile_ctr; // tiles drawn per stripe [n_waves] (at the place of the stripe's first member),
-                        // then members done per unit [units]; zeroed by the query-prep kernel
+    uint32_t *tile_ctr; // per stripe, at the place of its first member: tiles drawn [n_waves], members
+                        // done [n_waves]; then per unit: members / stripes done [units]; zeroed by
+                        // the query-prep kernel
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
     float sm_log2e;      // softmax scale times log2(e)
     int n_units, tiles_per_unit, n_waves; // work split: n_waves >= n_units waves, wave w serves unit w % n_units
