@@ -893,8 +893,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const int ts0 = (int)((long long)stripe * Tu / S);  // its tiles [ts0, ts1)
     const int ts1 = (int)((long long)(stripe + 1) * Tu / S);
 
-    // ---- end of the current unit's range in this wave: reduce over the wave, then write
-    // the normalised output (whole unit here) or this wave's partial state
+    // ---- end of this wave's tiles: reduce over the wave, then write the normalised output
+    // (the unit's only wave) or this wave's partial state
     auto flush = [&]() {
         const bool whole = team == 1;
         const int b = u / p.n_kv_heads;
