@@ -638,6 +638,21 @@ __device__ __forceinline__ void set_priority_for(int t, int Tu)
 // a multiple of n_cu the places of one CU's waves are made consecutive (x = (w mod n_cu) *
 // (W / n_cu) + w / n_cu): the members of a team, U places apart, then sit on different CUs
 // at different ages, and no team gets a much larger or smaller share of the device.
+// A wave-uniform integer pinned to a scalar register.  The divisions of the work split run
+// on the vector unit; the compiler drops a readfirstlane builtin on values it already knows to
+// be uniform, and may then keep the unit's slab descriptors and tile offsets in vector
+// registers, which puts a loop around every buffer load (one pass per distinct value).  The
+// opaque readfirstlane keeps everything derived from these values scalar.  The compiler does
+// not look inside the asm for hazards, so the wait states are part of it: the read of a VGPR
+// just written by another vector instruction needs one, and an SGPR written by a vector
+// instruction needs up to five before a memory instruction or a lane select may read it.
+__device__ __forceinline__ int sgpr(int v)
+{
+    int r;
+    asm volatile("s_nop 4\n\tv_readfirstlane_b32 %0, %1\n\ts_nop 4" : "=s"(r) : "v"(v));
+    return r;
+}
+
 __device__ __forceinline__ int team_slot(int w, int W, int n_cu)
 {
     return (n_cu > 0 && W % n_cu == 0) ? (w % n_cu) * (W / n_cu) + w / n_cu : w;
@@ -830,9 +845,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
     const int Tu = p.tiles_per_unit;
-    const int x = team_slot(w, p.n_waves, p.n_cu);       // this wave's place
-    const int u = x % p.n_units;                          // its unit
-    const int team = team_size(u, p.n_units, p.n_waves); // waves serving it
+    const int x = sgpr(team_slot(w, p.n_waves, p.n_cu));       // this wave's place
+    const int u = sgpr(x % p.n_units);                          // its unit
+    const int team = sgpr(team_size(u, p.n_units, p.n_waves)); // waves serving it
     const int n_q_heads = p.n_kv_heads * G;
     const uint32_t ucap = (uint32_t)p.cap;
 
@@ -885,13 +900,13 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     // stripes: a team of more than kStripe waves splits the unit's tiles into S contiguous
     // stripes, stripe s served by members s, s + S, ... with a counter of its own (at the
     // place of member s), so no counter takes more than kStripe waves' draws
-    const int member = x / p.n_units;
-    const int S = (team + kStripe - 1) / kStripe;
-    const int stripe = member % S;
-    const int smem = member / S;                        // index within the stripe
-    const int nst = (team - stripe + S - 1) / S;        // members of the stripe
-    const int ts0 = (int)((long long)stripe * Tu / S);  // its tiles [ts0, ts1)
-    const int ts1 = (int)((long long)(stripe + 1) * Tu / S);
+    const int member = sgpr(x / p.n_units);
+    const int S = sgpr((team + kStripe - 1) / kStripe);
+    const int stripe = sgpr(member % S);
+    const int smem = sgpr(member / S);                       // index within the stripe
+    const int nst = sgpr((team - stripe + S - 1) / S);       // members of the stripe
+    const int ts0 = sgpr((int)((long long)stripe * Tu / S)); // its tiles [ts0, ts1)
+    const int ts1 = sgpr((int)((long long)(stripe + 1) * Tu / S));
 
     // ---- end of this wave's tiles: reduce over the wave, then write the normalised output
     // (the unit's only wave) or this wave's partial state
