@@ -822,8 +822,8 @@ __device__ __forceinline__ void combine_stripe(const DecodeParams &p, int first,
     }
 }
 
-// Register budget: 4 heads over INT2 keys fit 3 waves per SIMD (168 VGPRs); 4-bit keys
-// (twice the key words in flight) and 8 heads get 2.
+// Register budget: 4 heads over INT2 or Lloyd-Max keys fit 3 waves per SIMD (168 VGPRs);
+// asymmetric 4-bit keys (twice the key words and their scales in flight) and 8 heads get 2.
 //
 // Work split: the grid holds one wave per resident slot of the device, at least one per unit
 // (see team_size).  Waves resident on one SIMD get unequal shares of its issue slots (older
@@ -833,7 +833,7 @@ __device__ __forceinline__ void combine_stripe(const DecodeParams &p, int first,
 // (m, l, o) in the slot of its place, and the last member to finish combines them.
 template <int D, int G, int KF>
 __global__ __launch_bounds__(kWave)
-__attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF == KVQ_K_ASYM2)) ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF != KVQ_K_ASYM4)) ? 3 : 2)))
 void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 {
     using C = Cfg<D, G, KF>;
