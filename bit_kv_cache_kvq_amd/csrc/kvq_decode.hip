@@ -695,14 +695,15 @@ constexpr int part_rec() { return D + 4; }
 // Combine the partial softmax states (m, l, o) of a unit's team, member k in slot u + k * U,
 // with the sink positions' state: one global softmax over all positions (Dual-QK sec. 3.4),
 // normalised into out_u[h][D].  Run by one wave; lane j holds channels j, j + 64 of every
-// head.  Members go in batches of NB, all heads at once (32 o loads per lane per batch),
+// head.  Members go in batches of NB, all heads at once (48 o loads per lane per batch),
 // and the next batch's loads are issued before the current batch is folded in, so a team
-// of n members costs about one memory latency plus n / NB load rounds.  Lane j < G * NB
-// reads (m, l) of head j / NB, member j % NB of the batch; readlane passes them on.
+// of n members costs about one memory latency plus n / NB load rounds (the tile loop's
+// registers are free by then: two batches take 96 VGPRs).  Lane j < G * NB reads (m, l)
+// of head j / NB, member j % NB of the batch; readlane passes them on.
 template <int D, int G>
 struct CombineBatch {
     static constexpr int CPL = D / 64;
-    static constexpr int NB = 32 / (G * CPL);
+    static constexpr int NB = 48 / (G * CPL);
     float m, l;
     float o[G][NB][CPL];
 };
@@ -897,16 +898,21 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         }
     };
 
-    // stripes: a team of more than kStripe waves splits the unit's tiles into S contiguous
-    // stripes, stripe s served by members s, s + S, ... with a counter of its own (at the
-    // place of member s), so no counter takes more than kStripe waves' draws
+    // stripes: a team of more than kStripe waves splits into S stripes of B = ceil(team / S)
+    // consecutive members (the last one may have fewer); a stripe serves a contiguous range
+    // of the unit's tiles in proportion to its members, with a counter of its own at the
+    // place of its first member, so no counter takes more than kStripe waves' draws.
+    // Consecutive members sit at different ages on their compute units (see team_slot), so
+    // every stripe gets a mix of fast and slow waves and the stripes end together.
     const int member = sgpr(x / p.n_units);
     const int S = sgpr((team + kStripe - 1) / kStripe);
-    const int stripe = sgpr(member % S);
-    const int smem = sgpr(member / S);                       // index within the stripe
-    const int nst = sgpr((team - stripe + S - 1) / S);       // members of the stripe
-    const int ts0 = sgpr((int)((long long)stripe * Tu / S)); // its tiles [ts0, ts1)
-    const int ts1 = sgpr((int)((long long)(stripe + 1) * Tu / S));
+    const int B = sgpr((team + S - 1) / S);
+    const int stripe = sgpr(member / B);
+    const int m0 = stripe * B;                                 // its first member
+    const int smem = sgpr(member - m0);                        // index within the stripe
+    const int nst = sgpr(min(m0 + B, team) - m0);              // members of the stripe
+    const int ts0 = sgpr((int)((long long)m0 * Tu / team));    // its tiles [ts0, ts1)
+    const int ts1 = sgpr((int)((long long)(m0 + nst) * Tu / team));
 
     // ---- end of this wave's tiles: reduce over the wave, then write the normalised output
     // (the unit's only wave) or this wave's partial state
@@ -988,19 +994,19 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 if ((int)uniform(arrived) == team - 1)
                     combine_unit<D, G>(p, sink, u, p.n_units, team, lane, out_u);
             } else {
-                const int sfirst = u + stripe * p.n_units; // place of the stripe's first member
+                const int sfirst = u + m0 * p.n_units; // place of the stripe's first member
                 if (lane == 0)
                     arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_waves + sfirst, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
                 if ((int)uniform(arrived) == nst - 1) {
-                    combine_stripe<D, G>(p, sfirst, S * p.n_units, nst, lane);
+                    combine_stripe<D, G>(p, sfirst, p.n_units, nst, lane);
                     __builtin_amdgcn_s_waitcnt(0);
                     uint32_t done = 0;
                     if (lane == 0)
                         done = __hip_atomic_fetch_add(p.tile_ctr + 2 * p.n_waves + u, 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
                     if ((int)uniform(done) == S - 1)
-                        combine_unit<D, G>(p, sink, u, p.n_units, S, lane, out_u);
+                        combine_unit<D, G>(p, sink, u, B * p.n_units, S, lane, out_u);
                 }
             }
         }
@@ -1016,7 +1022,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     uint2 vcur[VIT];
     reset();
     const Slabs sl = unit_slabs<D, G, KF>(p, u);
-    uint32_t *const ctr = p.tile_ctr + (u + stripe * p.n_units);
+    uint32_t *const ctr = p.tile_ctr + (u + m0 * p.n_units);
     const bool dynamic = p.dynamic && nst > 1;
     uint32_t ask = 0;
     if (dynamic && lane == 0)
