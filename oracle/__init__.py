@@ -32,6 +32,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
           "-fopenmp", "-Wall", "-Wextra"]
 
 K_ASYM2, K_ASYM4, K_LLOYD4, K_ASYM8 = 0, 1, 2, 3
+V_ASYM4_G32, V_ASYM2_TOKEN = 0, 1
 
 
 def build(force: bool = True) -> str:
@@ -71,7 +72,7 @@ def lib():
         L.oracle_tree_sum_f32.argtypes = [P, i]
         L.oracle_lloyd_max_gaussian.restype = i
         L.oracle_lloyd_max_gaussian.argtypes = [i, ctypes.c_double, i, P, P]
-        cache_args = [i, i, i, i, i, i, P, P, P, P, P, P, P, P]
+        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, P, P, P, P, P, P, P, P]
         L.oracle_quant_append.argtypes = cache_args + [P, P, i, i, i, P, P]
         L.oracle_prune_mask.restype = ctypes.c_uint32
         L.oracle_prune_mask.argtypes = [P, i, i, i]
@@ -165,6 +166,8 @@ class Geometry:
     k_format: int = K_ASYM2
     k_hadamard: int = 0
     k_ch0_bf16: int = 0
+    v_format: int = V_ASYM4_G32
+    v_clip: float = 1.0
 
     @property
     def units(self) -> int:
@@ -189,8 +192,9 @@ class OracleCache:
         self.k_sz = np.zeros((U, d // 32, cap), dtype=np.uint32)
         self.k_norm = np.zeros((U, cap), dtype=np.uint16)
         self.k_ch0 = np.zeros((U, cap), dtype=np.uint16)
-        self.v_codes = np.zeros((U, cap // 2, d // 4), dtype=np.uint32)
-        self.v_sz = np.zeros((U, d // 32, cap), dtype=np.uint32)
+        per_token = geo.v_format == V_ASYM2_TOKEN
+        self.v_codes = np.zeros((U, cap // 2, d // 8 if per_token else d // 4), dtype=np.uint32)
+        self.v_sz = np.zeros((U, 1 if per_token else d // 32, cap), dtype=np.uint32)
         self.sink_k = np.zeros((U, ns, d), dtype=np.uint16)
         self.sink_v = np.zeros((U, ns, d), dtype=np.uint16)
         self.len = 0
@@ -203,7 +207,7 @@ class OracleCache:
     def _cache_args(self):
         g = self.geo
         return [g.head_dim, g.capacity, g.n_sink, g.k_format, g.k_hadamard, g.k_ch0_bf16,
-                _p(self.k_codes), _p(self.k_sz), _p(self.k_norm), _p(self.k_ch0),
+                g.v_format, float(g.v_clip), _p(self.k_codes), _p(self.k_sz), _p(self.k_norm), _p(self.k_ch0),
                 _p(self.v_codes), _p(self.v_sz), _p(self.sink_k), _p(self.sink_v)]
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):

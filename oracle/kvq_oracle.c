@@ -20,6 +20,9 @@
  *     Dual-QK sec. 3.3 / 4.1: first tokens kept in BF16);
  *   - dynamic query-channel-group pruning with one mask per GQA group, ranked by
  *     query energy summed over the group's heads (Dual-QK sec. 3.2, sec. C.2, App. A);
+ *   - values as asymmetric INT4 per 32-channel group, or as per-token asymmetric INT2
+ *     with a clipping ratio (Dual-QK sec. 3.3 and sec. B.2: per-token INT2 values with
+ *     0.92 clipping);
  *   - attention over the decoded cache with one softmax over all positions
  *     (Dual-QK sec. 3.4: bucket scores share one global softmax).
  *
@@ -46,8 +49,10 @@
 /* ------------------------------------------------------------------------------------ */
 /* Format constants.  Key format ids: 0 = asymmetric INT2, 1 = asymmetric INT4,
  * 2 = 4-bit Lloyd-Max codebook, 3 = asymmetric INT8 (oracle only, for the convergence
- * check that 8-bit codes approach dense attention).  Values are always asymmetric INT4.  */
+ * check that 8-bit codes approach dense attention).  Value format ids: 0 = asymmetric INT4
+ * per 32-channel group, 1 = per-token asymmetric INT2 with a clipping ratio.            */
 enum { OK_ASYM2 = 0, OK_ASYM4 = 1, OK_LLOYD4 = 2, OK_ASYM8 = 3 };
+enum { OV_ASYM4_G32 = 0, OV_ASYM2_TOKEN = 1 };
 
 static int key_bits(int kfmt) { return kfmt == OK_ASYM2 ? 2 : kfmt == OK_ASYM8 ? 8 : 4; }
 
@@ -254,14 +259,20 @@ int oracle_lloyd_max_gaussian(int levels, double tol, int max_iter, double *cent
  *   k_sz    u32 [U][d/32][cap]    asymmetric keys: low 16 bits fp16 scale, high fp16 zero
  *   k_norm  u16 [U][cap]          Lloyd-Max keys: fp16 rho
  *   k_ch0   u16 [U][cap]          protected channel 0: bf16
- *   v_codes u32 [U][cap/2][d/4]   word j of token pair P: bits [4k,4k+3] = channel 4j+k of
- *                                 token 2P, bits [16+4k, 16+4k+3] = same channel of 2P+1
- *   v_sz    u32 [U][d/32][cap]    fp16 scale (low) / zero (high)
+ *   v_codes u32 [U][cap/2][d/4]   INT4 values: word j of token pair P: bits [4k,4k+3] =
+ *                                 channel 4j+k of token 2P, bits [16+4k, 16+4k+3] = same
+ *                                 channel of 2P+1
+ *           u32 [U][cap/2][d/8]   per-token INT2 values: word j of pair P: bits [2k,2k+1] =
+ *                                 channel 8j+k of token 2P, bits [16+2k, 16+2k+1] = same
+ *                                 channel of 2P+1
+ *   v_sz    u32 [U][d/32][cap]    fp16 scale (low) / zero (high); one row ([U][1][cap])
+ *                                 for per-token values
  *   sink_k  u16 [U][n_sink][d]    bf16 key in stored coordinates (rotated if rotation on)
  *   sink_v  u16 [U][n_sink][d]    bf16 value
  * Slots t < n_sink of the quantised arrays are never written.                           */
 typedef struct {
-    int d, cap, n_sink, kfmt, rotate, ch0;
+    int d, cap, n_sink, kfmt, rotate, ch0, vfmt;
+    float vclip; /* per-token INT2 values: clipping ratio */
     uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
     uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
     const float *cent, *thr; /* Lloyd-Max: 16 centroids, 15 thresholds (fp32) */
@@ -309,6 +320,46 @@ static void asym_group(const float *x, int n, int bits, int skip0, uint8_t *code
             r = 0.0f;
         if (r > (float)qmax)
             r = (float)qmax;
+        code[i] = (uint8_t)r;
+    }
+    *sh_out = sh;
+    *zh_out = zh;
+}
+
+/* Per-token asymmetric INT2 of one value vector with clipping ratio `clip` (Dual-QK
+ * sec. B.2: values use per-token asymmetric INT2 with a 0.92 clipping ratio).
+ * Reading: the clipped range is [clip*min, clip*max] (both ends scaled toward zero, the
+ * usual convention of rotation-based quantizers for a clipping ratio); scale = clipped
+ * range / 3 and zero = clip*min as fp16, codes against the rounded values as in
+ * asym_group, so entries outside the clipped range saturate at code 0 or 3.  With clip = 1
+ * this is asym_group over the whole vector.                                              */
+static void asym_token_clip(const float *x, int n, float clip, uint8_t *code, uint16_t *sh_out,
+                            uint16_t *zh_out)
+{
+    float mn = x[0], mx = x[0];
+    for (int i = 1; i < n; i++) {
+        if (x[i] < mn)
+            mn = x[i];
+        if (x[i] > mx)
+            mx = x[i];
+    }
+    mn = clip * mn + 0.0f;
+    mx = clip * mx;
+    float range = (mx - mn) + 0.0f;
+    float scale32 = range / 3.0f;
+    uint16_t sh = oracle_f32_to_f16(scale32);
+    uint16_t zh = oracle_f32_to_f16(mn);
+    float sf = oracle_f16_to_f32(sh);
+    float zf = oracle_f16_to_f32(zh);
+    float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+    for (int i = 0; i < n; i++) {
+        float diff = x[i] - zf;
+        float u = diff * inv;
+        float r = rintf(u);
+        if (r < 0.0f)
+            r = 0.0f;
+        if (r > 3.0f)
+            r = 3.0f;
         code[i] = (uint8_t)r;
     }
     *sh_out = sh;
@@ -380,8 +431,24 @@ static void quant_token(const ocache *c, size_t u, int t, const float *k, const 
         c->k_codes[(u * R + r) * cap + (size_t)t] = w;
     }
 
-    /* values: asymmetric INT4 per 32-channel group, no channel exclusion */
     uint8_t vc[256];
+    if (c->vfmt == OV_ASYM2_TOKEN) {
+        /* values: per-token asymmetric INT2 with clipping, pair-interleaved words */
+        uint16_t sh, zh;
+        asym_token_clip(v, d, c->vclip, vc, &sh, &zh);
+        c->v_sz[u * cap + (size_t)t] = (uint32_t)sh | ((uint32_t)zh << 16);
+        const size_t W2 = (size_t)(d / 8);
+        uint32_t *row2 = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * W2;
+        const int s16 = (t & 1) ? 16 : 0;
+        for (size_t j = 0; j < W2; j++) {
+            uint32_t half = 0;
+            for (int k2 = 0; k2 < 8; k2++)
+                half |= (uint32_t)vc[8 * j + (size_t)k2] << (2 * k2);
+            row2[j] = (row2[j] & ~(0xFFFFu << s16)) | (half << s16);
+        }
+        return;
+    }
+    /* values: asymmetric INT4 per 32-channel group, no channel exclusion */
     for (int g = 0; g < d / 32; g++) {
         uint16_t sh, zh;
         asym_group(v + 32 * g, 32, 4, 0, vc + 32 * g, &sh, &zh);
@@ -401,13 +468,13 @@ static void quant_token(const ocache *c, size_t u, int t, const float *k, const 
 
 /* Append n_new tokens per unit at positions [t0, t0+n_new) for units [0, n_units).
  * k_new, v_new: fp32 [n_units][n_new][d].  OpenMP over units.                            */
-void oracle_quant_append(int d, int cap, int n_sink, int kfmt, int rotate, int ch0,
+void oracle_quant_append(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
                          const float *cent, const float *thr, int n_units, int t0, int n_new,
                          const float *k_new, const float *v_new)
 {
-    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, k_codes, k_sz, v_codes, v_sz,
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, k_codes, k_sz, v_codes, v_sz,
                 k_norm, k_ch0, sink_k, sink_v, cent, thr};
 #pragma omp parallel for schedule(static)
     for (int u = 0; u < n_units; u++)
@@ -506,9 +573,20 @@ static void decode_value(const ocache *c, size_t u, int t, double *vh)
             vh[i] = (double)oracle_bf16_to_f32(sv[i]);
         return;
     }
+    const int sh16 = (t & 1) ? 16 : 0;
+    if (c->vfmt == OV_ASYM2_TOKEN) {
+        const uint32_t *row2 = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * (size_t)(d / 8);
+        uint32_t sz = c->v_sz[u * cap + (size_t)t];
+        double sf = (double)oracle_f16_to_f32((uint16_t)(sz & 0xFFFFu));
+        double zf = (double)oracle_f16_to_f32((uint16_t)(sz >> 16));
+        for (int i = 0; i < d; i++) {
+            int cd = (int)(((row2[i / 8] >> sh16) >> (2 * (i % 8))) & 0x3u);
+            vh[i] = (double)cd * sf + zf;
+        }
+        return;
+    }
     const size_t W = (size_t)(d / 4);
     const uint32_t *pairrow = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * W;
-    const int sh16 = (t & 1) ? 16 : 0;
     for (int g = 0; g < d / 32; g++) {
         uint32_t sz = c->v_sz[(u * (size_t)(d / 32) + (size_t)g) * cap + (size_t)t];
         double sf = (double)oracle_f16_to_f32((uint16_t)(sz & 0xFFFFu));
@@ -522,12 +600,12 @@ static void decode_value(const ocache *c, size_t u, int t, double *vh)
 }
 
 /* Decoded cache of one unit, for tests: keys in stored coordinates, values. [len][d]. */
-void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int ch0,
+void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
                          const float *cent, int unit, int len, double *kh, double *vh)
 {
-    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, k_codes, k_sz, v_codes, v_sz,
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, k_codes, k_sz, v_codes, v_sz,
                 k_norm, k_ch0, sink_k, sink_v, cent, 0};
     for (int t = 0; t < len; t++) {
         decode_key(&c, (size_t)unit, t, kh + (size_t)t * (size_t)d);
@@ -546,14 +624,14 @@ void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int c
  * The mask is computed from the fp32 stored-coordinate query (oracle_prune_mask) and
  * written to mask_out[u] when mask_out is not null.  logits_out (nullable) receives the
  * fp64 logits [n_units][G][len].                                                         */
-void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch0,
+void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
                         uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                         uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
                         const float *cent, int n_units, int len, int G, const float *q,
                         double sm, int keep_groups, double *out, uint8_t *mask_out,
                         double *logits_out)
 {
-    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, k_codes, k_sz, v_codes, v_sz,
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, k_codes, k_sz, v_codes, v_sz,
                 k_norm, k_ch0, sink_k, sink_v, cent, 0};
 #pragma omp parallel for schedule(dynamic, 1)
     for (int u = 0; u < n_units; u++) {

@@ -11,6 +11,9 @@ Format (per unit, absolute token positions):
   values: word j of token pair P = v_codes[P, j] holds channels 4j..4j+3, token 2P in the
   low 16 bits and token 2P+1 in the high 16 bits, channel 4j+k at nibble k of its half;
   v_sz like k_sz.
+  Per-token INT2 values (value format 1): word j of token pair P = v_codes[P, j] holds
+  channels 8j..8j+7, token 2P in the low 16 bits and 2P+1 in the high 16 bits, channel
+  8j+k at bits [2k, 2k+1] of its half; v_sz[0, t] holds the token's fp16 scale and zero.
 """
 import numpy as np
 
@@ -42,6 +45,15 @@ def value_codes(v_codes_unit, d, len_):
     return nib.reshape(npair * 2, d)[:len_].astype(np.int64)
 
 
+def value_codes_int2(v_codes_unit, d, len_):
+    """[len, d] integer codes from per-token INT2 v_codes[cap/2, d/8]."""
+    npair = (len_ + 1) // 2
+    w = v_codes_unit[:npair, : d // 8].astype(np.uint64)  # [P, d/8]
+    halves = np.stack([w & np.uint64(0xFFFF), w >> np.uint64(16)], axis=1)  # [P, 2, d/8]
+    crumbs = np.stack([(halves >> np.uint64(2 * k)) & np.uint64(3) for k in range(8)], axis=-1)
+    return crumbs.reshape(npair * 2, d)[:len_].astype(np.int64)
+
+
 def scale_zero(sz_unit, d, len_):
     """(scale, zero) fp64 [len, d/32] from sz[d/32, cap]."""
     s = sz_unit[: d // 32, :len_]
@@ -65,9 +77,14 @@ def decode_unit(oc, u, len_):
         kh[:] = codes * np.repeat(s, 32, axis=1) + np.repeat(z, 32, axis=1)
         if g.k_ch0_bf16:
             kh[:, 0] = bf16(oc.k_ch0[u, :len_])
-    vc = value_codes(oc.v_codes[u], d, len_)
-    s, z = scale_zero(oc.v_sz[u], d, len_)
-    vh[:] = vc * np.repeat(s, 32, axis=1) + np.repeat(z, 32, axis=1)
+    if getattr(g, "v_format", 0) == 1:
+        vc = value_codes_int2(oc.v_codes[u], d, len_)
+        sz = oc.v_sz[u, 0, :len_]
+        vh[:] = vc * f16(sz & 0xFFFF)[:, None] + f16(sz >> 16)[:, None]
+    else:
+        vc = value_codes(oc.v_codes[u], d, len_)
+        s, z = scale_zero(oc.v_sz[u], d, len_)
+        vh[:] = vc * np.repeat(s, 32, axis=1) + np.repeat(z, 32, axis=1)
     n = min(ns, len_)
     if n:
         kh[:n] = bf16(oc.sink_k[u, :n])

@@ -14,9 +14,9 @@ import pytest
 import format_ref as fr
 
 
-def _geo(oracle_mod, d, cap=512, kfmt=0, rot=0, ch0=0, ns=0, units=1):
+def _geo(oracle_mod, d, cap=512, kfmt=0, rot=0, ch0=0, ns=0, units=1, vfmt=0, vclip=1.0):
     return oracle_mod.Geometry(batch=units, n_kv_heads=1, head_dim=d, capacity=cap, n_sink=ns,
-                               k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0)
+                               k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0, v_format=vfmt, v_clip=vclip)
 
 
 def _brute(oracle_mod, oc, q, sm, keep):
@@ -44,23 +44,26 @@ def _brute(oracle_mod, oc, q, sm, keep):
 
 
 CASES = [
-    # d, kfmt, rot, ch0, n_sink, T, G, keep
-    (64, 0, 0, 1, 0, 1, 1, 0),
-    (64, 0, 0, 1, 0, 7, 1, 0),
-    (128, 0, 0, 1, 0, 8, 4, 5),
-    (128, 1, 0, 0, 2, 6, 4, 0),
-    (128, 2, 1, 0, 0, 5, 4, 3),
-    (64, 2, 0, 0, 3, 8, 2, 0),
-    (128, 0, 0, 0, 4, 8, 8, 7),
-    (64, 3, 0, 1, 0, 4, 1, 2),
+    # d, kfmt, rot, ch0, n_sink, T, G, keep, value format
+    (64, 0, 0, 1, 0, 1, 1, 0, 0),
+    (64, 0, 0, 1, 0, 7, 1, 0, 0),
+    (128, 0, 0, 1, 0, 8, 4, 5, 0),
+    (128, 1, 0, 0, 2, 6, 4, 0, 0),
+    (128, 2, 1, 0, 0, 5, 4, 3, 0),
+    (64, 2, 0, 0, 3, 8, 2, 0, 0),
+    (128, 0, 0, 0, 4, 8, 8, 7, 0),
+    (64, 3, 0, 1, 0, 4, 1, 2, 0),
+    (128, 0, 0, 1, 3, 9, 4, 5, 1),
+    (64, 1, 0, 0, 0, 7, 2, 0, 1),
 ]
 
 
-@pytest.mark.parametrize("d,kfmt,rot,ch0,ns,T,G,keep", CASES)
-def test_oracle_equals_bruteforce(oracle_mod, d, kfmt, rot, ch0, ns, T, G, keep):
+@pytest.mark.parametrize("d,kfmt,rot,ch0,ns,T,G,keep,vfmt", CASES)
+def test_oracle_equals_bruteforce(oracle_mod, d, kfmt, rot, ch0, ns, T, G, keep, vfmt):
     rng = np.random.default_rng(d + 10 * kfmt + T)
     U = 2
-    oc = oracle_mod.OracleCache(_geo(oracle_mod, d, kfmt=kfmt, rot=rot, ch0=ch0, ns=ns, units=U))
+    oc = oracle_mod.OracleCache(_geo(oracle_mod, d, kfmt=kfmt, rot=rot, ch0=ch0, ns=ns, units=U,
+                                     vfmt=vfmt, vclip=0.92))
     k = (rng.standard_normal((U, T, d)) * 2).astype(np.float32)
     v = rng.standard_normal((U, T, d)).astype(np.float32)
     oc.append(k, v)

@@ -4,7 +4,8 @@ Asymmetric INT-b keys with channel 0 in BF16 outside the range estimate: Dual-QK
 Queries and Flat Keys for Prunable 2-bit KV Caches, sec. 3.3 and sec. C.3.  Lloyd-Max
 codes after a Walsh-Hadamard rotation: TurboQuant on Quantized Models (topic list);
 Statistical Inference ... Inspired by TurboQuant (scheme KQV, Beta -> Gaussian marginal).
-Sink tokens in BF16: TurboQuant on Quantized Models (abstract).
+Sink tokens in BF16: TurboQuant on Quantized Models (abstract).  Per-token INT2 values with
+a clipping ratio: Dual-QK sec. 3.3 and sec. B.2.
 """
 import numpy as np
 import pytest
@@ -14,9 +15,9 @@ from scipy import stats
 import format_ref as fr
 
 
-def _cache(oracle_mod, d=128, cap=256, kfmt=0, rot=0, ch0=0, n_sink=0, units=1):
+def _cache(oracle_mod, d=128, cap=256, kfmt=0, rot=0, ch0=0, n_sink=0, units=1, vfmt=0, vclip=1.0):
     g = oracle_mod.Geometry(batch=units, n_kv_heads=1, head_dim=d, capacity=cap, n_sink=n_sink,
-                            k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0)
+                            k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0, v_format=vfmt, v_clip=vclip)
     return oracle_mod.OracleCache(g)
 
 
@@ -199,3 +200,98 @@ def test_input_validation(oracle_mod):
         oc.append(np.full((1, 1, 64), 7e4, np.float32), np.zeros((1, 1, 64), np.float32))
     with pytest.raises(ValueError):
         oc.append(np.zeros((1, 257, 64), np.float32), np.zeros((1, 257, 64), np.float32))
+
+
+def _token_int2(oc, d, T):
+    codes = fr.value_codes_int2(oc.v_codes[0], d, T)
+    sz = oc.v_sz[0, 0, :T]
+    return codes, fr.f16(sz & 0xFFFF), fr.f16(sz >> 16)
+
+
+@pytest.mark.parametrize("clip", [1.0, 0.92, 0.5])
+@pytest.mark.parametrize("kind", ["normal", "t3", "wide"])
+def test_token_int2_codes_are_nearest_level(oracle_mod, clip, kind):
+    """Per-token INT2 values with clipping (Dual-QK sec. B.2): brute force over the 4 levels
+    zf + k*sf (entries beyond the clipped range land on an end level), except within 1e-4
+    of a midpoint; the parameters describe the clipped range [clip*min, clip*max]."""
+    rng = np.random.default_rng(300)
+    T, d = 150, 128
+    x = _groups(rng, T * 4, kind).reshape(1, T, d)
+    oc = _cache(oracle_mod, d=d, vfmt=1, vclip=clip)
+    oc.append(x, x)
+    codes, s, z = _token_int2(oc, d, T)
+    levels = z[:, None, None] + np.arange(4)[None, None, :] * s[:, None, None]
+    brute = np.argmin(np.abs(x[0].astype(np.float64)[..., None] - levels), axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (x[0] - z[:, None]) / s[:, None]
+    frac = np.abs(u - np.floor(u) - 0.5)
+    ok = (frac > 1e-4) | ~np.isfinite(u)
+    assert np.all(codes[ok] == brute[ok])
+    mn, mx = x[0].astype(np.float64).min(-1), x[0].astype(np.float64).max(-1)
+    tol = 2 ** -10 * np.maximum(np.abs(mn), np.abs(mx))
+    assert np.all(np.abs(z - clip * mn) <= tol)
+    assert np.all(np.abs(z + 3 * s - clip * mx) <= 3 * tol)
+    # the extremes saturate at the end codes
+    assert np.all(codes[np.arange(T), np.argmax(x[0], -1)] == 3)
+    assert np.all(codes[np.arange(T), np.argmin(x[0], -1)] == 0)
+
+
+def test_token_int2_without_clipping_is_one_group_asym2(oracle_mod):
+    """With clip = 1 a per-token INT2 value is the (brute-force pinned) asymmetric INT2
+    quantizer over a group spanning the whole token: same codes and parameters as INT2
+    keys of a head whose 32-channel groups all hold copies of that token's extremes."""
+    rng = np.random.default_rng(301)
+    T, d = 64, 128
+    x = rng.standard_normal((1, T, d)).astype(np.float32)
+    # put each token's min and max into every 32-channel group, so every key group's
+    # range equals the whole token's range
+    mn, mx = x[0].min(-1), x[0].max(-1)
+    for g in range(4):
+        x[0, :, 32 * g] = mn
+        x[0, :, 32 * g + 1] = mx
+    oc = _cache(oracle_mod, d=d, vfmt=1, vclip=1.0)
+    oc.append(x, x)
+    codes, s, z = _token_int2(oc, d, T)
+    kcodes = fr.key_codes(oc.k_codes[0], 2, d, T)
+    ks, kz = fr.scale_zero(oc.k_sz[0], d, T)
+    np.testing.assert_array_equal(codes, kcodes)
+    for g in range(4):
+        np.testing.assert_array_equal(s, ks[:, g])
+        np.testing.assert_array_equal(z, kz[:, g])
+
+
+def test_token_int2_clipping_lowers_gaussian_error(oracle_mod):
+    """At 2 bits the uniform quantizer with least squared error on N(0,1) spans far less
+    than the extremes of 128 draws, so shrinking the range by 0.92 lowers the mean squared
+    error (the reason for the clipping ratio, Dual-QK sec. B.2)."""
+    rng = np.random.default_rng(302)
+    T, d = 400, 128
+    x = rng.standard_normal((1, T, d)).astype(np.float32)
+    err = {}
+    for clip in (1.0, 0.92):
+        oc = _cache(oracle_mod, d=d, cap=512, vfmt=1, vclip=clip)
+        oc.append(x, x)
+        _, vh = oc.dequant(0)
+        err[clip] = np.mean((vh - x[0]) ** 2)
+    assert err[0.92] < 0.97 * err[1.0]
+
+
+def test_token_int2_layout_two_independent_decoders(oracle_mod):
+    """C decoder and the numpy reader agree on per-token INT2 values, odd lengths and
+    appends split across a token pair included; sinks stay BF16."""
+    rng = np.random.default_rng(303)
+    for d, ns in [(128, 0), (64, 3), (128, 5)]:
+        T = 41
+        oc = _cache(oracle_mod, d=d, n_sink=ns, units=2, vfmt=1, vclip=0.92)
+        x = rng.standard_normal((2, T, d)).astype(np.float32)
+        v = rng.standard_normal((2, T, d)).astype(np.float32)
+        oc.append(x[:, :17], v[:, :17])
+        oc.append(x[:, 17:], v[:, 17:])
+        for u in range(2):
+            kh, vh = oc.dequant(u)
+            kr, vr = fr.decode_unit(oc, u, T)
+            np.testing.assert_array_equal(kh, kr)
+            np.testing.assert_array_equal(vh, vr)
+            rmse = np.sqrt(np.mean((vh[ns:] - v[u, ns:]) ** 2))
+            assert rmse < 0.6  # INT2 over ~[-2.4, 2.4]: step ~1.6, rms error ~0.45
+            np.testing.assert_array_equal(vh[:ns], fr.bf16(oc.sink_v[u, :ns]))
