@@ -18,6 +18,7 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY = 0, -1, -2, -3
 KVQ_ERR_WORKSPACE, KVQ_ERR_ALIGN, KVQ_ERR_HIP = -4, -5, -6
 KVQ_F32, KVQ_BF16 = 0, 1
 K_ASYM2, K_ASYM4, K_LLOYD4 = 0, 1, 2
+V_ASYM4_G32, V_ASYM2_TOKEN = 0, 1
 BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", "sink_v",
              "codebook", "thresholds"]
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
@@ -29,7 +30,8 @@ EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_w
 class KvqCacheC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink",
                                               "k_format", "k_hadamard", "k_ch0_bf16", "len")] + \
-               [(n, ctypes.c_void_p) for n in BUF_NAMES]
+               [(n, ctypes.c_void_p) for n in BUF_NAMES] + \
+               [("v_format", ctypes.c_int32), ("v_clip", ctypes.c_float)]
 
 
 class KvqError(RuntimeError):
@@ -135,9 +137,11 @@ class Cache:
     """A quantized KV cache whose buffers are torch device tensors (zero-initialised)."""
 
     def __init__(self, batch, n_kv_heads, head_dim, capacity, n_sink=0, k_format=K_ASYM2,
-                 k_hadamard=0, k_ch0_bf16=0, device="cuda"):
+                 k_hadamard=0, k_ch0_bf16=0, device="cuda", v_format=V_ASYM4_G32, v_clip=1.0):
         self.c = KvqCacheC(batch, n_kv_heads, head_dim, capacity, n_sink, k_format, k_hadamard,
                            k_ch0_bf16, 0)
+        self.c.v_format = int(v_format)
+        self.c.v_clip = float(v_clip)
         self.device = torch.device(device)
         self.buffers = {}
         for i, name in enumerate(BUF_NAMES):

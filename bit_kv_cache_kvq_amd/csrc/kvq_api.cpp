@@ -46,6 +46,10 @@ kvq_status check_geometry(const kvq_cache *c)
         return KVQ_ERR_ARG;
     if (c->k_ch0_bf16 && (c->k_hadamard || c->k_format == KVQ_K_LLOYD4))
         return KVQ_ERR_UNSUPPORTED;
+    if (c->v_format != KVQ_V_ASYM4_G32 && c->v_format != KVQ_V_ASYM2_TOKEN)
+        return KVQ_ERR_ARG;
+    if (c->v_format == KVQ_V_ASYM2_TOKEN && !(c->v_clip > 0.0f && c->v_clip <= 1.0f))
+        return KVQ_ERR_ARG;
     if (c->len > c->capacity)
         return KVQ_ERR_CAPACITY;
     return KVQ_OK;
@@ -63,8 +67,8 @@ size_t buffer_bytes(const kvq_cache *c, int which)
     case KVQ_BUF_K_SZ: return lloyd ? 0 : U * (d / 32) * cap * 4;
     case KVQ_BUF_K_NORM: return lloyd ? U * cap * 2 : 0;
     case KVQ_BUF_K_CH0: return c->k_ch0_bf16 ? U * cap * 2 : 0;
-    case KVQ_BUF_V_CODES: return U * (cap / 2) * (d / 4) * 4;
-    case KVQ_BUF_V_SZ: return U * (d / 32) * cap * 4;
+    case KVQ_BUF_V_CODES: return U * (cap / 2) * (c->v_format == KVQ_V_ASYM2_TOKEN ? d / 8 : d / 4) * 4;
+    case KVQ_BUF_V_SZ: return U * (c->v_format == KVQ_V_ASYM2_TOKEN ? 1 : d / 32) * cap * 4;
     case KVQ_BUF_SINK_K:
     case KVQ_BUF_SINK_V: return U * ns * d * 2;
     case KVQ_BUF_CODEBOOK: return lloyd ? 16 * 4 : 0;
@@ -197,6 +201,8 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
     p.kfmt = c->k_format;
     p.rotate = c->k_hadamard;
     p.ch0 = c->k_ch0_bf16;
+    p.vfmt = c->v_format;
+    p.vclip = c->v_clip;
     p.in_bf16 = dtype == KVQ_BF16;
     if (launch_append(c->head_dim, p, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
@@ -237,7 +243,7 @@ int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
     const int G = n_q_heads / c->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return 0;
-    return plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format)).n_waves;
+    return plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format, c->v_format)).n_waves;
 }
 
 kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
@@ -264,7 +270,7 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     if (!aligned16(ws))
         return KVQ_ERR_ALIGN;
 
-    const Plan pl = plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format));
+    const Plan pl = plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format, c->v_format));
     const size_t U = units_of(c);
     DecodeParams p;
     p.k_codes = c->k_codes;
@@ -300,7 +306,7 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
     if (!ev[0] || !ev[1])
         ev[0] = ev[1] = nullptr;
-    if (launch_decode(c->head_dim, G, c->k_format, (int)U, p, ev, (hipStream_t)stream) != hipSuccess)
+    if (launch_decode(c->head_dim, G, c->k_format, c->v_format, (int)U, p, ev, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
     return KVQ_OK;
 }

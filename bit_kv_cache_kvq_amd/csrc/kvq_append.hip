@@ -11,7 +11,8 @@
 //   across lanes, norm from the stride-halving tree of squares (an xor butterfly gives
 //   the same sums bit for bit because fp32 addition commutes), fp16 norm, codes by
 //   threshold count;
-//   values: asymmetric INT4 per 32-channel group;
+//   values: asymmetric INT4 per 32-channel group, or per-token asymmetric INT2 whose range
+//   is clipped to [c*min, c*max] (Dual-QK sec. B.2: per-token INT2 values, clipping ratio);
 //   positions below n_sink: BF16 keys and values (TurboQuant on Quantized Models, abstract).
 // Work per appended token is O(head_dim) and touches only that token's slots
 // (TurboQuant on Quantized Models, abstract: incremental cache).
@@ -204,6 +205,48 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
         const int rows = D * kbits / 32;
         if ((lane % lanes) == 0)
             p.k_codes[((size_t)u * (size_t)rows + (size_t)(lane / lanes)) * cap + (size_t)t] = word;
+    }
+
+    // ---- values, per-token INT2: range [c*min, c*max] over the whole token, codes against
+    // the fp16 scale and zero, 8 channels per 16-bit half of a token-pair word
+    if (p.vfmt == KVQ_V_ASYM2_TOKEN) {
+        float mn = v[0], mx = v[0];
+#pragma unroll
+        for (int s = 1; s < CPL; s++) {
+            mn = fminf(mn, v[s]);
+            mx = fmaxf(mx, v[s]);
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, m));
+            mx = fmaxf(mx, __shfl_xor(mx, m));
+        }
+        mn = p.vclip * mn + 0.0f;
+        mx = p.vclip * mx;
+        const float range = (mx - mn) + 0.0f;
+        const float scale32 = range / 3.0f;
+        const uint32_t sh = f32_to_f16(scale32);
+        const uint32_t zh = f32_to_f16(mn);
+        const float sf = f16_to_f32(sh);
+        const float zf = f16_to_f32(zh);
+        const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+        uint32_t vc[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++) {
+            const float diff = v[s] - zf;
+            const float uu = diff * inv;
+            const float r = fminf(fmaxf(__builtin_rintf(uu), 0.0f), 3.0f);
+            vc[s] = (uint32_t)r;
+        }
+        if (lane == 0)
+            p.v_sz[(size_t)u * cap + (size_t)t] = sh | (zh << 16);
+        const int lanes = 16 / (2 * CPL); // lanes forming one 16-bit half (8 channels)
+        const uint32_t half = pack_run<CPL>(vc, 2, lanes, lane);
+        if ((lane % lanes) == 0) {
+            const size_t word = ((size_t)u * (cap / 2) + (size_t)(t >> 1)) * (D / 8) + (size_t)(lane / lanes);
+            reinterpret_cast<uint16_t *>(p.v_codes)[word * 2 + (size_t)(t & 1)] = (uint16_t)half;
+        }
+        return;
     }
 
     // ---- values: asymmetric INT4, token-pair interleaved words

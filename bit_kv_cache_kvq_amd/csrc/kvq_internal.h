@@ -27,7 +27,8 @@ struct AppendParams {
     uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
     const float *thresholds;
     const void *k_new, *v_new;
-    int units, n_new, cap, len, n_sink, kfmt, rotate, ch0, in_bf16;
+    int units, n_new, cap, len, n_sink, kfmt, rotate, ch0, vfmt, in_bf16;
+    float vclip; // per-token INT2 values: clipping ratio
 };
 
 struct DecodeParams {
@@ -51,14 +52,18 @@ struct DecodeParams {
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
 // ev[0], ev[1]: optional events recorded around the decode kernel (both non-null or unused)
-hipError_t launch_decode(int head_dim, int group, int kfmt, int units, const DecodeParams &p, hipEvent_t const ev[2],
-                         hipStream_t s);
+hipError_t launch_decode(int head_dim, int group, int kfmt, int vfmt, int units, const DecodeParams &p,
+                         hipEvent_t const ev[2], hipStream_t s);
+// the per-token INT2 value instantiations (compiled apart): launch, and the kernel of a shape
+hipError_t launch_decode_v2(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
+                            hipEvent_t const ev[2], hipStream_t s);
+const void *decode_kernel_v2(int head_dim, int group, int kfmt);
 // Streaming-read probe over `bytes` (a multiple of 16) at p; out holds `blocks` words.
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *out, int blocks, hipStream_t s);
 // u32 words of one unit's query record (query-prep output read by the decode kernel).
 int decode_qrec_words(int head_dim, int group, int kfmt);
 // Resident decode workgroups (one wave each) the device holds for this instantiation.
-int decode_slots(int head_dim, int group, int kfmt);
+int decode_slots(int head_dim, int group, int kfmt, int vfmt);
 // Compute units of the current device (256 when the runtime cannot be asked).
 int device_cus();
 

@@ -12,7 +12,9 @@
  *     TurboQuant: scheme KQV and the Beta -> Gaussian marginal).
  *   - Keys stored channel-major so decode reads only the channel rows it keeps
  *     (Dual-QK sec. 3.3).
- *   - Values: asymmetric INT4, FP16 scale and zero per 32-channel group.
+ *   - Values: asymmetric INT4 with an FP16 scale and zero per 32-channel group, or
+ *     per-token asymmetric INT2 with a clipping ratio and one FP16 scale and zero per token
+ *     (Dual-QK sec. 3.3 and B.2: per-token INT2 values with a 0.92 clipping ratio).
  *   - The first n_sink positions of every sequence are stored in BF16 (TurboQuant on
  *     Quantized Models, abstract: sink-token preservation; Dual-QK sec. 3.3 / 4.1).
  *   - Decode scores queries straight against the packed codes (TurboQuant on Quantized
@@ -39,10 +41,14 @@
  *   k_norm   u16 [U][capacity]     Lloyd-Max keys: fp16 norm rho (RMS of the stored
  *                                  coordinates; equals ||k|| when rotated).
  *   k_ch0    u16 [U][capacity]     protected channel 0: bf16.
- *   v_codes  u32 [U][capacity/2][head_dim/4]  word j of token pair P holds channels
- *                                  4j..4j+3: token 2P in bits 0-15, token 2P+1 in bits
- *                                  16-31, channel 4j+k at nibble k of its half.
- *   v_sz     u32 [U][head_dim/32][capacity]  values: fp16 scale | fp16 zero << 16.
+ *   v_codes  u32 [U][capacity/2][head_dim/4]  INT4 values: word j of token pair P holds
+ *                                  channels 4j..4j+3: token 2P in bits 0-15, token 2P+1 in
+ *                                  bits 16-31, channel 4j+k at nibble k of its half.
+ *            u32 [U][capacity/2][head_dim/8]  per-token INT2 values: word j of pair P holds
+ *                                  channels 8j..8j+7, token 2P in bits 0-15, token 2P+1 in
+ *                                  bits 16-31, channel 8j+k at bits [2k, 2k+1] of its half.
+ *   v_sz     u32 [U][head_dim/32][capacity]  INT4 values: fp16 scale | fp16 zero << 16 per
+ *                                  group; per-token INT2 values: [U][1][capacity].
  *   sink_k   u16 [U][n_sink][head_dim]  bf16 keys of positions < n_sink, in stored
  *                                  coordinates (rotated when k_hadamard = 1).
  *   sink_v   u16 [U][n_sink][head_dim]  bf16 values of positions < n_sink.
@@ -58,6 +64,9 @@
  *   Lloyd-Max: y = FWHT(k) (unnormalised, stages h = 1, 2, 4, ... writing (a+b, a-b)) when
  *   rotated, else y = k; rho = fp16(sqrt(tree_sum(y*y) / d)) with the stride-halving
  *   tree; z = y * (rho > 0 ? 1/rho : 0).
+ *   per-token INT2 values: the range is clipped to [c*min, c*max] (c = v_clip, both ends
+ *   scaled toward zero), scale = fp16((c*max - c*min) / 3), zero = fp16(c*min), codes as
+ *   for the asymmetric groups (entries outside the clipped range saturate at 0 or 3).
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -83,12 +92,15 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
 typedef enum { KVQ_K_ASYM2 = 0, KVQ_K_ASYM4 = 1, KVQ_K_LLOYD4 = 2 } kvq_kfmt;
 
+typedef enum { KVQ_V_ASYM4_G32 = 0, KVQ_V_ASYM2_TOKEN = 1 } kvq_vfmt;
+
 /* Cache descriptor.  Geometry and format fields are set once by the caller; `len` is the
  * number of positions stored per sequence (uniform across sequences) and is advanced by
  * kvq_quant_append.  Constraints: head_dim in {64, 128}; capacity a positive multiple of
  * 256 and at most 2^24; batch * n_kv_heads <= 65535; 0 <= n_sink <= 64 and n_sink < capacity; k_hadamard and k_ch0_bf16 in {0, 1};
- * k_ch0_bf16 requires an asymmetric key format and k_hadamard = 0.  Pointers unused by
- * the chosen format may be NULL (see kvq_buffer_bytes).                                 */
+ * k_ch0_bf16 requires an asymmetric key format and k_hadamard = 0; v_format is a
+ * kvq_vfmt, and v_clip (per-token INT2 values only, otherwise ignored) lies in (0, 1].
+ * Pointers unused by the chosen format may be NULL (see kvq_buffer_bytes).              */
 typedef struct kvq_cache {
     int32_t batch, n_kv_heads, head_dim, capacity, n_sink;
     int32_t k_format, k_hadamard, k_ch0_bf16;
@@ -103,6 +115,8 @@ typedef struct kvq_cache {
     uint16_t *sink_v;
     const float *codebook;
     const float *thresholds;
+    int32_t v_format;
+    float v_clip;
 } kvq_cache;
 
 enum {

@@ -29,11 +29,13 @@ def _inputs(seed, Bsz, Hkv, T, d, dist="normal", dtype=torch.bfloat16, outliers=
 
 
 def _run(oracle_mod, *, d=128, kfmt=0, rot=0, ch0=0, ns=0, T=300, G=4, Hkv=2, Bsz=2, keep=0,
-         dtype=torch.bfloat16, chunks=None, dist="normal", seed=0, cap=None, q_scale=1.0, outliers=()):
+         dtype=torch.bfloat16, chunks=None, dist="normal", seed=0, cap=None, q_scale=1.0, outliers=(),
+         vfmt=0, vclip=0.92):
     cap = cap or max(256, (T + 255) // 256 * 256)
     note(f"case d={d} kfmt={kfmt} rot={rot} ch0={ch0} ns={ns} T={T} G={G} Hkv={Hkv} B={Bsz} keep={keep} "
-         f"dtype={dtype} chunks={chunks} dist={dist}")
-    c = B.Cache(Bsz, Hkv, d, cap, n_sink=ns, k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0)
+         f"dtype={dtype} chunks={chunks} dist={dist} vfmt={vfmt} vclip={vclip}")
+    c = B.Cache(Bsz, Hkv, d, cap, n_sink=ns, k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0,
+                v_format=vfmt, v_clip=vclip)
     oc = oracle_geo(oracle_mod, c)
     k, v = _inputs(seed, Bsz, Hkv, T, d, dist, dtype, outliers)
     chunks = chunks or [T]
@@ -214,3 +216,30 @@ def test_decode_event_hook(oracle_mod):
     note(f"  decode kernel {kern * 1e3:.1f} us of a {call * 1e3:.1f} us call")
     assert 0 < kern <= call
     assert torch.equal(out, out0)
+
+
+# per-token INT2 values with a clipping ratio (Dual-QK sec. B.2)
+@pytest.mark.parametrize("d,kfmt,rot,ch0,G,keep,ns,T,vclip", [
+    (128, 0, 0, 1, 4, 5, 4, 300, 0.92),
+    (128, 0, 0, 0, 4, 0, 0, 1, 0.92),
+    (128, 0, 0, 1, 4, 0, 64, 1000, 0.92),
+    (128, 2, 1, 0, 4, 3, 0, 257, 0.92),
+    (128, 1, 0, 0, 8, 0, 2, 129, 1.0),
+    (128, 0, 0, 0, 1, 0, 0, 65, 0.5),
+    (64, 0, 0, 1, 2, 2, 3, 255, 0.92),
+    (64, 2, 0, 0, 8, 0, 0, 384, 0.92),
+])
+def test_token_int2_values(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, vclip):
+    _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, keep=keep, ns=ns, T=T, vfmt=1, vclip=vclip,
+         chunks=[T // 3, T - T // 3] if T > 3 else None)
+
+
+def test_token_int2_values_teams_and_heavy_tails(oracle_mod):
+    """Long context on few units (wave teams, striped), Student-t3 values, across calls."""
+    _run(oracle_mod, d=128, kfmt=0, ch0=1, G=4, keep=5, ns=4, T=9000, Hkv=1, Bsz=1, dist="t3", vfmt=1)
+    for tps in (1, 3):
+        B.set_split_tiles(tps)
+        try:
+            _run(oracle_mod, d=128, kfmt=0, G=4, T=4000, Hkv=2, Bsz=1, vfmt=1, seed=3)
+        finally:
+            B.set_split_tiles(0)
