@@ -18,7 +18,7 @@ The default warm-up (128 steps, ~35 ms) lets the GPU reach its steady clocks fir
   cpu_baseline    the CPU oracle timed on a bounded sample of the same workload
 Inputs are resident in HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..6]
 """
 from __future__ import annotations
 
@@ -57,7 +57,7 @@ def decode_bytes_unit(w, length, mask):
         k_tok += 4 * sum(1 for g in range(d // 32) if kept[2 * g] or kept[2 * g + 1])
         if w.k_ch0_bf16 and kept[0]:
             k_tok += 2
-    v_tok = d // 2 + 4 * (d // 32)
+    v_tok = d // 4 + 4 if w.v_format == 1 else d // 2 + 4 * (d // 32)
     return quant * (k_tok + v_tok) + ns * d * 2 * 2
 
 
@@ -150,7 +150,7 @@ def cpu_baseline(w, length, budget_s):
     nseq = max(1, math.ceil(threads / H))
     geo = oracle.Geometry(batch=nseq, n_kv_heads=H, head_dim=w.head_dim, capacity=w.capacity(512),
                           n_sink=w.n_sink, k_format=w.k_format, k_hadamard=w.k_hadamard,
-                          k_ch0_bf16=w.k_ch0_bf16)
+                          k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip)
     oc = oracle.OracleCache(geo)
     prefill_len = length - (1 if w.steps else 0)
     k, v = synth.prefill(w, device="cpu", context=prefill_len, batch=nseq)
@@ -201,7 +201,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=128)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -270,7 +270,8 @@ def main():
     appends = args.warmup + 2 * args.steps if w.steps else 0
     cap = w.capacity(appends)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
-                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, device=dev)
+                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, device=dev, v_format=w.v_format,
+                v_clip=w.v_clip)
     log(f"workload {w.name}: capacity {cap}, building cache ...")
     k, v = synth.prefill(w, device=dev)
     c.append(k, v)
@@ -365,7 +366,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.context, "positions_attended_last_step": lens[-1],
                    "key_format": ["asym_int2", "asym_int4", "wht_lloyd4"][w.k_format],
-                   "value_format": "asym_int4_g32", "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink,
+                   "value_format": "asym_int2_token_clip%.2f" % w.v_clip if w.v_format == 1 else "asym_int4_g32",
+                   "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink,
                    "keep_groups": w.keep_groups, "appends_per_step": 1 if w.steps else 0,
                    "parallelism": "single GPU"},
         "effective_GBps": eff_gbps,

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     // BF16 sink rows, SB at a time (the last row repeated past n_sink); the first batch of
     // keys and values is loaded here, with the query, so its latency overlaps the query's
     const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
-    constexpr int SB = 8; // sinks per batch of loads
+    constexpr int SB = 32; // sinks per batch of loads: 64 sinks cost two rounds of latency
     auto load_sinks = [&](const uint16_t *base, int t0, float (&dst)[SB][CPL]) {
 #pragma unroll
         for (int j = 0; j < SB; j++) {

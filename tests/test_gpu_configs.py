@@ -1,4 +1,4 @@
-"""GPU parity on the five decode workloads at their full sizes, in the launch
+"""GPU parity on the six decode workloads at their full sizes, in the launch
 configuration the bench times.
 
 The whole cache is built on the GPU; the oracle re-encodes sampled sequences and must match
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 def _build(w, extra=0):
     cap = w.capacity(extra)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
-                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16)
+                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip)
     k, v = synth.prefill(w, device="cuda")
     note(f"workload {w.name}: prefill {tuple(k.shape)} {k.dtype}, capacity {cap}")
     c.append(k, v)
@@ -82,6 +82,15 @@ def test_workload4_pruned_128k(oracle_mod):
     ref = [oracle_mod.prune_mask(qn[u], w.keep_groups) for u in range(w.units)]
     np.testing.assert_array_equal(mask.cpu().numpy(), np.array(ref, np.uint8))
     assert all(bin(int(m)).count("1") == w.keep_groups for m in ref)
+
+
+def test_workload6_dualqk_storage_128k(oracle_mod):
+    """Dual-QK's storage recipe on the 128K shape: 64 BF16 sinks, per-token INT2 values
+    clipped to 0.92, INT2 keys with channel 0 in BF16, 5 of 8 groups kept."""
+    w = synth.WORKLOADS[6]
+    c, k, v = _build(w)
+    ocs = _oracle_for(oracle_mod, c, w, k, v, [0, w.batch - 1])
+    _check_decode(c, w, ocs, synth.query(w, 0, device="cuda"), "cfg6")
 
 
 def test_workload5_append_decode_steps(oracle_mod):
