@@ -33,7 +33,15 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b64_t16k_traffic.txt")
-DECODE_SRC = os.path.join(ROOT, "bit_kv_cache_kvq_amd", "csrc", "kvq_decode.hip")
+# the decode kernels' sources (kernel templates and the INT4-value instantiation the counters see)
+DECODE_SRC = [os.path.join(ROOT, "bit_kv_cache_kvq_amd", "csrc", f) for f in ("kvq_decode_impl.h", "kvq_decode.hip")]
+
+
+def decode_source_sha256():
+    h = hashlib.sha256()
+    for f in DECODE_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -71,7 +79,7 @@ def traffic_record():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    sha = decode_source_sha256()
     if kv.get("decode_source_sha256") != sha:
         return None
     try:
@@ -107,12 +115,13 @@ def write_traffic(dec_fetch, dec_write, copy_fetch, copy_write, out_path, copy_b
     cf_kib, cw_kib = sum(cf) / len(cf), sum(cw) / len(cw)
     ff, wf = copy_bytes / (cf_kib * 1024), copy_bytes / (cw_kib * 1024)
     hbm = fetch_kib * 1024 * ff + write_kib * 1024 * wf
-    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    sha = decode_source_sha256()
     lines = [
         "# HBM traffic of one decode_kernel launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE counters",
         "# (KiB per dispatch, each counter in its own run), scaled by the same counters on a copy of",
-        f"# {copy_bytes} bytes (python bench.py --copy-probe).  Valid only for the decode source whose",
-        "# sha256 is recorded below: bench.py ignores this file once the kernel changes.",
+        f"# {copy_bytes} bytes (python bench.py --copy-probe).  Valid only for the decode sources",
+        "# (kvq_decode_impl.h, then kvq_decode.hip) whose sha256 is recorded below: bench.py ignores",
+        "# this file once the kernel changes.",
         "# commands (from /tmp with TMPDIR=/tmp; each counter in a run of its own):",
         "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex decode_kernel --output-format csv -d F -o decF"
         " -- python3 <repo>/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
