@@ -194,7 +194,7 @@ __device__ __forceinline__ std::conditional_t<ONE, uint32_t, uint2> vload(rsrc_t
 // One workgroup per unit, one wave per query head of the GQA group: stored-coordinate query
 // (FWHT when keys are rotated), 16-channel group energies (fp32 stride-halving tree, the
 // order the format fixes), the group's mask, and the head's query operands and sink state.
-template <int D, int G, int KF>
+template <int D, int G, int KF, int SB>
 __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
 {
     using C = Cfg<D, G, KF>;
@@ -215,9 +215,9 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     float *recf = reinterpret_cast<float *>(rec);
 
     // BF16 sink rows, SB at a time (the last row repeated past n_sink); the first batch of
-    // keys and values is loaded here, with the query, so its latency overlaps the query's
+    // keys and values is loaded here, with the query, so its latency overlaps the query's.
+    // SB is 8, or 32 for more than 8 sinks (64 sinks then cost two rounds of latency).
     const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
-    constexpr int SB = 32; // sinks per batch of loads: 64 sinks cost two rounds of latency
     auto load_sinks = [&](const uint16_t *base, int t0, float (&dst)[SB][CPL]) {
 #pragma unroll
         for (int j = 0; j < SB; j++) {
@@ -1309,7 +1309,10 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 template <int D, int G, int KF, int VF>
 hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
-    hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
+    if (p.n_sink > 8)
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 32>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
+    else
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 8>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
