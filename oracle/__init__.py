@@ -72,7 +72,7 @@ def lib():
         L.oracle_tree_sum_f32.argtypes = [P, i]
         L.oracle_lloyd_max_gaussian.restype = i
         L.oracle_lloyd_max_gaussian.argtypes = [i, ctypes.c_double, i, P, P]
-        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, P, P, P, P, P, P, P, P]
+        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, i, P, P, P, P, P, P, P, P, P, P]
         L.oracle_quant_append.argtypes = cache_args + [P, P, i, i, i, P, P]
         L.oracle_prune_mask.restype = ctypes.c_uint32
         L.oracle_prune_mask.argtypes = [P, i, i, i]
@@ -168,6 +168,7 @@ class Geometry:
     k_ch0_bf16: int = 0
     v_format: int = V_ASYM4_G32
     v_clip: float = 1.0
+    n_recent: int = 0
 
     @property
     def units(self) -> int:
@@ -197,6 +198,9 @@ class OracleCache:
         self.v_sz = np.zeros((U, 1 if per_token else d // 32, cap), dtype=np.uint32)
         self.sink_k = np.zeros((U, ns, d), dtype=np.uint16)
         self.sink_v = np.zeros((U, ns, d), dtype=np.uint16)
+        nr = max(geo.n_recent, 1)
+        self.recent_k = np.zeros((U, nr, d), dtype=np.uint16)
+        self.recent_v = np.zeros((U, nr, d), dtype=np.uint16)
         self.len = 0
         if geo.k_format == K_LLOYD4:
             self.cent, self.thr = codebook_f32(16)
@@ -207,8 +211,9 @@ class OracleCache:
     def _cache_args(self):
         g = self.geo
         return [g.head_dim, g.capacity, g.n_sink, g.k_format, g.k_hadamard, g.k_ch0_bf16,
-                g.v_format, float(g.v_clip), _p(self.k_codes), _p(self.k_sz), _p(self.k_norm), _p(self.k_ch0),
-                _p(self.v_codes), _p(self.v_sz), _p(self.sink_k), _p(self.sink_v)]
+                g.v_format, float(g.v_clip), g.n_recent, _p(self.k_codes), _p(self.k_sz), _p(self.k_norm),
+                _p(self.k_ch0), _p(self.v_codes), _p(self.v_sz), _p(self.sink_k), _p(self.sink_v),
+                _p(self.recent_k), _p(self.recent_v)]
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):
         """k_new, v_new: fp32 [U, n_new, d]; writes positions [len, len+n_new)."""

@@ -18,6 +18,10 @@
  *        Beta -> Gaussian marginal that makes an N(0,1) codebook the right one);
  *   - BF16 sink tokens (TurboQuant on Quantized Models, abstract: sink-token preservation;
  *     Dual-QK sec. 3.3 / 4.1: first tokens kept in BF16);
+ *   - a window of the most recent positions kept in BF16 and quantized only when they leave
+ *     it (Dual-QK sec. 3.3 / 4.1: the most recent 256 entries stay BF16; TurboQuant on
+ *     Quantized Models, abstract: past-only quantization, the current token attends
+ *     unquantized);
  *   - dynamic query-channel-group pruning with one mask per GQA group, ranked by
  *     query energy summed over the group's heads (Dual-QK sec. 3.2, sec. C.2, App. A);
  *   - values as asymmetric INT4 per 32-channel group, or as per-token asymmetric INT2
@@ -269,13 +273,19 @@ int oracle_lloyd_max_gaussian(int levels, double tol, int max_iter, double *cent
  *                                 for per-token values
  *   sink_k  u16 [U][n_sink][d]    bf16 key in stored coordinates (rotated if rotation on)
  *   sink_v  u16 [U][n_sink][d]    bf16 value
- * Slots t < n_sink of the quantised arrays are never written.                           */
+ *   recent_k u16 [U][W][d]        recent window (W = n_recent > 0): ring slot t mod W holds
+ *   recent_v u16 [U][W][d]        the bf16 key (stored coordinates) / value of position t
+ *                                 while t is among the W most recent positions >= n_sink
+ * Slots t < n_sink of the quantised arrays are never written, nor are those of positions
+ * still in the recent window.                                                            */
 typedef struct {
     int d, cap, n_sink, kfmt, rotate, ch0, vfmt;
     float vclip; /* per-token INT2 values: clipping ratio */
+    int n_recent; /* W: most recent positions kept in BF16 (0: none) */
     uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
-    uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
+    uint16_t *k_norm, *k_ch0, *sink_k, *sink_v, *recent_k, *recent_v;
     const float *cent, *thr; /* Lloyd-Max: 16 centroids, 15 thresholds (fp32) */
+    int len; /* positions stored (decode: where the recent window starts) */
 } ocache;
 
 static size_t krows(const ocache *c) { return (size_t)(c->d * key_bits(c->kfmt) / 32); }
@@ -366,29 +376,12 @@ static void asym_token_clip(const float *x, int n, float clip, uint8_t *code, ui
     *zh_out = zh;
 }
 
-/* Quantise and store one token (K and V) at absolute position t of unit u.
- * k and v are d fp32 values each.                                                        */
-static void quant_token(const ocache *c, size_t u, int t, const float *k, const float *v)
+/* Quantise and store the key y (stored coordinates: already rotated when rotation is on)
+ * and the value v of position t of unit u; d fp32 values each.                          */
+static void quant_stored(const ocache *c, size_t u, int t, const float *y, const float *v)
 {
     const int d = c->d;
     const size_t cap = (size_t)c->cap;
-    float y[256];
-    memcpy(y, k, sizeof(float) * (size_t)d);
-    if (c->rotate)
-        oracle_fwht_f32(y, d);
-
-    if (t < c->n_sink) {
-        /* Sink token: BF16 key (in stored coordinates) and BF16 value.
-         * (TurboQuant on Quantized Models: sink-token preservation.)                    */
-        uint16_t *sk = c->sink_k + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
-        uint16_t *sv = c->sink_v + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
-        for (int i = 0; i < d; i++) {
-            sk[i] = oracle_f32_to_bf16(y[i]);
-            sv[i] = oracle_f32_to_bf16(v[i]);
-        }
-        return;
-    }
-
     uint8_t code[256];
     const int kb = key_bits(c->kfmt);
     if (c->kfmt == OK_LLOYD4) {
@@ -466,16 +459,66 @@ static void quant_token(const ocache *c, size_t u, int t, const float *k, const 
     }
 }
 
+/* Store one token (K and V) at absolute position t of unit u; k and v are d fp32 values.
+ * The key goes to stored coordinates first (FWHT when rotation is on).  Positions below
+ * n_sink are kept in BF16.  Without a recent window every other position is quantised at
+ * once.  With a window of W positions (reading of Dual-QK sec. 3.3 / 4.1 and of past-only
+ * quantization), a position enters ring slot t mod W as BF16 and is quantised only when the
+ * position t + W takes its slot, from that BF16 copy -- so with a window the codes of a
+ * position never depend on how the appends were cut.                                    */
+static void quant_token(const ocache *c, size_t u, int t, const float *k, const float *v)
+{
+    const int d = c->d;
+    float y[256];
+    memcpy(y, k, sizeof(float) * (size_t)d);
+    if (c->rotate)
+        oracle_fwht_f32(y, d);
+
+    if (t < c->n_sink) {
+        /* Sink token: BF16 key (in stored coordinates) and BF16 value.
+         * (TurboQuant on Quantized Models: sink-token preservation.)                    */
+        uint16_t *sk = c->sink_k + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
+        uint16_t *sv = c->sink_v + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
+        for (int i = 0; i < d; i++) {
+            sk[i] = oracle_f32_to_bf16(y[i]);
+            sv[i] = oracle_f32_to_bf16(v[i]);
+        }
+        return;
+    }
+    if (c->n_recent == 0) {
+        quant_stored(c, u, t, y, v);
+        return;
+    }
+    const size_t W = (size_t)c->n_recent;
+    uint16_t *rk = c->recent_k + (u * W + (size_t)t % W) * (size_t)d;
+    uint16_t *rv = c->recent_v + (u * W + (size_t)t % W) * (size_t)d;
+    if (t - (int)W >= c->n_sink) {
+        /* position t - W leaves the window: quantise its BF16 copy */
+        float ok[256], ov[256];
+        for (int i = 0; i < d; i++) {
+            ok[i] = oracle_bf16_to_f32(rk[i]);
+            ov[i] = oracle_bf16_to_f32(rv[i]);
+        }
+        quant_stored(c, u, t - (int)W, ok, ov);
+    }
+    for (int i = 0; i < d; i++) {
+        rk[i] = oracle_f32_to_bf16(y[i]);
+        rv[i] = oracle_f32_to_bf16(v[i]);
+    }
+}
+
 /* Append n_new tokens per unit at positions [t0, t0+n_new) for units [0, n_units).
  * k_new, v_new: fp32 [n_units][n_new][d].  OpenMP over units.                            */
 void oracle_quant_append(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
+                         int n_recent,
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
+                         uint16_t *recent_k, uint16_t *recent_v,
                          const float *cent, const float *thr, int n_units, int t0, int n_new,
                          const float *k_new, const float *v_new)
 {
-    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, cent, thr};
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, thr, t0 + n_new};
 #pragma omp parallel for schedule(static)
     for (int u = 0; u < n_units; u++)
         for (int i = 0; i < n_new; i++) {
@@ -526,6 +569,12 @@ uint32_t oracle_prune_mask(const float *qt, int G, int d, int m)
 /* ------------------------------------------------------------------------------------ */
 /* Decoding of stored tokens into fp64 (stored coordinates).                             */
 
+/* Position t (< len) is still in the recent window: held in BF16 in ring slot t mod W. */
+static int in_window(const ocache *c, int t)
+{
+    return c->n_recent > 0 && t >= c->n_sink && t >= c->len - c->n_recent;
+}
+
 static void decode_key(const ocache *c, size_t u, int t, double *kh)
 {
     const int d = c->d;
@@ -534,6 +583,13 @@ static void decode_key(const ocache *c, size_t u, int t, double *kh)
         const uint16_t *sk = c->sink_k + (u * (size_t)c->n_sink + (size_t)t) * (size_t)d;
         for (int i = 0; i < d; i++)
             kh[i] = (double)oracle_bf16_to_f32(sk[i]);
+        return;
+    }
+    if (in_window(c, t)) {
+        const size_t W = (size_t)c->n_recent;
+        const uint16_t *rk = c->recent_k + (u * W + (size_t)t % W) * (size_t)d;
+        for (int i = 0; i < d; i++)
+            kh[i] = (double)oracle_bf16_to_f32(rk[i]);
         return;
     }
     const int kb = key_bits(c->kfmt);
@@ -573,6 +629,13 @@ static void decode_value(const ocache *c, size_t u, int t, double *vh)
             vh[i] = (double)oracle_bf16_to_f32(sv[i]);
         return;
     }
+    if (in_window(c, t)) {
+        const size_t W = (size_t)c->n_recent;
+        const uint16_t *rv = c->recent_v + (u * W + (size_t)t % W) * (size_t)d;
+        for (int i = 0; i < d; i++)
+            vh[i] = (double)oracle_bf16_to_f32(rv[i]);
+        return;
+    }
     const int sh16 = (t & 1) ? 16 : 0;
     if (c->vfmt == OV_ASYM2_TOKEN) {
         const uint32_t *row2 = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * (size_t)(d / 8);
@@ -601,12 +664,14 @@ static void decode_value(const ocache *c, size_t u, int t, double *vh)
 
 /* Decoded cache of one unit, for tests: keys in stored coordinates, values. [len][d]. */
 void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
+                         int n_recent,
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
+                         uint16_t *recent_k, uint16_t *recent_v,
                          const float *cent, int unit, int len, double *kh, double *vh)
 {
-    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, cent, 0};
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len};
     for (int t = 0; t < len; t++) {
         decode_key(&c, (size_t)unit, t, kh + (size_t)t * (size_t)d);
         decode_value(&c, (size_t)unit, t, vh + (size_t)t * (size_t)d);
@@ -625,14 +690,16 @@ void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int c
  * written to mask_out[u] when mask_out is not null.  logits_out (nullable) receives the
  * fp64 logits [n_units][G][len].                                                         */
 void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
+                         int n_recent,
                         uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                         uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
+                         uint16_t *recent_k, uint16_t *recent_v,
                         const float *cent, int n_units, int len, int G, const float *q,
                         double sm, int keep_groups, double *out, uint8_t *mask_out,
                         double *logits_out)
 {
-    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, cent, 0};
+    ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len};
 #pragma omp parallel for schedule(dynamic, 1)
     for (int u = 0; u < n_units; u++) {
         const float *qu = q + (size_t)u * (size_t)G * (size_t)d;

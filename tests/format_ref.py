@@ -14,6 +14,8 @@ Format (per unit, absolute token positions):
   Per-token INT2 values (value format 1): word j of token pair P = v_codes[P, j] holds
   channels 8j..8j+7, token 2P in the low 16 bits and 2P+1 in the high 16 bits, channel
   8j+k at bits [2k, 2k+1] of its half; v_sz[0, t] holds the token's fp16 scale and zero.
+  Recent window of W positions: positions t >= max(n_sink, len - W) are read as BF16 from
+  ring slot t mod W of recent_k / recent_v (keys in stored coordinates).
 """
 import numpy as np
 
@@ -89,4 +91,9 @@ def decode_unit(oc, u, len_):
     if n:
         kh[:n] = bf16(oc.sink_k[u, :n])
         vh[:n] = bf16(oc.sink_v[u, :n])
+    W = getattr(g, "n_recent", 0)
+    if W:
+        for t in range(max(ns, len_ - W), len_):
+            kh[t] = bf16(oc.recent_k[u, t % W])
+            vh[t] = bf16(oc.recent_v[u, t % W])
     return kh, vh

@@ -14,9 +14,10 @@ import pytest
 import format_ref as fr
 
 
-def _geo(oracle_mod, d, cap=512, kfmt=0, rot=0, ch0=0, ns=0, units=1, vfmt=0, vclip=1.0):
+def _geo(oracle_mod, d, cap=512, kfmt=0, rot=0, ch0=0, ns=0, units=1, vfmt=0, vclip=1.0, nr=0):
     return oracle_mod.Geometry(batch=units, n_kv_heads=1, head_dim=d, capacity=cap, n_sink=ns,
-                               k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0, v_format=vfmt, v_clip=vclip)
+                               k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0, v_format=vfmt, v_clip=vclip,
+                               n_recent=nr)
 
 
 def _brute(oracle_mod, oc, q, sm, keep):
@@ -56,14 +57,16 @@ CASES = [
     (128, 0, 0, 1, 3, 9, 4, 5, 1),
     (64, 1, 0, 0, 0, 7, 2, 0, 1),
 ]
+# recent BF16 window cases: (d, kfmt, rot, ch0, n_sink, T, G, keep, value format, window)
+WCASES = [(128, 0, 0, 1, 2, 9, 4, 5, 0, 3), (64, 2, 1, 0, 0, 8, 2, 0, 1, 1), (128, 1, 0, 0, 1, 6, 4, 0, 0, 16)]
 
 
-@pytest.mark.parametrize("d,kfmt,rot,ch0,ns,T,G,keep,vfmt", CASES)
-def test_oracle_equals_bruteforce(oracle_mod, d, kfmt, rot, ch0, ns, T, G, keep, vfmt):
+@pytest.mark.parametrize("d,kfmt,rot,ch0,ns,T,G,keep,vfmt,nr", [c + (0,) for c in CASES] + WCASES)
+def test_oracle_equals_bruteforce(oracle_mod, d, kfmt, rot, ch0, ns, T, G, keep, vfmt, nr):
     rng = np.random.default_rng(d + 10 * kfmt + T)
     U = 2
     oc = oracle_mod.OracleCache(_geo(oracle_mod, d, kfmt=kfmt, rot=rot, ch0=ch0, ns=ns, units=U,
-                                     vfmt=vfmt, vclip=0.92))
+                                     vfmt=vfmt, vclip=0.92, nr=nr))
     k = (rng.standard_normal((U, T, d)) * 2).astype(np.float32)
     v = rng.standard_normal((U, T, d)).astype(np.float32)
     oc.append(k, v)
