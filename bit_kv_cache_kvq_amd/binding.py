@@ -20,7 +20,7 @@ KVQ_F32, KVQ_BF16 = 0, 1
 K_ASYM2, K_ASYM4, K_LLOYD4 = 0, 1, 2
 V_ASYM4_G32, V_ASYM2_TOKEN = 0, 1
 BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", "sink_v",
-             "codebook", "thresholds"]
+             "codebook", "thresholds", "recent_k", "recent_v"]  # KVQ_BUF_* order
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles", "kvq_set_deterministic",
            "kvq_set_decode_events", "kvq_probe_stream_read",
@@ -30,8 +30,9 @@ EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_w
 class KvqCacheC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink",
                                               "k_format", "k_hadamard", "k_ch0_bf16", "len")] + \
-               [(n, ctypes.c_void_p) for n in BUF_NAMES] + \
-               [("v_format", ctypes.c_int32), ("v_clip", ctypes.c_float)]
+               [(n, ctypes.c_void_p) for n in BUF_NAMES[:10]] + \
+               [("v_format", ctypes.c_int32), ("v_clip", ctypes.c_float), ("n_recent", ctypes.c_int32)] + \
+               [(n, ctypes.c_void_p) for n in BUF_NAMES[10:]]
 
 
 class KvqError(RuntimeError):
@@ -137,11 +138,12 @@ class Cache:
     """A quantized KV cache whose buffers are torch device tensors (zero-initialised)."""
 
     def __init__(self, batch, n_kv_heads, head_dim, capacity, n_sink=0, k_format=K_ASYM2,
-                 k_hadamard=0, k_ch0_bf16=0, device="cuda", v_format=V_ASYM4_G32, v_clip=1.0):
+                 k_hadamard=0, k_ch0_bf16=0, device="cuda", v_format=V_ASYM4_G32, v_clip=1.0, n_recent=0):
         self.c = KvqCacheC(batch, n_kv_heads, head_dim, capacity, n_sink, k_format, k_hadamard,
                            k_ch0_bf16, 0)
         self.c.v_format = int(v_format)
         self.c.v_clip = float(v_clip)
+        self.c.n_recent = int(n_recent)
         self.device = torch.device(device)
         self.buffers = {}
         for i, name in enumerate(BUF_NAMES):

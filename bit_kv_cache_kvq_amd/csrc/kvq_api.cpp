@@ -50,12 +50,24 @@ kvq_status check_geometry(const kvq_cache *c)
         return KVQ_ERR_ARG;
     if (c->v_format == KVQ_V_ASYM2_TOKEN && !(c->v_clip > 0.0f && c->v_clip <= 1.0f))
         return KVQ_ERR_ARG;
+    if (c->n_recent < 0 || c->n_recent > kMaxRecent)
+        return KVQ_ERR_UNSUPPORTED;
     if (c->len > c->capacity)
         return KVQ_ERR_CAPACITY;
     return KVQ_OK;
 }
 
 size_t units_of(const kvq_cache *c) { return (size_t)c->batch * (size_t)c->n_kv_heads; }
+
+// End of the quantised positions [n_sink, q_end) when len positions are stored: with a
+// recent window of W positions, the W most recent ones (>= n_sink) are still in BF16.
+int quant_end(const kvq_cache *c, int len)
+{
+    if (c->n_recent <= 0)
+        return len;
+    const int e = len - c->n_recent;
+    return e > c->n_sink ? e : c->n_sink;
+}
 
 size_t buffer_bytes(const kvq_cache *c, int which)
 {
@@ -73,15 +85,18 @@ size_t buffer_bytes(const kvq_cache *c, int which)
     case KVQ_BUF_SINK_V: return U * ns * d * 2;
     case KVQ_BUF_CODEBOOK: return lloyd ? 16 * 4 : 0;
     case KVQ_BUF_THRESHOLDS: return lloyd ? 15 * 4 : 0;
+    case KVQ_BUF_RECENT_K:
+    case KVQ_BUF_RECENT_V: return U * (size_t)c->n_recent * d * 2;
     default: return 0;
     }
 }
 
 kvq_status check_buffers(const kvq_cache *c)
 {
-    const void *ptrs[10] = {c->k_codes, c->k_sz, c->k_norm, c->k_ch0, c->v_codes,
-                            c->v_sz, c->sink_k, c->sink_v, c->codebook, c->thresholds};
-    for (int i = 0; i < 10; i++) {
+    const void *ptrs[12] = {c->k_codes, c->k_sz,     c->k_norm,     c->k_ch0,
+                            c->v_codes, c->v_sz,     c->sink_k,     c->sink_v,
+                            c->codebook, c->thresholds, c->recent_k, c->recent_v};
+    for (int i = 0; i < 12; i++) {
         if (buffer_bytes(c, i) == 0)
             continue;
         if (!ptrs[i])
@@ -190,6 +205,8 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
     p.k_ch0 = c->k_ch0;
     p.sink_k = c->sink_k;
     p.sink_v = c->sink_v;
+    p.recent_k = c->recent_k;
+    p.recent_v = c->recent_v;
     p.thresholds = c->thresholds;
     p.k_new = k_new;
     p.v_new = v_new;
@@ -204,6 +221,22 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
     p.vfmt = c->v_format;
     p.vclip = c->v_clip;
     p.in_bf16 = dtype == KVQ_BF16;
+    p.n_recent = c->n_recent;
+    p.q_end = quant_end(c, c->len + n_new);
+    p.evict = 0;
+    p.e0 = 0;
+    // recent window: first quantise the ring positions that leave it (their slots are
+    // overwritten by the new positions of the second launch)
+    const int q_old = quant_end(c, c->len);
+    const int ev_end = p.q_end < c->len ? p.q_end : c->len;
+    if (c->n_recent > 0 && ev_end > q_old) {
+        AppendParams e = p;
+        e.evict = 1;
+        e.e0 = q_old;
+        e.n_new = ev_end - q_old;
+        if (launch_append(c->head_dim, e, (hipStream_t)stream) != hipSuccess)
+            return KVQ_ERR_HIP;
+    }
     if (launch_append(c->head_dim, p, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
     c->len += n_new;
@@ -243,7 +276,7 @@ int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
     const int G = n_q_heads / c->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return 0;
-    return plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format, c->v_format)).n_waves;
+    return plan_splits(c, quant_end(c, c->len), decode_slots(c->head_dim, G, c->k_format, c->v_format)).n_waves;
 }
 
 kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
@@ -270,7 +303,7 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     if (!aligned16(ws))
         return KVQ_ERR_ALIGN;
 
-    const Plan pl = plan_splits(c, c->len, decode_slots(c->head_dim, G, c->k_format, c->v_format));
+    const Plan pl = plan_splits(c, quant_end(c, c->len), decode_slots(c->head_dim, G, c->k_format, c->v_format));
     const size_t U = units_of(c);
     DecodeParams p;
     p.k_codes = c->k_codes;
@@ -281,6 +314,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.k_ch0 = c->k_ch0;
     p.sink_k = c->sink_k;
     p.sink_v = c->sink_v;
+    p.recent_k = c->recent_k;
+    p.recent_v = c->recent_v;
     p.codebook = c->codebook;
     p.q = q;
     p.out = out;
@@ -293,6 +328,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.cap = c->capacity;
     p.len = c->len;
     p.n_sink = c->n_sink;
+    p.n_recent = c->n_recent;
+    p.q_end = quant_end(c, c->len);
     p.rotate = c->k_hadamard;
     p.ch0 = c->k_ch0_bf16;
     p.keep = keep_groups;

@@ -13,7 +13,10 @@
 //   threshold count;
 //   values: asymmetric INT4 per 32-channel group, or per-token asymmetric INT2 whose range
 //   is clipped to [c*min, c*max] (Dual-QK sec. B.2: per-token INT2 values, clipping ratio);
-//   positions below n_sink: BF16 keys and values (TurboQuant on Quantized Models, abstract).
+//   positions below n_sink: BF16 keys and values (TurboQuant on Quantized Models, abstract);
+//   with a recent window of W positions (Dual-QK sec. 3.3 / 4.1; past-only quantization),
+//   new positions go to ring slot t mod W in BF16 and are quantised from that copy when they
+//   leave the window (a first launch with `evict` set does those of earlier appends).
 // Work per appended token is O(head_dim) and touches only that token's slots
 // (TurboQuant on Quantized Models, abstract: incremental cache).
 #include "kvq_device.h"
@@ -137,24 +140,52 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
         return;
     const int u = (int)(wave / p.n_new);
     const int i = (int)(wave % p.n_new);
-    const int t = p.len + i;
     const size_t cap = (size_t)p.cap;
-    const size_t in_off = ((size_t)u * (size_t)p.n_new + (size_t)i) * D + (size_t)lane * CPL;
+    const size_t W = (size_t)p.n_recent;
 
-    float k[CPL], v[CPL];
-    load_row<CPL>(p.k_new, in_off, p.in_bf16, k);
-    load_row<CPL>(p.v_new, in_off, p.in_bf16, v);
-    if (p.rotate)
-        fwht<CPL>(k, lane);
+    float k[CPL], v[CPL]; // the key in stored coordinates, the value
+    int t;
+    if (p.evict) {
+        // position t leaves the recent window: quantise its BF16 copy from the ring
+        t = p.e0 + i;
+        const size_t ro = ((size_t)u * W + (size_t)t % W) * D + (size_t)lane * CPL;
+        load_row<CPL>(p.recent_k, ro, 1, k);
+        load_row<CPL>(p.recent_v, ro, 1, v);
+    } else {
+        t = p.len + i;
+        const size_t in_off = ((size_t)u * (size_t)p.n_new + (size_t)i) * D + (size_t)lane * CPL;
+        load_row<CPL>(p.k_new, in_off, p.in_bf16, k);
+        load_row<CPL>(p.v_new, in_off, p.in_bf16, v);
+        if (p.rotate)
+            fwht<CPL>(k, lane);
 
-    if (t < p.n_sink) {
-        const size_t so = ((size_t)u * (size_t)p.n_sink + (size_t)t) * D + (size_t)lane * CPL;
+        if (t < p.n_sink) {
+            const size_t so = ((size_t)u * (size_t)p.n_sink + (size_t)t) * D + (size_t)lane * CPL;
 #pragma unroll
-        for (int s = 0; s < CPL; s++) {
-            p.sink_k[so + s] = (uint16_t)f32_to_bf16(k[s]);
-            p.sink_v[so + s] = (uint16_t)f32_to_bf16(v[s]);
+            for (int s = 0; s < CPL; s++) {
+                p.sink_k[so + s] = (uint16_t)f32_to_bf16(k[s]);
+                p.sink_v[so + s] = (uint16_t)f32_to_bf16(v[s]);
+            }
+            return;
         }
-        return;
+        if (W > 0) {
+            if (t >= p.q_end) {
+                // still among the W most recent positions: into its ring slot, in BF16
+                const size_t ro = ((size_t)u * W + (size_t)t % W) * D + (size_t)lane * CPL;
+#pragma unroll
+                for (int s = 0; s < CPL; s++) {
+                    p.recent_k[ro + s] = (uint16_t)f32_to_bf16(k[s]);
+                    p.recent_v[ro + s] = (uint16_t)f32_to_bf16(v[s]);
+                }
+                return;
+            }
+            // already W behind the new end: quantised from the BF16 copy it would have had
+#pragma unroll
+            for (int s = 0; s < CPL; s++) {
+                k[s] = bf16_to_f32(f32_to_bf16(k[s]));
+                v[s] = bf16_to_f32(f32_to_bf16(v[s]));
+            }
+        }
     }
 
     // ---- keys

@@ -352,10 +352,6 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine - m) : 0.0f;
         sp[h][lane] = pr;
         const float l = wave_sum_dpp(pr);
-        if (lane == 0) {
-            recf[C::OFF_SINK + h * (D + 2)] = m;
-            recf[C::OFF_SINK + h * (D + 2) + 1] = l;
-        }
         __syncthreads();
         float o[CPL];
 #pragma unroll
@@ -372,6 +368,64 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
                 for (int s = 0; s < CPL; s++)
                     o[s] = fmaf(sp[h][t0 + j], vv[j][s], o[s]);
             }
+        }
+        // recent BF16 window, positions [wlo, len) in ring slots t mod W (Dual-QK sec. 3.3 /
+        // 4.1): 64 positions at a time, lane j scoring position wlo + c0 + j over all
+        // channels from its ring row, folded into the state (m, l, o) online
+        float M = m, L = l;
+        const int wlo = p.q_end > n_sink ? p.q_end : n_sink;
+        const int n_win = p.len - wlo;
+        for (int c0 = 0; c0 < n_win; c0 += kWave) {
+            const int nc = n_win - c0 < kWave ? n_win - c0 : kWave; // positions in this chunk
+            const bool valid = lane < nc;
+            const int tk = wlo + c0 + (valid ? lane : 0);
+            const uint16_t *krow = p.recent_k + ((size_t)unit * p.n_recent + (size_t)(tk % p.n_recent)) * D;
+            float dot = 0.0f;
+#pragma unroll
+            for (int c = 0; c < D; c += 8) {
+                const uint4 kw = *reinterpret_cast<const uint4 *>(krow + c);
+                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    dot = fmaf(sq_[h][c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dot);
+                    dot = fmaf(sq_[h][c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dot);
+                }
+            }
+            const float lw = valid ? dot : -__builtin_inff();
+            const float Mn = fmaxf(M, wave_max_dpp(lw)); // finite: the chunk has a position
+            const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+            const float pw = valid ? __builtin_amdgcn_exp2f(lw - Mn) : 0.0f;
+            L = fmaf(L, fo, wave_sum_dpp(pw));
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                o[s] *= fo;
+            // values, 32 positions per batch of loads (rows past the chunk repeat its last
+            // position with weight 0); lane owns channels lane*CPL ..
+#pragma unroll
+            for (int b0 = 0; b0 < kWave; b0 += 32) {
+                float vw[32][CPL];
+#pragma unroll
+                for (int jj = 0; jj < 32; jj++) {
+                    const int tv = wlo + c0 + (b0 + jj < nc ? b0 + jj : nc - 1);
+                    const uint16_t *vrow =
+                        p.recent_v + ((size_t)unit * p.n_recent + (size_t)(tv % p.n_recent)) * D + lane * CPL;
+#pragma unroll
+                    for (int s = 0; s < CPL; s++)
+                        vw[jj][s] = bf16_to_f32(vrow[s]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 32; jj++) {
+                    const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), b0 + jj));
+#pragma unroll
+                    for (int s = 0; s < CPL; s++)
+                        o[s] = fmaf(pj, vw[jj][s], o[s]);
+                }
+            }
+            M = Mn;
+        }
+        if (lane == 0) {
+            recf[C::OFF_SINK + h * (D + 2)] = M;
+            recf[C::OFF_SINK + h * (D + 2) + 1] = L;
         }
 #pragma unroll
         for (int s = 0; s < CPL; s++)
@@ -884,7 +938,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const int vs = lane % LPP;         // value slot: channels 8*vs .. 8*vs+7
     const int vgrp = V2 ? 0 : vs / 4;  // its scale group
     const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u; // value word offset
-    const int q_lo = p.n_sink, q_hi = p.len; // quantized positions [q_lo, q_hi)
+    const int q_lo = p.n_sink, q_hi = p.q_end; // quantized positions [q_lo, q_hi)
 
     // ---- the unit's query scalars (uniform loads from its record)
     const uint32_t *__restrict__ rec = qrec + (size_t)u * C::QREC;

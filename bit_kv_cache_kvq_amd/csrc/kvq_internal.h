@@ -19,21 +19,27 @@ constexpr int kMaxWaves = 16384;
 // Cache capacity granule (public contract: capacity is a multiple of 256 positions).
 constexpr int kCapacityQuantum = 256;
 constexpr int kMaxSink = 64;
+// Largest recent BF16 window (positions per sequence).
+constexpr int kMaxRecent = 1024;
 // Largest capacity (positions per sequence): keeps every per-unit slab under 1 GiB.
 constexpr int kMaxCapacity = 1 << 24;
 
 struct AppendParams {
     uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
-    uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
+    uint16_t *k_norm, *k_ch0, *sink_k, *sink_v, *recent_k, *recent_v;
     const float *thresholds;
     const void *k_new, *v_new;
     int units, n_new, cap, len, n_sink, kfmt, rotate, ch0, vfmt, in_bf16;
-    float vclip; // per-token INT2 values: clipping ratio
+    float vclip;  // per-token INT2 values: clipping ratio
+    int n_recent; // recent BF16 window W (0: none)
+    int q_end;    // positions below q_end (and >= n_sink) end up quantised by this append
+    int evict;    // 1: quantise ring positions [len - ..., ) leaving the window (see the kernel)
+    int e0;       // evict: first position to quantise; n_new positions from there
 };
 
 struct DecodeParams {
     const uint32_t *k_codes, *k_sz, *v_codes, *v_sz;
-    const uint16_t *k_norm, *k_ch0, *sink_k, *sink_v;
+    const uint16_t *k_norm, *k_ch0, *sink_k, *sink_v, *recent_k, *recent_v;
     const float *codebook;
     const void *q;
     float *out;
@@ -44,6 +50,8 @@ struct DecodeParams {
                         // done [n_waves]; then per unit: members / stripes done [units]; zeroed by
                         // the query-prep kernel
     int n_kv_heads, cap, len, n_sink, rotate, ch0, keep, q_bf16;
+    int n_recent;       // recent BF16 window W (0: none)
+    int q_end;          // quantised positions are [n_sink, q_end); [max(n_sink, q_end), len) is the window
     float sm_log2e;      // softmax scale times log2(e)
     int n_units, tiles_per_unit, n_waves; // work split: n_waves >= n_units waves, wave w serves unit w % n_units
     int dynamic;        // 1: tiles from the unit counters; 0: member k of n takes k, k + n, ...

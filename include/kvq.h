@@ -16,7 +16,10 @@
  *     per-token asymmetric INT2 with a clipping ratio and one FP16 scale and zero per token
  *     (Dual-QK sec. 3.3 and B.2: per-token INT2 values with a 0.92 clipping ratio).
  *   - The first n_sink positions of every sequence are stored in BF16 (TurboQuant on
- *     Quantized Models, abstract: sink-token preservation; Dual-QK sec. 3.3 / 4.1).
+ *     Quantized Models, abstract: sink-token preservation; Dual-QK sec. 3.3 / 4.1), and
+ *     optionally the n_recent most recent ones too, quantized only when they leave that
+ *     window (Dual-QK sec. 3.3 / 4.1: the most recent 256 entries stay BF16; TurboQuant on
+ *     Quantized Models, abstract: past-only quantization).
  *   - Decode scores queries straight against the packed codes (TurboQuant on Quantized
  *     Models, abstract: fused scoring without key decompression), with optional dynamic
  *     query-channel-group pruning: one mask per GQA group keeping the m 16-channel groups
@@ -52,10 +55,17 @@
  *   sink_k   u16 [U][n_sink][head_dim]  bf16 keys of positions < n_sink, in stored
  *                                  coordinates (rotated when k_hadamard = 1).
  *   sink_v   u16 [U][n_sink][head_dim]  bf16 values of positions < n_sink.
+ *   recent_k u16 [U][n_recent][head_dim]  recent window (n_recent = W > 0): ring slot t mod
+ *   recent_v u16 [U][n_recent][head_dim]  W holds the bf16 key (stored coordinates) / value
+ *                                  of position t while t is one of the W most recent
+ *                                  positions >= n_sink.
  *   codebook f32 [16], thresholds f32 [15]  Lloyd-Max keys: centroids ascending and the
  *                                  decision thresholds; a rotated coordinate z codes to the
  *                                  number of thresholds strictly below z.
- * Quantized arrays are never written or read at positions t < n_sink.
+ * Quantized arrays are never written or read at positions t < n_sink, nor at positions still
+ * in the recent window; with a window, a position is quantized from its bf16 copy (keys in
+ * stored coordinates) when it leaves the window, so its codes do not depend on how the
+ * appends were cut.
  * Encoding arithmetic is fixed (fp32, IEEE round-to-nearest-even, no contraction) so the
  * packed bytes are reproducible bit for bit:
  *   asym b-bit group: scale = fp16((max - min) / (2^b - 1)), zero = fp16(min), with
@@ -99,7 +109,8 @@ typedef enum { KVQ_V_ASYM4_G32 = 0, KVQ_V_ASYM2_TOKEN = 1 } kvq_vfmt;
  * kvq_quant_append.  Constraints: head_dim in {64, 128}; capacity a positive multiple of
  * 256 and at most 2^24; batch * n_kv_heads <= 65535; 0 <= n_sink <= 64 and n_sink < capacity; k_hadamard and k_ch0_bf16 in {0, 1};
  * k_ch0_bf16 requires an asymmetric key format and k_hadamard = 0; v_format is a
- * kvq_vfmt, and v_clip (per-token INT2 values only, otherwise ignored) lies in (0, 1].
+ * kvq_vfmt, and v_clip (per-token INT2 values only, otherwise ignored) lies in (0, 1];
+ * 0 <= n_recent <= 1024.
  * Pointers unused by the chosen format may be NULL (see kvq_buffer_bytes).              */
 typedef struct kvq_cache {
     int32_t batch, n_kv_heads, head_dim, capacity, n_sink;
@@ -117,6 +128,9 @@ typedef struct kvq_cache {
     const float *thresholds;
     int32_t v_format;
     float v_clip;
+    int32_t n_recent;
+    uint16_t *recent_k;
+    uint16_t *recent_v;
 } kvq_cache;
 
 enum {
@@ -129,7 +143,9 @@ enum {
     KVQ_BUF_SINK_K = 6,
     KVQ_BUF_SINK_V = 7,
     KVQ_BUF_CODEBOOK = 8,
-    KVQ_BUF_THRESHOLDS = 9
+    KVQ_BUF_THRESHOLDS = 9,
+    KVQ_BUF_RECENT_K = 10,
+    KVQ_BUF_RECENT_V = 11
 };
 
 /* Bytes the caller must allocate for buffer `which` (KVQ_BUF_*) of this geometry; 0 when
@@ -144,9 +160,12 @@ kvq_status kvq_validate(const kvq_cache *c);
  * ([batch][n_kv_heads][n_new][head_dim], dtype KVQ_F32 or KVQ_BF16, row-major, device)
  * into positions [len, len + n_new), then set len += n_new.  Only those positions are
  * written (O(1) work per appended token; TurboQuant on Quantized Models, abstract:
- * incremental cache).  Positions below n_sink go to sink_k / sink_v in BF16.  Inputs must
- * be finite with |x| < 65504 so the fp16 parameters stay finite; other inputs give
- * unspecified codes.  n_new = 0 is a no-op.                                               */
+ * incremental cache).  Positions below n_sink go to sink_k / sink_v in BF16.  With a
+ * recent window, new positions go to the ring in BF16 and the positions leaving the window
+ * (old ones, and new ones already W behind the new end) are quantized from their BF16
+ * copies; this takes two kernel launches, eviction first.  Inputs must be finite with
+ * |x| < 65504 so the fp16 parameters stay finite; other inputs give unspecified codes.
+ * n_new = 0 is a no-op.                                                                   */
 kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, int32_t dtype,
                             int32_t n_new, void *stream);
 

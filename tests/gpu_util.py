@@ -19,7 +19,7 @@ def oracle_geo(oracle_mod, c: B.Cache, units=None):
     g = oracle_mod.Geometry(batch=c.c.batch, n_kv_heads=c.c.n_kv_heads, head_dim=c.c.head_dim,
                             capacity=c.c.capacity, n_sink=c.c.n_sink, k_format=c.c.k_format,
                             k_hadamard=c.c.k_hadamard, k_ch0_bf16=c.c.k_ch0_bf16,
-                            v_format=c.c.v_format, v_clip=float(c.c.v_clip))
+                            v_format=c.c.v_format, v_clip=float(c.c.v_clip), n_recent=c.c.n_recent)
     return oracle_mod.OracleCache(g, units=units)
 
 
@@ -32,9 +32,10 @@ def gpu_arrays(c: B.Cache, u0=0, u1=None):
     v2 = c.c.v_format == B.V_ASYM2_TOKEN
     shapes = {"k_codes": (R, cap), "k_sz": (d // 32, cap), "k_norm": (cap,), "k_ch0": (cap,),
               "v_codes": (cap // 2, d // 8 if v2 else d // 4), "v_sz": (1 if v2 else d // 32, cap),
-              "sink_k": (ns, d), "sink_v": (ns, d)}
+              "sink_k": (ns, d), "sink_v": (ns, d), "recent_k": (c.c.n_recent, d), "recent_v": (c.c.n_recent, d)}
     dts = {"k_codes": torch.int32, "k_sz": torch.int32, "k_norm": torch.int16, "k_ch0": torch.int16,
-           "v_codes": torch.int32, "v_sz": torch.int32, "sink_k": torch.int16, "sink_v": torch.int16}
+           "v_codes": torch.int32, "v_sz": torch.int32, "sink_k": torch.int16, "sink_v": torch.int16,
+           "recent_k": torch.int16, "recent_v": torch.int16}
     out = {}
     for name, shp in shapes.items():
         if name not in c.buffers:

@@ -30,10 +30,11 @@ def test_exports_every_declared_function():
 
 def _cache(**kw):
     c = dict(batch=2, n_kv_heads=3, head_dim=128, capacity=512, n_sink=0, k_format=0, k_hadamard=0,
-             k_ch0_bf16=0, len=0)
+             k_ch0_bf16=0, len=0, v_format=0, v_clip=1.0, n_recent=0)
     c.update(kw)
     s = B.KvqCacheC(*[c[k] for k in ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink", "k_format",
                                       "k_hadamard", "k_ch0_bf16", "len")])
+    s.v_format, s.v_clip, s.n_recent = c["v_format"], c["v_clip"], c["n_recent"]
     for name in B.BUF_NAMES:
         setattr(s, name, FAKE)
     return s
@@ -50,6 +51,12 @@ def test_buffer_bytes_follow_layout():
     nb = [L.kvq_buffer_bytes(ctypes.byref(s), i) for i in range(10)]
     assert nb == [U * 8 * cap * 4, 0, U * cap * 2, 0, U * cap // 2 * 16 * 4, U * 2 * cap * 4, 0, 0, 64, 60]
     assert L.kvq_buffer_bytes(ctypes.byref(_cache(head_dim=96)), 0) == 0
+    # per-token INT2 values: d/8 words per pair, one scale/zero row; recent window rings
+    s = _cache(v_format=1, v_clip=0.92, n_recent=256)
+    nb = [L.kvq_buffer_bytes(ctypes.byref(s), i) for i in range(12)]
+    assert nb[4:6] == [U * cap // 2 * 16 * 4, U * cap * 4]
+    assert nb[10:] == [U * 256 * d * 2, U * 256 * d * 2]
+    assert L.kvq_buffer_bytes(ctypes.byref(_cache()), 10) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -63,6 +70,11 @@ def test_buffer_bytes_follow_layout():
     (dict(len=513), B.KVQ_ERR_CAPACITY),
     (dict(batch=70000), B.KVQ_ERR_UNSUPPORTED),
     (dict(capacity=(1 << 24) + 256), B.KVQ_ERR_UNSUPPORTED),
+    (dict(v_format=2), B.KVQ_ERR_ARG),
+    (dict(v_format=1, v_clip=0.0), B.KVQ_ERR_ARG),
+    (dict(v_format=1, v_clip=1.5), B.KVQ_ERR_ARG),
+    (dict(n_recent=-1), B.KVQ_ERR_UNSUPPORTED),
+    (dict(n_recent=1025), B.KVQ_ERR_UNSUPPORTED),
 ])
 def test_validate_rejects(kw, code):
     assert B.lib().kvq_validate(ctypes.byref(_cache(**kw))) == code

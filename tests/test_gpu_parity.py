@@ -30,12 +30,12 @@ def _inputs(seed, Bsz, Hkv, T, d, dist="normal", dtype=torch.bfloat16, outliers=
 
 def _run(oracle_mod, *, d=128, kfmt=0, rot=0, ch0=0, ns=0, T=300, G=4, Hkv=2, Bsz=2, keep=0,
          dtype=torch.bfloat16, chunks=None, dist="normal", seed=0, cap=None, q_scale=1.0, outliers=(),
-         vfmt=0, vclip=0.92):
+         vfmt=0, vclip=0.92, nr=0):
     cap = cap or max(256, (T + 255) // 256 * 256)
     note(f"case d={d} kfmt={kfmt} rot={rot} ch0={ch0} ns={ns} T={T} G={G} Hkv={Hkv} B={Bsz} keep={keep} "
-         f"dtype={dtype} chunks={chunks} dist={dist} vfmt={vfmt} vclip={vclip}")
+         f"dtype={dtype} chunks={chunks} dist={dist} vfmt={vfmt} vclip={vclip} nr={nr}")
     c = B.Cache(Bsz, Hkv, d, cap, n_sink=ns, k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0,
-                v_format=vfmt, v_clip=vclip)
+                v_format=vfmt, v_clip=vclip, n_recent=nr)
     oc = oracle_geo(oracle_mod, c)
     k, v = _inputs(seed, Bsz, Hkv, T, d, dist, dtype, outliers)
     chunks = chunks or [T]
@@ -243,3 +243,25 @@ def test_token_int2_values_teams_and_heavy_tails(oracle_mod):
             _run(oracle_mod, d=128, kfmt=0, G=4, T=4000, Hkv=2, Bsz=1, vfmt=1, seed=3)
         finally:
             B.set_split_tiles(0)
+
+
+# recent BF16 window (Dual-QK sec. 3.3 / 4.1; past-only quantization)
+@pytest.mark.parametrize("d,kfmt,rot,ch0,G,keep,ns,T,nr,vfmt,chunks", [
+    (128, 0, 0, 1, 4, 5, 64, 1000, 256, 1, [300, 1, 699]),
+    (128, 0, 0, 0, 4, 0, 0, 300, 1, 0, [299, 1]),
+    (128, 0, 0, 1, 4, 0, 4, 10, 16, 0, [3, 7]),
+    (128, 1, 0, 0, 4, 0, 2, 1000, 100, 0, None),
+    (128, 2, 1, 0, 4, 3, 0, 700, 256, 1, [200, 500]),
+    (64, 0, 0, 1, 8, 2, 3, 333, 64, 0, [100, 233]),
+    (64, 2, 0, 0, 2, 0, 0, 130, 130, 1, [60, 70]),
+])
+def test_recent_window(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, nr, vfmt, chunks):
+    _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, keep=keep, ns=ns, T=T, nr=nr, vfmt=vfmt,
+         chunks=chunks, dtype=torch.float32 if d == 64 else torch.bfloat16)
+
+
+def test_recent_window_single_token_steps(oracle_mod):
+    """One append per step (the decode-time pattern): every step evicts the oldest window
+    position; decoded after the last step, and with teams drawing tiles."""
+    _run(oracle_mod, d=128, kfmt=0, G=4, ns=4, T=2100, nr=256, Hkv=1, Bsz=2, chunks=[2000] + [1] * 100,
+         dist="t3", vfmt=1)
