@@ -48,15 +48,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes_unit(w, length, mask):
+def decode_bytes_unit(w, length, mask, bf16=True):
     """Algorithmic HBM bytes one decode reads for one (sequence, KV head): the code words,
     scale/zero words and channel-0 / norm halves of the kept key rows, every value word and
-    value scale/zero word, and the BF16 sink rows.  mask: kept 16-channel groups (bit p)."""
+    value scale/zero word of the quantised positions, and (bf16=True) the BF16 rows of the
+    sinks and of the recent window, which the query-prep kernel reads rather than the main
+    decode kernel.  mask: kept 16-channel groups (bit p)."""
     d = w.head_dim
     P = d // 16
     kept = [(mask >> p) & 1 for p in range(P)]
     ns = min(w.n_sink, length)
-    quant = length - ns
+    nr = max(0, min(w.n_recent, length - ns))  # recent positions still in BF16
+    quant = length - ns - nr
     kbits = 2 if w.k_format == 0 else 4
     k_tok = sum(kept) * 16 * kbits // 8
     if w.k_format == 2:
@@ -66,7 +69,7 @@ def decode_bytes_unit(w, length, mask):
         if w.k_ch0_bf16 and kept[0]:
             k_tok += 2
     v_tok = d // 4 + 4 if w.v_format == 1 else d // 2 + 4 * (d // 32)
-    return quant * (k_tok + v_tok) + ns * d * 2 * 2
+    return quant * (k_tok + v_tok) + ((ns + nr) * d * 2 * 2 if bf16 else 0)
 
 
 def traffic_record():
@@ -159,7 +162,7 @@ def cpu_baseline(w, length, budget_s):
     nseq = max(1, math.ceil(threads / H))
     geo = oracle.Geometry(batch=nseq, n_kv_heads=H, head_dim=w.head_dim, capacity=w.capacity(512),
                           n_sink=w.n_sink, k_format=w.k_format, k_hadamard=w.k_hadamard,
-                          k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip)
+                          k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip, n_recent=w.n_recent)
     oc = oracle.OracleCache(geo)
     prefill_len = length - (1 if w.steps else 0)
     k, v = synth.prefill(w, device="cpu", context=prefill_len, batch=nseq)
@@ -280,7 +283,7 @@ def main():
     cap = w.capacity(appends)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
                 k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, device=dev, v_format=w.v_format,
-                v_clip=w.v_clip)
+                v_clip=w.v_clip, n_recent=w.n_recent)
     log(f"workload {w.name}: capacity {cap}, building cache ...")
     k, v = synth.prefill(w, device=dev)
     c.append(k, v)
@@ -342,7 +345,7 @@ def main():
     masks = mask.cpu().tolist() if w.keep_groups else [full] * w.units
     bytes_per = [sum(decode_bytes_unit(w, L, m) for m in masks) for L in lens]
     # algorithmic bytes of the launches the events timed
-    bytes_ev = [sum(decode_bytes_unit(w, L, m) for m in masks) for L in lens_ev]
+    bytes_ev = [sum(decode_bytes_unit(w, L, m, bf16=False) for m in masks) for L in lens_ev]
     avg_bytes = sum(bytes_ev) / len(bytes_ev)
     tokens = sum(w.batch * L for L in lens)
     value = tokens / elapsed
@@ -376,7 +379,7 @@ def main():
                    "head_dim": w.head_dim, "context": w.context, "positions_attended_last_step": lens[-1],
                    "key_format": ["asym_int2", "asym_int4", "wht_lloyd4"][w.k_format],
                    "value_format": "asym_int2_token_clip%.2f" % w.v_clip if w.v_format == 1 else "asym_int4_g32",
-                   "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink,
+                   "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink, "recent_bf16_tokens": w.n_recent,
                    "keep_groups": w.keep_groups, "appends_per_step": 1 if w.steps else 0,
                    "parallelism": "single GPU"},
         "effective_GBps": eff_gbps,

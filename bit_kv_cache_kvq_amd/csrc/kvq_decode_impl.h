@@ -378,8 +378,14 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         for (int c0 = 0; c0 < n_win; c0 += kWave) {
             const int nc = n_win - c0 < kWave ? n_win - c0 : kWave; // positions in this chunk
             const bool valid = lane < nc;
-            const int tk = wlo + c0 + (valid ? lane : 0);
-            const uint16_t *krow = p.recent_k + ((size_t)unit * p.n_recent + (size_t)(tk % p.n_recent)) * D;
+            // ring slot of the chunk's position j: slot0 + j, wrapped once at most (the window
+            // holds at most W positions); positions past the chunk repeat its last one
+            const int slot0 = (wlo + c0) % p.n_recent;
+            auto slot = [&](int j) {
+                const int sl = slot0 + (j < nc ? j : nc - 1);
+                return sl >= p.n_recent ? sl - p.n_recent : sl;
+            };
+            const uint16_t *krow = p.recent_k + ((size_t)unit * p.n_recent + (size_t)slot(lane)) * D;
             float dot = 0.0f;
 #pragma unroll
             for (int c = 0; c < D; c += 8) {
@@ -406,9 +412,8 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
                 float vw[32][CPL];
 #pragma unroll
                 for (int jj = 0; jj < 32; jj++) {
-                    const int tv = wlo + c0 + (b0 + jj < nc ? b0 + jj : nc - 1);
                     const uint16_t *vrow =
-                        p.recent_v + ((size_t)unit * p.n_recent + (size_t)(tv % p.n_recent)) * D + lane * CPL;
+                        p.recent_v + ((size_t)unit * p.n_recent + (size_t)slot(b0 + jj)) * D + lane * CPL;
 #pragma unroll
                     for (int s = 0; s < CPL; s++)
                         vw[jj][s] = bf16_to_f32(vrow[s]);

@@ -70,6 +70,7 @@ class Workload:
     steps: int = 0  # decode steps, each appending one token per sequence first
     v_format: int = 0  # 0 asym INT4 per 32-channel group, 1 per-token asym INT2 (clipped)
     v_clip: float = 1.0  # clipping ratio of per-token INT2 values
+    n_recent: int = 0  # most recent positions kept in BF16 (0: none)
 
     @property
     def group(self) -> int:
@@ -101,10 +102,11 @@ WORKLOADS = {
     5: Workload(5, "b64_gqa32x8_d128_t16384_t3_sink4_int2_int4_append64", 64, 32, 8, 128, 16384,
                 0, n_sink=4, dist="t3", steps=64),
     # Dual-QK's storage recipe (sec. 3.3, 4.1, B.2) on the 128K shape: INT2 keys with channel 0
-    # in BF16, 5 of 8 query-channel groups kept, the first 64 positions in BF16, per-token
-    # INT2 values clipped to 0.92 of their range
-    6: Workload(6, "b4_gqa32x8_d128_t131072_int2ch0_prune5of8_sink64_int2tok_clip092", 4, 32, 8, 128,
-                131072, 0, k_ch0_bf16=1, n_sink=64, keep_groups=5, v_format=1, v_clip=0.92),
+    # in BF16, 5 of 8 query-channel groups kept, the first 64 and the most recent 256 positions
+    # in BF16, per-token INT2 values clipped to 0.92 of their range
+    6: Workload(6, "b4_gqa32x8_d128_t131072_int2ch0_prune5of8_sink64_recent256_int2tok_clip092", 4, 32, 8,
+                128, 131072, 0, k_ch0_bf16=1, n_sink=64, keep_groups=5, v_format=1, v_clip=0.92,
+                n_recent=256),
 }
 
 

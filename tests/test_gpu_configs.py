@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 def _build(w, extra=0):
     cap = w.capacity(extra)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
-                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip)
+                k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip,
+                n_recent=w.n_recent)
     k, v = synth.prefill(w, device="cuda")
     note(f"workload {w.name}: prefill {tuple(k.shape)} {k.dtype}, capacity {cap}")
     c.append(k, v)
@@ -85,8 +86,9 @@ def test_workload4_pruned_128k(oracle_mod):
 
 
 def test_workload6_dualqk_storage_128k(oracle_mod):
-    """Dual-QK's storage recipe on the 128K shape: 64 BF16 sinks, per-token INT2 values
-    clipped to 0.92, INT2 keys with channel 0 in BF16, 5 of 8 groups kept."""
+    """Dual-QK's storage recipe on the 128K shape: the first 64 and most recent 256 positions
+    in BF16, per-token INT2 values clipped to 0.92, INT2 keys with channel 0 in BF16, 5 of 8
+    groups kept."""
     w = synth.WORKLOADS[6]
     c, k, v = _build(w)
     ocs = _oracle_for(oracle_mod, c, w, k, v, [0, w.batch - 1])
