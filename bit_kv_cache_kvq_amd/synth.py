@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the quantized-KV decode workloads.
 
 This module holds no arithmetic of the method: it only draws random keys, values and
-queries with the shapes and distributions of the five workloads, from torch generators
+queries with the shapes and distributions of the seven workloads, from torch generators
 seeded by a stable hash of (seed, workload, tensor, step).  Both the HIP path and the
 CPU oracle consume what it produces; nothing here quantizes, rotates or attends.
 
@@ -71,6 +71,8 @@ class Workload:
     v_format: int = 0  # 0 asym INT4 per 32-channel group, 1 per-token asym INT2 (clipped)
     v_clip: float = 1.0  # clipping ratio of per-token INT2 values
     n_recent: int = 0  # most recent positions kept in BF16 (0: none)
+    rope_bucket: int = 0  # bucket-relative RoPE: bucket width (0: off)
+    rope_theta: float = 10000.0  # rotary base of the model the inputs stand for
 
     @property
     def group(self) -> int:
@@ -107,7 +109,37 @@ WORKLOADS = {
     6: Workload(6, "b4_gqa32x8_d128_t131072_int2ch0_prune5of8_sink64_recent256_int2tok_clip092", 4, 32, 8,
                 128, 131072, 0, k_ch0_bf16=1, n_sink=64, keep_groups=5, v_format=1, v_clip=0.92,
                 n_recent=256),
+    # workload 6 with bucket-relative RoPE (Dual-QK sec. 3.4, C.4): buckets of 2048 positions,
+    # a rotary base of 10^4; keys and queries count as carrying their rotary embedding
+    7: Workload(7, "b4_gqa32x8_d128_t131072_int2ch0_prune5of8_sink64_recent256_int2tok_clip092_rope2048", 4,
+                32, 8, 128, 131072, 0, k_ch0_bf16=1, n_sink=64, keep_groups=5, v_format=1, v_clip=0.92,
+                n_recent=256, rope_bucket=2048),
 }
+
+
+def rope_table(w: Workload, capacity: int):
+    """The model's rotary (cos, sin) at every bucket anchor: float32 [ceil(capacity / w)][d/2][2],
+    entry (b, i) for the angle (b * w) * theta^(-2i/d) (computed in fp64, then rounded).  This
+    is the model side's positional table, an input like the keys; None without RoPE.
+
+    The keys and queries drawn here are i.i.d. N(0,1) per channel, whose distribution any
+    rotation of a channel pair leaves unchanged, so they serve as keys and queries with
+    their rotary embedding already applied; nothing here rotates them."""
+    if not w.rope_bucket:
+        return None
+    return rope_anchor_table(w.head_dim, w.rope_bucket, capacity, w.rope_theta)
+
+
+def rope_anchor_table(head_dim: int, bucket: int, capacity: int, theta: float = 10000.0):
+    """(cos, sin) of the angles (b * bucket) * theta^(-2i/head_dim), b < ceil(capacity /
+    bucket), i < head_dim / 2: float32 [buckets][head_dim/2][2] (fp64, then rounded)."""
+    import numpy as np
+
+    nb = -(-capacity // bucket)
+    half = head_dim // 2
+    inv_freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / head_dim)
+    ang = (np.arange(nb, dtype=np.float64) * bucket)[:, None] * inv_freq[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
 
 
 def _torch_dtype(w: Workload):

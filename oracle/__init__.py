@@ -72,7 +72,7 @@ def lib():
         L.oracle_tree_sum_f32.argtypes = [P, i]
         L.oracle_lloyd_max_gaussian.restype = i
         L.oracle_lloyd_max_gaussian.argtypes = [i, ctypes.c_double, i, P, P]
-        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, i, P, P, P, P, P, P, P, P, P, P]
+        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, i, P, P, P, P, P, P, P, P, P, P, i, P]
         L.oracle_quant_append.argtypes = cache_args + [P, P, i, i, i, P, P]
         L.oracle_prune_mask.restype = ctypes.c_uint32
         L.oracle_prune_mask.argtypes = [P, i, i, i]
@@ -169,6 +169,7 @@ class Geometry:
     v_format: int = V_ASYM4_G32
     v_clip: float = 1.0
     n_recent: int = 0
+    rope_bucket: int = 0
 
     @property
     def units(self) -> int:
@@ -178,11 +179,18 @@ class Geometry:
     def key_bits(self) -> int:
         return {K_ASYM2: 2, K_ASYM4: 4, K_LLOYD4: 4, K_ASYM8: 8}[self.k_format]
 
+    @property
+    def rope_buckets(self) -> int:
+        """Buckets of the capacity under bucket-relative RoPE, else 1."""
+        return -(-self.capacity // self.rope_bucket) if self.rope_bucket > 0 else 1
+
 
 class OracleCache:
     """Host-side packed cache with the same byte layout the format defines."""
 
-    def __init__(self, geo: Geometry, units: int | None = None):
+    def __init__(self, geo: Geometry, units: int | None = None, rope_table: np.ndarray | None = None):
+        """rope_table: bucket-relative RoPE's anchor (cos, sin) table, fp32
+        [geo.rope_buckets][d/2][2] (an input, like the keys)."""
         self.geo = geo
         U = geo.units if units is None else units
         self.U = U
@@ -202,6 +210,12 @@ class OracleCache:
         self.recent_k = np.zeros((U, nr, d), dtype=np.uint16)
         self.recent_v = np.zeros((U, nr, d), dtype=np.uint16)
         self.len = 0
+        if geo.rope_bucket > 0:
+            if rope_table is None:
+                raise ValueError("bucket-relative RoPE needs its anchor table")
+            self.rope_cs = np.ascontiguousarray(rope_table, dtype=np.float32).reshape(geo.rope_buckets, d // 2, 2)
+        else:
+            self.rope_cs = np.zeros((1, 1, 2), dtype=np.float32)
         if geo.k_format == K_LLOYD4:
             self.cent, self.thr = codebook_f32(16)
         else:
@@ -213,7 +227,7 @@ class OracleCache:
         return [g.head_dim, g.capacity, g.n_sink, g.k_format, g.k_hadamard, g.k_ch0_bf16,
                 g.v_format, float(g.v_clip), g.n_recent, _p(self.k_codes), _p(self.k_sz), _p(self.k_norm),
                 _p(self.k_ch0), _p(self.v_codes), _p(self.v_sz), _p(self.sink_k), _p(self.sink_v),
-                _p(self.recent_k), _p(self.recent_v)]
+                _p(self.recent_k), _p(self.recent_v), g.rope_bucket, _p(self.rope_cs)]
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):
         """k_new, v_new: fp32 [U, n_new, d]; writes positions [len, len+n_new)."""
@@ -241,12 +255,14 @@ class OracleCache:
         return kh, vh
 
     def decode(self, q: np.ndarray, sm: float, keep_groups: int = 0, want_logits: bool = False):
-        """q: fp32 [U, G, d].  Returns (out fp64 [U, G, d], mask u8 [U][, logits])."""
+        """q: fp32 [U, G, d].  Returns (out fp64 [U, G, d], mask u8 [U][, logits]); with
+        bucket-relative RoPE the masks are u8 [U, rope_buckets] (entries past the buckets
+        holding positions stay 0)."""
         q = np.ascontiguousarray(q, dtype=np.float32)
         U, G, d = q.shape
         assert U == self.U and d == self.geo.head_dim
         out = np.zeros((U, G, d), dtype=np.float64)
-        mask = np.zeros(U, dtype=np.uint8)
+        mask = np.zeros((U, self.geo.rope_buckets) if self.geo.rope_bucket > 0 else U, dtype=np.uint8)
         logits = np.zeros((U, G, self.len), dtype=np.float64) if want_logits else None
         lib().oracle_decode_attn(*self._cache_args(), _p(self.cent), U, self.len, G, _p(q),
                                  float(sm), int(keep_groups), _p(out), _p(mask), _p(logits))

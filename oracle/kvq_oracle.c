@@ -28,7 +28,12 @@
  *     with a clipping ratio (Dual-QK sec. 3.3 and sec. B.2: per-token INT2 values with
  *     0.92 clipping);
  *   - attention over the decoded cache with one softmax over all positions
- *     (Dual-QK sec. 3.4: bucket scores share one global softmax).
+ *     (Dual-QK sec. 3.4: bucket scores share one global softmax);
+ *   - bucket-relative RoPE (Dual-QK sec. 3.4 and C.4): keys, given with their rotary
+ *     embedding at their absolute position, are stored relative to the anchor of their
+ *     bucket of w positions, and the query is moved to each bucket's anchor the same way
+ *     before it scores that bucket's keys (so each score is the one of the original
+ *     keys); the pruning mask is taken per bucket.
  *
  * Precision.  The encoding (quantize + pack) runs in fp32 with a fixed operation order;
  * build with -ffp-contract=off and without fast-math so that every fp32 operation is a
@@ -286,7 +291,40 @@ typedef struct {
     uint16_t *k_norm, *k_ch0, *sink_k, *sink_v, *recent_k, *recent_v;
     const float *cent, *thr; /* Lloyd-Max: 16 centroids, 15 thresholds (fp32) */
     int len; /* positions stored (decode: where the recent window starts) */
+    int rope_w; /* bucket-relative RoPE: bucket width w (0: off) */
+    const float *rope_cs; /* (cos, sin) of each bucket anchor's angles [bucket][d/2][2] */
 } ocache;
+
+/* Bucket-relative RoPE (Dual-QK sec. 3.4 and C.4).  Reading: the rotary embedding pairs
+ * channel i with channel i + d/2 (rotate-half layout), and a vector moved to the anchor of
+ * bucket b is rotated back by that anchor's angles: with (cos, sin) = rope_cs[b][i],
+ *   y_i <- y_i cos + y_{i+d/2} sin,   y_{i+d/2} <- y_{i+d/2} cos - y_i sin.
+ * fp32 version: each product rounded, then the sum (this decides codes and masks).        */
+static void anchor_back_f32(const ocache *c, int bucket, float *y)
+{
+    const int h = c->d / 2;
+    const float *cs = c->rope_cs + (size_t)bucket * (size_t)c->d;
+    for (int i = 0; i < h; i++) {
+        float co = cs[2 * i], si = cs[2 * i + 1];
+        float a = y[i], b = y[i + h];
+        float p1 = a * co, p2 = b * si, p3 = b * co, p4 = a * si;
+        y[i] = p1 + p2;
+        y[i + h] = p3 - p4;
+    }
+}
+
+/* The same rotation in fp64 (the query for the logits), from the same table entries. */
+static void anchor_back_f64(const ocache *c, int bucket, double *y)
+{
+    const int h = c->d / 2;
+    const float *cs = c->rope_cs + (size_t)bucket * (size_t)c->d;
+    for (int i = 0; i < h; i++) {
+        double co = (double)cs[2 * i], si = (double)cs[2 * i + 1];
+        double a = y[i], b = y[i + h];
+        y[i] = a * co + b * si;
+        y[i + h] = b * co - a * si;
+    }
+}
 
 static size_t krows(const ocache *c) { return (size_t)(c->d * key_bits(c->kfmt) / 32); }
 
@@ -471,6 +509,8 @@ static void quant_token(const ocache *c, size_t u, int t, const float *k, const 
     const int d = c->d;
     float y[256];
     memcpy(y, k, sizeof(float) * (size_t)d);
+    if (c->rope_w > 0)
+        anchor_back_f32(c, t / c->rope_w, y);
     if (c->rotate)
         oracle_fwht_f32(y, d);
 
@@ -513,12 +553,12 @@ void oracle_quant_append(int d, int cap, int n_sink, int kfmt, int rotate, int c
                          int n_recent,
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
-                         uint16_t *recent_k, uint16_t *recent_v,
+                         uint16_t *recent_k, uint16_t *recent_v, int rope_w, const float *rope_cs,
                          const float *cent, const float *thr, int n_units, int t0, int n_new,
                          const float *k_new, const float *v_new)
 {
     ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, thr, t0 + n_new};
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, thr, t0 + n_new, rope_w, rope_cs};
 #pragma omp parallel for schedule(static)
     for (int u = 0; u < n_units; u++)
         for (int i = 0; i < n_new; i++) {
@@ -667,11 +707,11 @@ void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int c
                          int n_recent,
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
-                         uint16_t *recent_k, uint16_t *recent_v,
+                         uint16_t *recent_k, uint16_t *recent_v, int rope_w, const float *rope_cs,
                          const float *cent, int unit, int len, double *kh, double *vh)
 {
     ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len};
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len, rope_w, rope_cs};
     for (int t = 0; t < len; t++) {
         decode_key(&c, (size_t)unit, t, kh + (size_t)t * (size_t)d);
         decode_value(&c, (size_t)unit, t, vh + (size_t)t * (size_t)d);
@@ -687,48 +727,67 @@ void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int c
  * d_rot = d; otherwise qs = q and d_rot = 1), k^ the decoded stored key; p = softmax(l);
  * out = sum_t p_t v^_t.  All in fp64, two passes (max, then exp and sums).
  * The mask is computed from the fp32 stored-coordinate query (oracle_prune_mask) and
- * written to mask_out[u] when mask_out is not null.  logits_out (nullable) receives the
+ * written to mask_out[u] when mask_out is not null.  With bucket-relative RoPE (rope_w > 0)
+ * the query is moved to each bucket's anchor first, in fp32 for the mask and in fp64 for the
+ * logits, so every bucket b < ceil(len / w) has its own query and mask, written to
+ * mask_out[u * ceil(cap / w) + b]; position t is scored in bucket t / w.  logits_out (nullable) receives the
  * fp64 logits [n_units][G][len].                                                         */
 void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch0, int vfmt, float vclip,
                          int n_recent,
                         uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                         uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
-                         uint16_t *recent_k, uint16_t *recent_v,
+                         uint16_t *recent_k, uint16_t *recent_v, int rope_w, const float *rope_cs,
                         const float *cent, int n_units, int len, int G, const float *q,
                         double sm, int keep_groups, double *out, uint8_t *mask_out,
                         double *logits_out)
 {
     ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len};
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len, rope_w, rope_cs};
 #pragma omp parallel for schedule(dynamic, 1)
     for (int u = 0; u < n_units; u++) {
         const float *qu = q + (size_t)u * (size_t)G * (size_t)d;
-        /* fp32 stored-coordinate query for the mask */
+        /* one query per bucket (one bucket without RoPE): the fp32 stored-coordinate query
+         * for the bucket's mask, and the fp64 one for its logits                          */
+        const int nbq = (rope_w > 0 && len > 0) ? (len + rope_w - 1) / rope_w : 1;
         float *qt32 = (float *)malloc(sizeof(float) * (size_t)G * (size_t)d);
-        double *qs = (double *)malloc(sizeof(double) * (size_t)G * (size_t)d);
+        double *qs = (double *)malloc(sizeof(double) * (size_t)nbq * (size_t)G * (size_t)d);
+        uint32_t *masks = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)nbq);
         double *lg = (double *)malloc(sizeof(double) * (size_t)G * (size_t)(len > 0 ? len : 1));
         double kh[256], vh[256];
-        for (int h = 0; h < G; h++) {
-            memcpy(qt32 + (size_t)h * (size_t)d, qu + (size_t)h * (size_t)d, sizeof(float) * (size_t)d);
-            if (rotate)
-                oracle_fwht_f32(qt32 + (size_t)h * (size_t)d, d);
-            for (int i = 0; i < d; i++)
-                qs[(size_t)h * (size_t)d + (size_t)i] = (double)qu[(size_t)h * (size_t)d + (size_t)i];
-            if (rotate)
-                oracle_fwht_f64(qs + (size_t)h * (size_t)d, d);
+        for (int bq = 0; bq < nbq; bq++) {
+            for (int h = 0; h < G; h++) {
+                float *q32 = qt32 + (size_t)h * (size_t)d;
+                double *q64 = qs + ((size_t)bq * (size_t)G + (size_t)h) * (size_t)d;
+                memcpy(q32, qu + (size_t)h * (size_t)d, sizeof(float) * (size_t)d);
+                for (int i = 0; i < d; i++)
+                    q64[i] = (double)q32[i];
+                if (rope_w > 0) {
+                    anchor_back_f32(&c, bq, q32);
+                    anchor_back_f64(&c, bq, q64);
+                }
+                if (rotate) {
+                    oracle_fwht_f32(q32, d);
+                    oracle_fwht_f64(q64, d);
+                }
+            }
+            masks[bq] = oracle_prune_mask(qt32, G, d, keep_groups);
+            if (mask_out) {
+                const int n_rb = rope_w > 0 ? (cap + rope_w - 1) / rope_w : 1;
+                mask_out[(size_t)u * (size_t)n_rb + (size_t)bq] = (uint8_t)masks[bq];
+            }
         }
-        uint32_t mask = oracle_prune_mask(qt32, G, d, keep_groups);
-        if (mask_out)
-            mask_out[u] = (uint8_t)mask;
         const double scale = sm / (rotate ? (double)d : 1.0);
-        /* pass 1: logits */
+        /* pass 1: logits, each position against its bucket's query and mask */
         for (int t = 0; t < len; t++) {
             decode_key(&c, (size_t)u, t, kh);
+            const int bq = rope_w > 0 ? t / rope_w : 0;
+            const uint32_t mask = masks[bq];
             for (int h = 0; h < G; h++) {
+                const double *q64 = qs + ((size_t)bq * (size_t)G + (size_t)h) * (size_t)d;
                 double s = 0.0;
                 for (int i = 0; i < d; i++)
                     if (mask & (1u << (i / 16)))
-                        s += qs[(size_t)h * (size_t)d + (size_t)i] * kh[i];
+                        s += q64[i] * kh[i];
                 lg[(size_t)h * (size_t)len + (size_t)t] = scale * s;
             }
         }
@@ -761,6 +820,7 @@ void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch
                 o[(size_t)h * (size_t)d + (size_t)i] = len > 0 ? o[(size_t)h * (size_t)d + (size_t)i] / den[h] : 0.0;
         free(qt32);
         free(qs);
+        free(masks);
         free(lg);
     }
 }
