@@ -53,23 +53,33 @@ def decode_bytes_unit(w, length, mask, bf16=True):
     scale/zero words and channel-0 / norm halves of the kept key rows, every value word and
     value scale/zero word of the quantised positions, and (bf16=True) the BF16 rows of the
     sinks and of the recent window, which the query-prep kernel reads rather than the main
-    decode kernel.  mask: kept 16-channel groups (bit p)."""
+    decode kernel.  mask: kept 16-channel groups (bit p); under bucket-relative RoPE a list,
+    one mask per bucket of w.rope_bucket positions."""
     d = w.head_dim
     P = d // 16
-    kept = [(mask >> p) & 1 for p in range(P)]
+
+    def per_token(m):
+        kept = [(m >> p) & 1 for p in range(P)]
+        kbits = 2 if w.k_format == 0 else 4
+        k_tok = sum(kept) * 16 * kbits // 8
+        if w.k_format == 2:
+            k_tok += 2
+        else:
+            k_tok += 4 * sum(1 for g in range(d // 32) if kept[2 * g] or kept[2 * g + 1])
+            if w.k_ch0_bf16 and kept[0]:
+                k_tok += 2
+        v_tok = d // 4 + 4 if w.v_format == 1 else d // 2 + 4 * (d // 32)
+        return k_tok + v_tok
+
     ns = min(w.n_sink, length)
     nr = max(0, min(w.n_recent, length - ns))  # recent positions still in BF16
-    quant = length - ns - nr
-    kbits = 2 if w.k_format == 0 else 4
-    k_tok = sum(kept) * 16 * kbits // 8
-    if w.k_format == 2:
-        k_tok += 2
+    q0, q1 = ns, length - nr  # quantised positions
+    if isinstance(mask, (list, tuple)):
+        bw = w.rope_bucket
+        quant = sum(max(0, min(q1, (b + 1) * bw) - max(q0, b * bw)) * per_token(m) for b, m in enumerate(mask))
     else:
-        k_tok += 4 * sum(1 for g in range(d // 32) if kept[2 * g] or kept[2 * g + 1])
-        if w.k_ch0_bf16 and kept[0]:
-            k_tok += 2
-    v_tok = d // 4 + 4 if w.v_format == 1 else d // 2 + 4 * (d // 32)
-    return quant * (k_tok + v_tok) + ((ns + nr) * d * 2 * 2 if bf16 else 0)
+        quant = (q1 - q0) * per_token(mask)
+    return quant + ((ns + nr) * d * 2 * 2 if bf16 else 0)
 
 
 def traffic_record():
@@ -162,8 +172,9 @@ def cpu_baseline(w, length, budget_s):
     nseq = max(1, math.ceil(threads / H))
     geo = oracle.Geometry(batch=nseq, n_kv_heads=H, head_dim=w.head_dim, capacity=w.capacity(512),
                           n_sink=w.n_sink, k_format=w.k_format, k_hadamard=w.k_hadamard,
-                          k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip, n_recent=w.n_recent)
-    oc = oracle.OracleCache(geo)
+                          k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip, n_recent=w.n_recent,
+                          rope_bucket=w.rope_bucket)
+    oc = oracle.OracleCache(geo, rope_table=synth.rope_table(w, geo.capacity))
     prefill_len = length - (1 if w.steps else 0)
     k, v = synth.prefill(w, device="cpu", context=prefill_len, batch=nseq)
     oc.append(k.float().numpy().reshape(nseq * H, prefill_len, w.head_dim),
@@ -213,7 +224,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=128)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -283,7 +294,7 @@ def main():
     cap = w.capacity(appends)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
                 k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, device=dev, v_format=w.v_format,
-                v_clip=w.v_clip, n_recent=w.n_recent)
+                v_clip=w.v_clip, n_recent=w.n_recent, rope_bucket=w.rope_bucket, rope_table=synth.rope_table(w, cap))
     log(f"workload {w.name}: capacity {cap}, building cache ...")
     k, v = synth.prefill(w, device=dev)
     c.append(k, v)
@@ -294,7 +305,7 @@ def main():
     queries = [synth.query(w, i, device=dev) for i in range(nsteps)]
     news = [synth.append_tokens(w, i, device=dev) for i in range(nsteps)] if w.steps else []
     out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
-    mask = torch.zeros(w.units, dtype=torch.uint8, device=dev)
+    mask = torch.zeros(w.units * c.rope_buckets, dtype=torch.uint8, device=dev)
     c.workspace(w.n_q_heads)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -342,7 +353,10 @@ def main():
     call_avg_s = sum(call_ms) / len(call_ms) / 1e3
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     full = (1 << (w.head_dim // 16)) - 1
-    masks = mask.cpu().tolist() if w.keep_groups else [full] * w.units
+    if w.rope_bucket:
+        masks = mask.view(w.units, -1).cpu().tolist() if w.keep_groups else [[full] * c.rope_buckets] * w.units
+    else:
+        masks = mask.cpu().tolist() if w.keep_groups else [full] * w.units
     bytes_per = [sum(decode_bytes_unit(w, L, m) for m in masks) for L in lens]
     # algorithmic bytes of the launches the events timed
     bytes_ev = [sum(decode_bytes_unit(w, L, m, bf16=False) for m in masks) for L in lens_ev]
@@ -380,6 +394,7 @@ def main():
                    "key_format": ["asym_int2", "asym_int4", "wht_lloyd4"][w.k_format],
                    "value_format": "asym_int2_token_clip%.2f" % w.v_clip if w.v_format == 1 else "asym_int4_g32",
                    "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink, "recent_bf16_tokens": w.n_recent,
+                   "rope_bucket": w.rope_bucket,
                    "keep_groups": w.keep_groups, "appends_per_step": 1 if w.steps else 0,
                    "parallelism": "single GPU"},
         "effective_GBps": eff_gbps,

@@ -20,7 +20,7 @@ KVQ_F32, KVQ_BF16 = 0, 1
 K_ASYM2, K_ASYM4, K_LLOYD4 = 0, 1, 2
 V_ASYM4_G32, V_ASYM2_TOKEN = 0, 1
 BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", "sink_v",
-             "codebook", "thresholds", "recent_k", "recent_v"]  # KVQ_BUF_* order
+             "codebook", "thresholds", "recent_k", "recent_v", "rope_cs"]  # KVQ_BUF_* order
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles", "kvq_set_deterministic",
            "kvq_set_decode_events", "kvq_probe_stream_read",
@@ -32,7 +32,8 @@ class KvqCacheC(ctypes.Structure):
                                               "k_format", "k_hadamard", "k_ch0_bf16", "len")] + \
                [(n, ctypes.c_void_p) for n in BUF_NAMES[:10]] + \
                [("v_format", ctypes.c_int32), ("v_clip", ctypes.c_float), ("n_recent", ctypes.c_int32)] + \
-               [(n, ctypes.c_void_p) for n in BUF_NAMES[10:]]
+               [(n, ctypes.c_void_p) for n in BUF_NAMES[10:12]] + \
+               [("rope_bucket", ctypes.c_int32), ("rope_cs", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -138,12 +139,17 @@ class Cache:
     """A quantized KV cache whose buffers are torch device tensors (zero-initialised)."""
 
     def __init__(self, batch, n_kv_heads, head_dim, capacity, n_sink=0, k_format=K_ASYM2,
-                 k_hadamard=0, k_ch0_bf16=0, device="cuda", v_format=V_ASYM4_G32, v_clip=1.0, n_recent=0):
+                 k_hadamard=0, k_ch0_bf16=0, device="cuda", v_format=V_ASYM4_G32, v_clip=1.0, n_recent=0,
+                 rope_bucket=0, rope_table=None):
+        """rope_bucket: bucket width w of bucket-relative RoPE (0: off); rope_table: the model's
+        (cos, sin) of every bucket anchor, float32 [ceil(capacity / w)][head_dim / 2][2]
+        (copied into the cache's rope_cs buffer)."""
         self.c = KvqCacheC(batch, n_kv_heads, head_dim, capacity, n_sink, k_format, k_hadamard,
                            k_ch0_bf16, 0)
         self.c.v_format = int(v_format)
         self.c.v_clip = float(v_clip)
         self.c.n_recent = int(n_recent)
+        self.c.rope_bucket = int(rope_bucket)
         self.device = torch.device(device)
         self.buffers = {}
         for i, name in enumerate(BUF_NAMES):
@@ -157,10 +163,24 @@ class Cache:
             cent, thr = codebook_gaussian(4)
             self.buffers["codebook"].view(torch.float32).copy_(torch.tensor(cent, dtype=torch.float32))
             self.buffers["thresholds"].view(torch.float32).copy_(torch.tensor(thr, dtype=torch.float32))
+        if rope_bucket:
+            if rope_table is None:
+                raise ValueError("bucket-relative RoPE needs its anchor table")
+            tab = torch.as_tensor(rope_table, dtype=torch.float32).reshape(-1)
+            dst = self.buffers["rope_cs"].view(torch.float32)
+            if tab.numel() != dst.numel():
+                raise ValueError(f"rope_table holds {tab.numel()} floats, the cache needs {dst.numel()}")
+            dst.copy_(tab.to(self.device))
         st = lib().kvq_validate(ctypes.byref(self.c))
         if st != KVQ_OK:
             raise KvqError(st, "kvq_validate")
         self._ws = {}
+
+    @property
+    def rope_buckets(self) -> int:
+        """Buckets of the capacity under bucket-relative RoPE (mask entries per unit), else 1."""
+        w = int(self.c.rope_bucket)
+        return -(-int(self.c.capacity) // w) if w > 0 else 1
 
     @property
     def len(self) -> int:
@@ -191,7 +211,8 @@ class Cache:
         if out is None:
             out = torch.empty(q.shape[0], hq, q.shape[2], dtype=torch.float32, device=q.device)
         if mask_out is None:
-            mask_out = torch.zeros(self.c.batch * self.c.n_kv_heads, dtype=torch.uint8, device=q.device)
+            mask_out = torch.zeros(self.c.batch * self.c.n_kv_heads * self.rope_buckets, dtype=torch.uint8,
+                                   device=q.device)
         ws = self.workspace(hq)
         dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
         st = lib().kvq_decode_attn(ctypes.byref(self.c), _ptr(q), dt, hq, float(sm_scale), int(keep_groups),

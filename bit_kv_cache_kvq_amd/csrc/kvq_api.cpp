@@ -52,12 +52,32 @@ kvq_status check_geometry(const kvq_cache *c)
         return KVQ_ERR_ARG;
     if (c->n_recent < 0 || c->n_recent > kMaxRecent)
         return KVQ_ERR_UNSUPPORTED;
+    if (c->rope_bucket < 0)
+        return KVQ_ERR_ARG;
+    if (c->rope_bucket != 0 && (c->rope_bucket < kTile || c->rope_bucket > kMaxCapacity ||
+                                (c->rope_bucket & (c->rope_bucket - 1)) != 0))
+        return KVQ_ERR_UNSUPPORTED;
     if (c->len > c->capacity)
         return KVQ_ERR_CAPACITY;
     return KVQ_OK;
 }
 
 size_t units_of(const kvq_cache *c) { return (size_t)c->batch * (size_t)c->n_kv_heads; }
+
+// Bucket-relative RoPE: buckets of the capacity (query records per unit; 1 when off), and
+// log2 of the bucket width (0 when off).
+int rope_buckets(const kvq_cache *c)
+{
+    return c->rope_bucket > 0 ? (c->capacity + c->rope_bucket - 1) / c->rope_bucket : 1;
+}
+
+int rope_log2(const kvq_cache *c)
+{
+    int lw = 0;
+    while (c->rope_bucket > 0 && (1 << lw) < c->rope_bucket)
+        lw++;
+    return lw;
+}
 
 // End of the quantised positions [n_sink, q_end) when len positions are stored: with a
 // recent window of W positions, the W most recent ones (>= n_sink) are still in BF16.
@@ -87,16 +107,17 @@ size_t buffer_bytes(const kvq_cache *c, int which)
     case KVQ_BUF_THRESHOLDS: return lloyd ? 15 * 4 : 0;
     case KVQ_BUF_RECENT_K:
     case KVQ_BUF_RECENT_V: return U * (size_t)c->n_recent * d * 2;
+    case KVQ_BUF_ROPE_CS: return c->rope_bucket > 0 ? (size_t)rope_buckets(c) * (d / 2) * 2 * 4 : 0;
     default: return 0;
     }
 }
 
 kvq_status check_buffers(const kvq_cache *c)
 {
-    const void *ptrs[12] = {c->k_codes, c->k_sz,     c->k_norm,     c->k_ch0,
-                            c->v_codes, c->v_sz,     c->sink_k,     c->sink_v,
-                            c->codebook, c->thresholds, c->recent_k, c->recent_v};
-    for (int i = 0; i < 12; i++) {
+    const void *ptrs[13] = {c->k_codes,  c->k_sz,       c->k_norm,   c->k_ch0,    c->v_codes,
+                            c->v_sz,     c->sink_k,     c->sink_v,   c->codebook, c->thresholds,
+                            c->recent_k, c->recent_v,   c->rope_cs};
+    for (int i = 0; i < 13; i++) {
         if (buffer_bytes(c, i) == 0)
             continue;
         if (!ptrs[i])
@@ -225,6 +246,8 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
     p.q_end = quant_end(c, c->len + n_new);
     p.evict = 0;
     p.e0 = 0;
+    p.rope_cs = c->rope_cs;
+    p.rope_lw = rope_log2(c);
     // recent window: first quantise the ring positions that leave it (their slots are
     // overwritten by the new positions of the second launch)
     const int q_old = quant_end(c, c->len);
@@ -254,7 +277,8 @@ static size_t part_region_bytes(const kvq_cache *c, int G)
 
 static size_t qrec_region_bytes(const kvq_cache *c, int G)
 {
-    return round256(units_of(c) * (size_t)decode_qrec_words(c->head_dim, G, c->k_format) * sizeof(uint32_t));
+    return round256(units_of(c) * (size_t)rope_buckets(c) *
+                    (size_t)decode_qrec_words(c->head_dim, G, c->k_format) * sizeof(uint32_t));
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
@@ -340,6 +364,10 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.n_waves = pl.n_waves;
     p.dynamic = !g_deterministic.load();
     p.n_cu = device_cus();
+    p.rope_cs = c->rope_cs;
+    p.rope_lw = rope_log2(c);
+    p.n_rb = rope_buckets(c);
+    p.n_qb = c->rope_bucket > 0 && c->len > 0 ? (c->len + c->rope_bucket - 1) / c->rope_bucket : 1;
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
     if (!ev[0] || !ev[1])
         ev[0] = ev[1] = nullptr;

@@ -17,6 +17,8 @@
 //   with a recent window of W positions (Dual-QK sec. 3.3 / 4.1; past-only quantization),
 //   new positions go to ring slot t mod W in BF16 and are quantised from that copy when they
 //   leave the window (a first launch with `evict` set does those of earlier appends).
+//   with bucket-relative RoPE (Dual-QK sec. 3.4 / C.4), keys are first rotated back by the
+//   anchor of their position's bucket, before the Walsh-Hadamard rotation.
 // Work per appended token is O(head_dim) and touches only that token's slots
 // (TurboQuant on Quantized Models, abstract: incremental cache).
 #include "kvq_device.h"
@@ -156,6 +158,8 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
         const size_t in_off = ((size_t)u * (size_t)p.n_new + (size_t)i) * D + (size_t)lane * CPL;
         load_row<CPL>(p.k_new, in_off, p.in_bf16, k);
         load_row<CPL>(p.v_new, in_off, p.in_bf16, v);
+        if (p.rope_lw)
+            anchor_rotate<CPL>(k, p.rope_cs + (size_t)(t >> p.rope_lw) * D, lane);
         if (p.rotate)
             fwht<CPL>(k, lane);
 

@@ -207,11 +207,15 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
 
     const int lane = threadIdx.x % kWave;
     const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
-    const int unit = blockIdx.x;
+    // workgroups of bucket 0 first: they also compute the BF16 positions' softmax state, the
+    // longest work of the kernel, so they start before the other buckets' records
+    const int bk = (int)blockIdx.x / p.n_units; // bucket of this record (0 without RoPE)
+    const int unit = (int)blockIdx.x % p.n_units;
     const int b = unit / p.n_kv_heads;
     const int kvh = unit % p.n_kv_heads;
     const int n_q_heads = p.n_kv_heads * G;
-    uint32_t *rec = p.qprep + (size_t)unit * C::QREC;
+    const bool state = bk == 0; // this workgroup also computes the BF16 positions' state
+    uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
     float *recf = reinterpret_cast<float *>(rec);
 
     // BF16 sink rows, SB at a time (the last row repeated past n_sink); the first batch of
@@ -229,25 +233,40 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         }
     };
     float kv[SB][CPL], vv[SB][CPL];
-    if (n_sink > 0) {
+    if (state && n_sink > 0) {
         load_sinks(p.sink_k, 0, kv);
         load_sinks(p.sink_v, 0, vv);
     }
 
+    float yq[CPL]; // this head's query as given
     {
         const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
-        float y[CPL];
         if (p.q_bf16) {
             const uint16_t *qb = static_cast<const uint16_t *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                y[s] = bf16_to_f32(qb[s]);
+                yq[s] = bf16_to_f32(qb[s]);
         } else {
             const float *qf = static_cast<const float *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                y[s] = qf[s];
+                yq[s] = qf[s];
         }
+    }
+    const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
+
+    // The query of bucket bq in stored coordinates (rotated back by the bucket's anchor under
+    // bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys are rotated),
+    // its group energies, the mask, and this head's scaled, masked query in qr and sq_[h].
+    // Every wave of the workgroup calls it together (two barriers).
+    float qr[CPL];
+    auto prep = [&](int bq) -> uint32_t {
+        float y[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            y[s] = yq[s];
+        if (p.rope_lw)
+            anchor_rotate<CPL>(y, p.rope_cs + (size_t)bq * D, lane);
         if (p.rotate)
             fwht_wave<CPL>(y, lane);
         float sq[CPL], am = 0.0f;
@@ -273,170 +292,65 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
             se[h][lane / (16 / CPL)] = e;
             sam[h][lane / (16 / CPL)] = am;
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // mask (every wave computes the same one): keep the `keep` highest group energies
-    // summed over the heads in ascending head order, ties to the lower group
-    uint32_t mask = (1u << NP) - 1u;
-    if (p.keep > 0 && p.keep < NP) {
-        float E[NP];
+        // mask (every wave computes the same one): keep the `keep` highest group energies
+        // summed over the heads in ascending head order, ties to the lower group
+        uint32_t mask = (1u << NP) - 1u;
+        if (p.keep > 0 && p.keep < NP) {
+            float E[NP];
 #pragma unroll
-        for (int g = 0; g < NP; g++) {
-            float acc = se[0][g];
+            for (int g = 0; g < NP; g++) {
+                float acc = se[0][g];
 #pragma unroll
-            for (int hh = 1; hh < G; hh++)
-                acc = acc + se[hh][g];
-            E[g] = acc;
+                for (int hh = 1; hh < G; hh++)
+                    acc = acc + se[hh][g];
+                E[g] = acc;
+            }
+            mask = 0;
+#pragma unroll
+            for (int g = 0; g < NP; g++) {
+                int rank = 0;
+#pragma unroll
+                for (int o = 0; o < NP; o++)
+                    rank += (E[o] > E[g] || (E[o] == E[g] && o < g)) ? 1 : 0;
+                if (rank < p.keep)
+                    mask |= 1u << g;
+            }
         }
-        mask = 0;
+        mask = uniform(mask);
+
+        // this head's scaled, masked fp32 query
 #pragma unroll
-        for (int g = 0; g < NP; g++) {
-            int rank = 0;
-#pragma unroll
-            for (int o = 0; o < NP; o++)
-                rank += (E[o] > E[g] || (E[o] == E[g] && o < g)) ? 1 : 0;
-            if (rank < p.keep)
-                mask |= 1u << g;
+        for (int s = 0; s < CPL; s++) {
+            const int c = lane * CPL + s;
+            const bool kept = (mask >> (c / 16)) & 1u;
+            qr[s] = kept ? sq_[h][c] * qscale : 0.0f;
+            sq_[h][c] = qr[s];
         }
+        __syncthreads();
+        return mask;
+    };
+    const uint32_t mask = prep(bk);
+
+    if (state) {
+        // the decode kernel's tile and arrival counters of this unit's stripes, at the places
+        // u + k * units
+        for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
+            if (unit + k * p.n_units < p.n_waves) {
+                p.tile_ctr[unit + k * p.n_units] = 0u;
+                p.tile_ctr[p.n_waves + unit + k * p.n_units] = 0u;
+            }
+        if (threadIdx.x == 0)
+            p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
     }
-    mask = uniform(mask);
-    // the decode kernel's tile and arrival counters of this unit's stripes, at the places
-    // u + k * units
-    for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
-        if (unit + k * p.n_units < p.n_waves) {
-            p.tile_ctr[unit + k * p.n_units] = 0u;
-            p.tile_ctr[p.n_waves + unit + k * p.n_units] = 0u;
-        }
     if (threadIdx.x == 0) {
-        p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
         rec[C::OFF_MASK] = mask;
         if (p.mask_out)
-            p.mask_out[unit] = (uint8_t)mask;
-    }
-    const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
-
-    // this head's scaled, masked fp32 query
-    float qr[CPL];
-#pragma unroll
-    for (int s = 0; s < CPL; s++) {
-        const int c = lane * CPL + s;
-        const bool kept = (mask >> (c / 16)) & 1u;
-        qr[s] = kept ? sq_[h][c] * qscale : 0.0f;
-        sq_[h][c] = qr[s];
-    }
-    __syncthreads();
-
-    // BF16 sink positions (t < min(n_sink, len)): dense dot over the kept channels, then
-    // the head's softmax state over them -- log2 max m, sum l and o = sum_t 2^(l_t - m) v_t
-    // -- which the decode kernel folds into the unit's result.  Lanes own
-    // channels; one wave-wide sum per sink gives its logit, lane t keeps that of sink t.
-    {
-        float mine = -__builtin_inff();
-        for (int t0 = 0; t0 < n_sink; t0 += SB) {
-            if (t0 > 0)
-                load_sinks(p.sink_k, t0, kv);
-#pragma unroll
-            for (int j = 0; j < SB; j++) {
-                if (t0 + j >= n_sink)
-                    break;
-                float part = 0.0f;
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    part = fmaf(qr[s], kv[j][s], part);
-                const float tot = wave_sum_dpp(part);
-                mine = lane == t0 + j ? tot : mine;
-            }
-        }
-        const float m = wave_max_dpp(mine);
-        const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine - m) : 0.0f;
-        sp[h][lane] = pr;
-        const float l = wave_sum_dpp(pr);
-        __syncthreads();
-        float o[CPL];
-#pragma unroll
-        for (int s = 0; s < CPL; s++)
-            o[s] = 0.0f;
-        for (int t0 = 0; t0 < n_sink; t0 += SB) {
-            if (t0 > 0)
-                load_sinks(p.sink_v, t0, vv);
-#pragma unroll
-            for (int j = 0; j < SB; j++) {
-                if (t0 + j >= n_sink)
-                    break;
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    o[s] = fmaf(sp[h][t0 + j], vv[j][s], o[s]);
-            }
-        }
-        // recent BF16 window, positions [wlo, len) in ring slots t mod W (Dual-QK sec. 3.3 /
-        // 4.1): 64 positions at a time, lane j scoring position wlo + c0 + j over all
-        // channels from its ring row, folded into the state (m, l, o) online
-        float M = m, L = l;
-        const int wlo = p.q_end > n_sink ? p.q_end : n_sink;
-        const int n_win = p.len - wlo;
-        for (int c0 = 0; c0 < n_win; c0 += kWave) {
-            const int nc = n_win - c0 < kWave ? n_win - c0 : kWave; // positions in this chunk
-            const bool valid = lane < nc;
-            // ring slot of the chunk's position j: slot0 + j, wrapped once at most (the window
-            // holds at most W positions); positions past the chunk repeat its last one
-            const int slot0 = (wlo + c0) % p.n_recent;
-            auto slot = [&](int j) {
-                const int sl = slot0 + (j < nc ? j : nc - 1);
-                return sl >= p.n_recent ? sl - p.n_recent : sl;
-            };
-            const uint16_t *krow = p.recent_k + ((size_t)unit * p.n_recent + (size_t)slot(lane)) * D;
-            float dot = 0.0f;
-#pragma unroll
-            for (int c = 0; c < D; c += 8) {
-                const uint4 kw = *reinterpret_cast<const uint4 *>(krow + c);
-                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    dot = fmaf(sq_[h][c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dot);
-                    dot = fmaf(sq_[h][c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dot);
-                }
-            }
-            const float lw = valid ? dot : -__builtin_inff();
-            const float Mn = fmaxf(M, wave_max_dpp(lw)); // finite: the chunk has a position
-            const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-            const float pw = valid ? __builtin_amdgcn_exp2f(lw - Mn) : 0.0f;
-            L = fmaf(L, fo, wave_sum_dpp(pw));
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                o[s] *= fo;
-            // values, 32 positions per batch of loads (rows past the chunk repeat its last
-            // position with weight 0); lane owns channels lane*CPL ..
-#pragma unroll
-            for (int b0 = 0; b0 < kWave; b0 += 32) {
-                float vw[32][CPL];
-#pragma unroll
-                for (int jj = 0; jj < 32; jj++) {
-                    const uint16_t *vrow =
-                        p.recent_v + ((size_t)unit * p.n_recent + (size_t)slot(b0 + jj)) * D + lane * CPL;
-#pragma unroll
-                    for (int s = 0; s < CPL; s++)
-                        vw[jj][s] = bf16_to_f32(vrow[s]);
-                }
-#pragma unroll
-                for (int jj = 0; jj < 32; jj++) {
-                    const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), b0 + jj));
-#pragma unroll
-                    for (int s = 0; s < CPL; s++)
-                        o[s] = fmaf(pj, vw[jj][s], o[s]);
-                }
-            }
-            M = Mn;
-        }
-        if (lane == 0) {
-            recf[C::OFF_SINK + h * (D + 2)] = M;
-            recf[C::OFF_SINK + h * (D + 2) + 1] = L;
-        }
-#pragma unroll
-        for (int s = 0; s < CPL; s++)
-            recf[C::OFF_SINK + h * (D + 2) + 2 + lane * CPL + s] = o[s];
+            p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
     }
 
+    // ---- the query operands of this record
     if constexpr (KF == KVQ_K_LLOYD4) {
         // fp16 pairs scaled so the largest kept |q| of the group lands in [2^12, 2^13);
         // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
@@ -515,6 +429,129 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
             recf[C::OFF_QSC + h] = unit_q / F;
             recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv * F : 0.0f;
         }
+    }
+    if (!state)
+        return;
+
+    // BF16 sink positions (t < min(n_sink, len), all in bucket 0): dense dot over the kept
+    // channels, then the head's softmax state over them -- log2 max m, sum l and
+    // o = sum_t 2^(l_t - m) v_t -- which the decode kernel folds into the unit's result.
+    // Lanes own channels; one wave-wide sum per sink gives its logit, lane t keeps that of
+    // sink t.
+    {
+        float mine = -__builtin_inff();
+        for (int t0 = 0; t0 < n_sink; t0 += SB) {
+            if (t0 > 0)
+                load_sinks(p.sink_k, t0, kv);
+#pragma unroll
+            for (int j = 0; j < SB; j++) {
+                if (t0 + j >= n_sink)
+                    break;
+                float part = 0.0f;
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    part = fmaf(qr[s], kv[j][s], part);
+                const float tot = wave_sum_dpp(part);
+                mine = lane == t0 + j ? tot : mine;
+            }
+        }
+        const float m = wave_max_dpp(mine);
+        const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine - m) : 0.0f;
+        sp[h][lane] = pr;
+        const float l = wave_sum_dpp(pr);
+        __syncthreads();
+        float o[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            o[s] = 0.0f;
+        for (int t0 = 0; t0 < n_sink; t0 += SB) {
+            if (t0 > 0)
+                load_sinks(p.sink_v, t0, vv);
+#pragma unroll
+            for (int j = 0; j < SB; j++) {
+                if (t0 + j >= n_sink)
+                    break;
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    o[s] = fmaf(sp[h][t0 + j], vv[j][s], o[s]);
+            }
+        }
+        // recent BF16 window, positions [wlo, len) in ring slots t mod W (Dual-QK sec. 3.3 /
+        // 4.1), one bucket's positions at a time (the query of that bucket), 64 positions per
+        // chunk, lane j scoring position c0 + j over all channels from its ring row, folded
+        // into the state (m, l, o) online
+        float M = m, L = l;
+        const int wlo = p.q_end > n_sink ? p.q_end : n_sink;
+        int qb = 0; // bucket whose query qr / sq_ hold
+        for (int s0 = wlo; s0 < p.len;) {
+            const int bs = p.rope_lw ? s0 >> p.rope_lw : 0;
+            const int s1 = p.rope_lw ? min(p.len, (bs + 1) << p.rope_lw) : p.len;
+            if (bs != qb) {
+                (void)prep(bs);
+                qb = bs;
+            }
+            for (int c0 = s0; c0 < s1; c0 += kWave) {
+                const int nc = s1 - c0 < kWave ? s1 - c0 : kWave; // positions in this chunk
+                const bool valid = lane < nc;
+                // ring slot of the chunk's position j: slot0 + j, wrapped once at most (the window
+                // holds at most W positions); positions past the chunk repeat its last one
+                const int slot0 = c0 % p.n_recent;
+                auto slot = [&](int j) {
+                    const int sl = slot0 + (j < nc ? j : nc - 1);
+                    return sl >= p.n_recent ? sl - p.n_recent : sl;
+                };
+                const uint16_t *krow = p.recent_k + ((size_t)unit * p.n_recent + (size_t)slot(lane)) * D;
+                float dot = 0.0f;
+#pragma unroll
+                for (int c = 0; c < D; c += 8) {
+                    const uint4 kw = *reinterpret_cast<const uint4 *>(krow + c);
+                    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        dot = fmaf(sq_[h][c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dot);
+                        dot = fmaf(sq_[h][c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dot);
+                    }
+                }
+                const float lw = valid ? dot : -__builtin_inff();
+                const float Mn = fmaxf(M, wave_max_dpp(lw)); // finite: the chunk has a position
+                const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+                const float pw = valid ? __builtin_amdgcn_exp2f(lw - Mn) : 0.0f;
+                L = fmaf(L, fo, wave_sum_dpp(pw));
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    o[s] *= fo;
+                // values, 32 positions per batch of loads (rows past the chunk repeat its last
+                // position with weight 0); lane owns channels lane*CPL ..
+#pragma unroll
+                for (int b0 = 0; b0 < kWave; b0 += 32) {
+                    float vw[32][CPL];
+#pragma unroll
+                    for (int jj = 0; jj < 32; jj++) {
+                        const uint16_t *vrow =
+                            p.recent_v + ((size_t)unit * p.n_recent + (size_t)slot(b0 + jj)) * D + lane * CPL;
+#pragma unroll
+                        for (int s = 0; s < CPL; s++)
+                            vw[jj][s] = bf16_to_f32(vrow[s]);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < 32; jj++) {
+                        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), b0 + jj));
+#pragma unroll
+                        for (int s = 0; s < CPL; s++)
+                            o[s] = fmaf(pj, vw[jj][s], o[s]);
+                    }
+                }
+                M = Mn;
+            }
+            s0 = s1;
+        }
+        if (lane == 0) {
+            recf[C::OFF_SINK + h * (D + 2)] = M;
+            recf[C::OFF_SINK + h * (D + 2) + 1] = L;
+        }
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            recf[C::OFF_SINK + h * (D + 2) + 2 + lane * CPL + s] = o[s];
     }
 }
 
@@ -945,18 +982,26 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u; // value word offset
     const int q_lo = p.n_sink, q_hi = p.q_end; // quantized positions [q_lo, q_hi)
 
-    // ---- the unit's query scalars (uniform loads from its record)
-    const uint32_t *__restrict__ rec = qrec + (size_t)u * C::QREC;
+    // ---- the unit's query scalars (uniform loads from its record).  Under bucket-relative
+    // RoPE every bucket of w positions has a record of its own (query rotated back by the
+    // bucket's anchor, its mask and scales): tile t reads record t >> tlw; without RoPE
+    // tlw = 31, so every tile reads the first one.  The first record also holds the BF16
+    // positions' softmax state.
+    const uint32_t *__restrict__ rec = qrec + (size_t)u * p.n_rb * C::QREC;
+    const int tlw = p.rope_lw ? p.rope_lw - 7 : 31; // log2 of the tiles per bucket
+    static_assert(C::TILE == 1 << 7, "tiles per bucket");
     const uint32_t mask = rec[C::OFF_MASK];
     float acc_to_logit[G], logit_to_acc[G];
-    {
-        const float *recf = reinterpret_cast<const float *>(rec);
+    int qbk = 0; // bucket whose scales acc_to_logit / logit_to_acc hold
+    auto load_scales = [&](int bq) {
+        const float *recf = reinterpret_cast<const float *>(rec + (size_t)bq * C::QREC);
 #pragma unroll
         for (int h = 0; h < G; h++) {
             acc_to_logit[h] = recf[C::OFF_QSC + h];
             logit_to_acc[h] = 1.0f / acc_to_logit[h];
         }
-    }
+    };
+    load_scales(0);
 
     // ---- running softmax state of the current unit
     float acc[G][8];
@@ -1116,13 +1161,18 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         ask = draw_tile(ctr);
     // the tile loop, compiled for every-row-kept or not (ALL) and channel 0 apart or not
     // (CH0), so that neither costs a branch per tile
-    auto tiles = [&](auto all_c, auto ch0_c) {
+    auto tiles = [&](auto all_c, auto ch0_c, auto rope_c) {
         constexpr bool ALL = decltype(all_c)::value;
         constexpr bool CH0 = decltype(ch0_c)::value;
+        constexpr bool RP = decltype(rope_c)::value; // per-bucket records (bucket-relative RoPE)
+        // mask of the tile in `cur` (its bucket's; without RoPE the unit's)
+        uint32_t mcur = mask;
         {
             const int t = ts0 + smem;
             const uint32_t off = t < ts1 ? 0u : kNoAccess;
-            load_ktile<D, G, KF, VF, ALL, CH0>(cur, sl, ucap, lane, t * TILE, mask, off);
+            if (RP && t < ts1)
+                mcur = rec[(size_t)(t >> tlw) * C::QREC + C::OFF_MASK];
+            load_ktile<D, G, KF, VF, ALL, CH0>(cur, sl, ucap, lane, t * TILE, mcur, off);
 #pragma unroll
             for (int it = 0; it < VIT; it++)
                 vcur[it] = vload<V2>(sl.vc, vvo + off, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
@@ -1140,7 +1190,16 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             // operands are read through an address that depends on the tile number (the
             // added term is always 0: t >= 0), so they are reloaded per tile from the scalar
             // cache rather than hoisted out of the loop into more scalar registers than exist.
-            const uint32_t *__restrict__ rq = rec + ((uint32_t)t >> 31);
+            const int bt = RP ? t >> tlw : 0;
+            const uint32_t *__restrict__ rq = rec + ((uint32_t)t >> 31) + (size_t)bt * C::QREC;
+            if (RP && bt != qbk) {
+                // a tile of another bucket: its scales, and the raise threshold in its units
+                load_scales(bt);
+                qbk = bt;
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    mthr[h] = (mrun[h] + kSlack) * logit_to_acc[h];
+            }
             float lg[TPL][G];
 #pragma unroll
             for (int i = 0; i < TPL; i++)
@@ -1148,11 +1207,11 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 for (int h = 0; h < G; h++)
                     lg[i][h] = 0.0f;
             if constexpr (KF != KVQ_K_LLOYD4) {
-                score_asym<D, G, KF, VF, ALL, CH0>(cur, rq, mask, lg);
+                score_asym<D, G, KF, VF, ALL, CH0>(cur, rq, mcur, lg);
             } else {
 #pragma unroll
                 for (int r = 0; r < KROWS; r++) {
-                    if (!ALL && !(mask >> (r / C::RPP) & 1u))
+                    if (!ALL && !(mcur >> (r / C::RPP) & 1u))
                         continue;
                     uint32_t pr[TPL][4];
 #pragma unroll
@@ -1209,7 +1268,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             // in flight during the rest of this tile.  After the wave's last tile the loads
             // access nothing.
             const uint32_t noff = more ? 0u : kNoAccess;
-            load_ktile<D, G, KF, VF, ALL, CH0>(cur, sl, ucap, lane, tn * TILE, mask, noff);
+            if constexpr (RP)
+                mcur = more ? rec[(size_t)(tn >> tlw) * C::QREC + C::OFF_MASK] : mask;
+            load_ktile<D, G, KF, VF, ALL, CH0>(cur, sl, ucap, lane, tn * TILE, mcur, noff);
 
             // ---- online softmax (log2 units), per head.  The running maximum m is raised
             // (wave-wide DPP max, rescale of that head's state) only when a logit exceeds
@@ -1350,16 +1411,23 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             t = tn;
         }
     };
-    if (mask == (1u << NP) - 1u) {
+    // (bucket-relative RoPE takes the pruned-rows variant whatever the masks: they differ
+    // by bucket)
+    if (p.rope_lw) {
         if (KF != KVQ_K_LLOYD4 && p.ch0)
-            tiles(BoolC<true>(), BoolC<KF != KVQ_K_LLOYD4>());
+            tiles(BoolC<false>(), BoolC<KF != KVQ_K_LLOYD4>(), BoolC<true>());
         else
-            tiles(BoolC<true>(), BoolC<false>());
+            tiles(BoolC<false>(), BoolC<false>(), BoolC<true>());
+    } else if (mask == (1u << NP) - 1u) {
+        if (KF != KVQ_K_LLOYD4 && p.ch0)
+            tiles(BoolC<true>(), BoolC<KF != KVQ_K_LLOYD4>(), BoolC<false>());
+        else
+            tiles(BoolC<true>(), BoolC<false>(), BoolC<false>());
     } else {
         if (KF != KVQ_K_LLOYD4 && p.ch0)
-            tiles(BoolC<false>(), BoolC<KF != KVQ_K_LLOYD4>());
+            tiles(BoolC<false>(), BoolC<KF != KVQ_K_LLOYD4>(), BoolC<false>());
         else
-            tiles(BoolC<false>(), BoolC<false>());
+            tiles(BoolC<false>(), BoolC<false>(), BoolC<false>());
     }
     flush();
 }
@@ -1369,9 +1437,9 @@ template <int D, int G, int KF, int VF>
 hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
     if (p.n_sink > 8)
-        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 32>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 32>), dim3((unsigned)(p.n_qb * units)), dim3(kWave * G), 0, s, p);
     else
-        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 8>), dim3((unsigned)units), dim3(kWave * G), 0, s, p);
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 8>), dim3((unsigned)(p.n_qb * units)), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

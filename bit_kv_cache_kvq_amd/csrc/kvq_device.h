@@ -73,6 +73,26 @@ __device__ __forceinline__ float wave_sum(float v)
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Bucket-relative RoPE (Dual-QK sec. 3.4 / C.4): rotate a head vector back by its bucket's
+// anchor.  Lane l holds channels CPL*l .. CPL*l+CPL-1; channel i < D/2 pairs with i + D/2,
+// which sits in lane l ^ 32.  cs = the bucket's (cos, sin) pairs [D/2][2].  With (c, s) of
+// pair i: y_i <- y_i c + y_{i+D/2} s, y_{i+D/2} <- y_{i+D/2} c - y_i s, each product rounded
+// before the sum (no contraction), as the format fixes.
+template <int CPL>
+__device__ __forceinline__ void anchor_rotate(float (&y)[CPL], const float *__restrict__ cs, int lane)
+{
+#pragma clang fp contract(off)
+    const bool upper = lane >= 32;
+#pragma unroll
+    for (int s = 0; s < CPL; s++) {
+        const float other = __shfl_xor(y[s], 32);
+        const float2 e = *reinterpret_cast<const float2 *>(cs + 2 * ((lane & 31) * CPL + s));
+        const float a = y[s] * e.x;
+        const float b = other * e.y;
+        y[s] = upper ? a - b : a + b;
+    }
+}
+
 __device__ __forceinline__ float uniformf(float v)
 {
     return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));

@@ -35,6 +35,8 @@ struct AppendParams {
     int q_end;    // positions below q_end (and >= n_sink) end up quantised by this append
     int evict;    // 1: quantise ring positions [len - ..., ) leaving the window (see the kernel)
     int e0;       // evict: first position to quantise; n_new positions from there
+    const float *rope_cs; // bucket-relative RoPE: (cos, sin) of each bucket's anchor [bucket][D/2][2]
+    int rope_lw;          // log2 of the bucket width, 0: off
 };
 
 struct DecodeParams {
@@ -56,6 +58,10 @@ struct DecodeParams {
     int n_units, tiles_per_unit, n_waves; // work split: n_waves >= n_units waves, wave w serves unit w % n_units
     int dynamic;        // 1: tiles from the unit counters; 0: member k of n takes k, k + n, ...
     int n_cu;           // compute units of the device (places of waves, see the decode kernel)
+    const float *rope_cs; // bucket-relative RoPE: (cos, sin) of each bucket's anchor [bucket][D/2][2]
+    int rope_lw;        // log2 of the bucket width, 0: off
+    int n_rb;           // query records per unit: one per bucket of the capacity (1 without RoPE)
+    int n_qb;           // buckets holding positions < len (query records the prep writes per unit)
 };
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);

@@ -25,6 +25,12 @@
  *     query-channel-group pruning: one mask per GQA group keeping the m 16-channel groups
  *     of largest query energy summed over the group's heads (Dual-QK sec. 3.2, C.2,
  *     App. A), and one softmax over all positions (Dual-QK sec. 3.4).
+ *   - Optional bucket-relative RoPE (Dual-QK sec. 3.4 and C.4): keys arrive with their
+ *     rotary embedding applied at their absolute position t and are stored relative to the
+ *     anchor a = w * floor(t / w) of their bucket (w = rope_bucket), i.e. rotated back by a;
+ *     decode rotates the query back by each bucket's anchor before scoring that bucket, so
+ *     every score equals the one of the un-bucketed keys before quantization.  The masks may
+ *     differ across buckets; all buckets share one softmax.
  *
  * Conventions for every entry point:
  *   - All buffer pointers are DEVICE pointers owned by the caller unless stated otherwise.
@@ -59,6 +65,10 @@
  *   recent_v u16 [U][n_recent][head_dim]  W holds the bf16 key (stored coordinates) / value
  *                                  of position t while t is one of the W most recent
  *                                  positions >= n_sink.
+ *   rope_cs  f32 [ceil(capacity / rope_bucket)][head_dim/2][2]  bucket-relative RoPE: entry
+ *                                  (b, i) = (cos, sin) of the anchor b*w times the model's
+ *                                  rotary frequency of channel pair i (its checkpoint's
+ *                                  frequencies, scaled ones included); filled by the caller.
  *   codebook f32 [16], thresholds f32 [15]  Lloyd-Max keys: centroids ascending and the
  *                                  decision thresholds; a rotated coordinate z codes to the
  *                                  number of thresholds strictly below z.
@@ -77,6 +87,10 @@
  *   per-token INT2 values: the range is clipped to [c*min, c*max] (c = v_clip, both ends
  *   scaled toward zero), scale = fp16((c*max - c*min) / 3), zero = fp16(c*min), codes as
  *   for the asymmetric groups (entries outside the clipped range saturate at 0 or 3).
+ *   bucket-relative RoPE (rotate-half pairing: channel i pairs with i + head_dim/2): with
+ *   (c, s) = rope_cs[t / w][i], k'_i = k_i*c + k_{i+d/2}*s and k'_{i+d/2} = k_{i+d/2}*c -
+ *   k_i*s (each product rounded, then the sum), before the Walsh-Hadamard rotation.  The
+ *   decode query of bucket b is rotated the same way with entry b.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -110,7 +124,8 @@ typedef enum { KVQ_V_ASYM4_G32 = 0, KVQ_V_ASYM2_TOKEN = 1 } kvq_vfmt;
  * 256 and at most 2^24; batch * n_kv_heads <= 65535; 0 <= n_sink <= 64 and n_sink < capacity; k_hadamard and k_ch0_bf16 in {0, 1};
  * k_ch0_bf16 requires an asymmetric key format and k_hadamard = 0; v_format is a
  * kvq_vfmt, and v_clip (per-token INT2 values only, otherwise ignored) lies in (0, 1];
- * 0 <= n_recent <= 1024.
+ * 0 <= n_recent <= 1024; rope_bucket is 0 (off) or a power of two in [128, 2^24], and needs
+ * rope_cs.
  * Pointers unused by the chosen format may be NULL (see kvq_buffer_bytes).              */
 typedef struct kvq_cache {
     int32_t batch, n_kv_heads, head_dim, capacity, n_sink;
@@ -131,6 +146,8 @@ typedef struct kvq_cache {
     int32_t n_recent;
     uint16_t *recent_k;
     uint16_t *recent_v;
+    int32_t rope_bucket;
+    const float *rope_cs;
 } kvq_cache;
 
 enum {
@@ -145,7 +162,8 @@ enum {
     KVQ_BUF_CODEBOOK = 8,
     KVQ_BUF_THRESHOLDS = 9,
     KVQ_BUF_RECENT_K = 10,
-    KVQ_BUF_RECENT_V = 11
+    KVQ_BUF_RECENT_V = 11,
+    KVQ_BUF_ROPE_CS = 12
 };
 
 /* Bytes the caller must allocate for buffer `which` (KVQ_BUF_*) of this geometry; 0 when
@@ -184,7 +202,11 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
  *            the lower group), 0 or >= head_dim/16 keeps all channels.  The mask applies to
  *            every key (sink tokens included) and never to values.
  *   out      [batch][n_q_heads][head_dim] fp32, device.
- *   mask_out nullable, [batch * n_kv_heads] bytes, bit p set = group p was read.
+ *   mask_out nullable, [batch * n_kv_heads] bytes, bit p set = group p was read.  With
+ *            bucket-relative RoPE: [batch * n_kv_heads][ceil(capacity / rope_bucket)] bytes,
+ *            entry (u, b) the mask of bucket b, written for b < ceil(len / rope_bucket).
+ *   q        with bucket-relative RoPE: the query with its rotary embedding applied at its
+ *            own position (as the keys were when appended).
  *   ws       workspace of ws_bytes >= kvq_decode_workspace_bytes(c, n_q_heads).
  * len = 0 writes zeros.  By default the waves serving one sequence and KV head take its
  * 128-position tiles in the order they ask for them, so the fp32 summation order, and the

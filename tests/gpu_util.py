@@ -19,8 +19,10 @@ def oracle_geo(oracle_mod, c: B.Cache, units=None):
     g = oracle_mod.Geometry(batch=c.c.batch, n_kv_heads=c.c.n_kv_heads, head_dim=c.c.head_dim,
                             capacity=c.c.capacity, n_sink=c.c.n_sink, k_format=c.c.k_format,
                             k_hadamard=c.c.k_hadamard, k_ch0_bf16=c.c.k_ch0_bf16,
-                            v_format=c.c.v_format, v_clip=float(c.c.v_clip), n_recent=c.c.n_recent)
-    return oracle_mod.OracleCache(g, units=units)
+                            v_format=c.c.v_format, v_clip=float(c.c.v_clip), n_recent=c.c.n_recent,
+                            rope_bucket=c.c.rope_bucket)
+    table = c.buffers["rope_cs"].view(torch.float32).cpu().numpy() if c.c.rope_bucket else None
+    return oracle_mod.OracleCache(g, units=units, rope_table=table)
 
 
 def gpu_arrays(c: B.Cache, u0=0, u1=None):

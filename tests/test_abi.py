@@ -30,11 +30,12 @@ def test_exports_every_declared_function():
 
 def _cache(**kw):
     c = dict(batch=2, n_kv_heads=3, head_dim=128, capacity=512, n_sink=0, k_format=0, k_hadamard=0,
-             k_ch0_bf16=0, len=0, v_format=0, v_clip=1.0, n_recent=0)
+             k_ch0_bf16=0, len=0, v_format=0, v_clip=1.0, n_recent=0, rope_bucket=0)
     c.update(kw)
     s = B.KvqCacheC(*[c[k] for k in ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink", "k_format",
                                       "k_hadamard", "k_ch0_bf16", "len")])
     s.v_format, s.v_clip, s.n_recent = c["v_format"], c["v_clip"], c["n_recent"]
+    s.rope_bucket = c["rope_bucket"]
     for name in B.BUF_NAMES:
         setattr(s, name, FAKE)
     return s
@@ -57,6 +58,10 @@ def test_buffer_bytes_follow_layout():
     assert nb[4:6] == [U * cap // 2 * 16 * 4, U * cap * 4]
     assert nb[10:] == [U * 256 * d * 2, U * 256 * d * 2]
     assert L.kvq_buffer_bytes(ctypes.byref(_cache()), 10) == 0
+    # bucket-relative RoPE: (cos, sin) per anchor and channel pair, ceil(capacity / w) anchors
+    assert L.kvq_buffer_bytes(ctypes.byref(_cache(rope_bucket=128)), 12) == 4 * (d // 2) * 2 * 4
+    assert L.kvq_buffer_bytes(ctypes.byref(_cache(rope_bucket=2048)), 12) == 1 * (d // 2) * 2 * 4
+    assert L.kvq_buffer_bytes(ctypes.byref(_cache()), 12) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -75,6 +80,10 @@ def test_buffer_bytes_follow_layout():
     (dict(v_format=1, v_clip=1.5), B.KVQ_ERR_ARG),
     (dict(n_recent=-1), B.KVQ_ERR_UNSUPPORTED),
     (dict(n_recent=1025), B.KVQ_ERR_UNSUPPORTED),
+    (dict(rope_bucket=-128), B.KVQ_ERR_ARG),
+    (dict(rope_bucket=64), B.KVQ_ERR_UNSUPPORTED),
+    (dict(rope_bucket=384), B.KVQ_ERR_UNSUPPORTED),
+    (dict(rope_bucket=1 << 25), B.KVQ_ERR_UNSUPPORTED),
 ])
 def test_validate_rejects(kw, code):
     assert B.lib().kvq_validate(ctypes.byref(_cache(**kw))) == code
@@ -89,6 +98,10 @@ def test_validate_pointers():
     s = _cache()
     s.k_codes = FAKE + 4
     assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_ERR_ALIGN
+    s = _cache(rope_bucket=256)
+    assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_OK
+    s.rope_cs = None
+    assert L.kvq_validate(ctypes.byref(s)) == B.KVQ_ERR_ARG
     s = _cache()
     s.k_norm = None  # unused by asymmetric keys
     s.codebook = None

@@ -1,4 +1,4 @@
-"""GPU parity on the six decode workloads at their full sizes, in the launch
+"""GPU parity on the seven decode workloads at their full sizes, in the launch
 configuration the bench times.
 
 The whole cache is built on the GPU; the oracle re-encodes sampled sequences and must match
@@ -21,7 +21,7 @@ def _build(w, extra=0):
     cap = w.capacity(extra)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
                 k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip,
-                n_recent=w.n_recent)
+                n_recent=w.n_recent, rope_bucket=w.rope_bucket, rope_table=synth.rope_table(w, cap))
     k, v = synth.prefill(w, device="cuda")
     note(f"workload {w.name}: prefill {tuple(k.shape)} {k.dtype}, capacity {cap}")
     c.append(k, v)
@@ -50,7 +50,8 @@ def _check_decode(c, w, ocs, q, what):
     for b, oc in ocs.items():
         qb = to_f32_np(q[b]).reshape(H, G, d)
         ref, rmask = oc.decode(qb, w.sm_scale, w.keep_groups)
-        np.testing.assert_array_equal(mask[b * H:(b + 1) * H].cpu().numpy(), rmask)
+        np.testing.assert_array_equal(mask.view(-1, c.rope_buckets)[b * H:(b + 1) * H].cpu().numpy()
+                                      .reshape(rmask.shape), rmask)
         worst = max(worst, compare_outputs(out[b], ref, f"{what} seq {b}"))
     note(f"  {what}: outputs within tolerance, worst err/||o|| = {worst:.2e}")
     return out, mask
@@ -93,6 +94,17 @@ def test_workload6_dualqk_storage_128k(oracle_mod):
     c, k, v = _build(w)
     ocs = _oracle_for(oracle_mod, c, w, k, v, [0, w.batch - 1])
     _check_decode(c, w, ocs, synth.query(w, 0, device="cuda"), "cfg6")
+
+
+def test_workload7_rope_buckets_128k(oracle_mod):
+    """Workload 6 with bucket-relative RoPE (buckets of 2048 positions, 64 per sequence): one
+    query record and mask per bucket, tiles of all buckets in one softmax."""
+    w = synth.WORKLOADS[7]
+    c, k, v = _build(w)
+    ocs = _oracle_for(oracle_mod, c, w, k, v, [0, w.batch - 1])
+    _, mask = _check_decode(c, w, ocs, synth.query(w, 0, device="cuda"), "cfg7")
+    m = mask.view(-1, c.rope_buckets)[:, :64].cpu().numpy()
+    assert len(np.unique(m)) > 1  # the buckets' masks differ
 
 
 def test_workload5_append_decode_steps(oracle_mod):

@@ -30,12 +30,13 @@ def _inputs(seed, Bsz, Hkv, T, d, dist="normal", dtype=torch.bfloat16, outliers=
 
 def _run(oracle_mod, *, d=128, kfmt=0, rot=0, ch0=0, ns=0, T=300, G=4, Hkv=2, Bsz=2, keep=0,
          dtype=torch.bfloat16, chunks=None, dist="normal", seed=0, cap=None, q_scale=1.0, outliers=(),
-         vfmt=0, vclip=0.92, nr=0):
+         vfmt=0, vclip=0.92, nr=0, rope=0):
     cap = cap or max(256, (T + 255) // 256 * 256)
     note(f"case d={d} kfmt={kfmt} rot={rot} ch0={ch0} ns={ns} T={T} G={G} Hkv={Hkv} B={Bsz} keep={keep} "
-         f"dtype={dtype} chunks={chunks} dist={dist} vfmt={vfmt} vclip={vclip} nr={nr}")
+         f"dtype={dtype} chunks={chunks} dist={dist} vfmt={vfmt} vclip={vclip} nr={nr} rope={rope}")
     c = B.Cache(Bsz, Hkv, d, cap, n_sink=ns, k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0,
-                v_format=vfmt, v_clip=vclip, n_recent=nr)
+                v_format=vfmt, v_clip=vclip, n_recent=nr, rope_bucket=rope,
+                rope_table=synth.rope_anchor_table(d, rope, cap) if rope else None)
     oc = oracle_geo(oracle_mod, c)
     k, v = _inputs(seed, Bsz, Hkv, T, d, dist, dtype, outliers)
     chunks = chunks or [T]
@@ -54,7 +55,7 @@ def _run(oracle_mod, *, d=128, kfmt=0, rot=0, ch0=0, ns=0, T=300, G=4, Hkv=2, Bs
     out, mask = c.decode(q.cuda(), sm, keep)
     torch.cuda.synchronize()
     ref, rmask = oc.decode(to_f32_np(q).reshape(Bsz * Hkv, G, d), sm, keep)
-    np.testing.assert_array_equal(mask.cpu().numpy(), rmask)
+    np.testing.assert_array_equal(mask.cpu().numpy().reshape(rmask.shape), rmask)
     worst = compare_outputs(out, ref, "decode")
     note(f"  ok, worst err/||o|| = {worst:.2e}")
     return c, oc, q, out
@@ -265,3 +266,33 @@ def test_recent_window_single_token_steps(oracle_mod):
     position; decoded after the last step, and with teams drawing tiles."""
     _run(oracle_mod, d=128, kfmt=0, G=4, ns=4, T=2100, nr=256, Hkv=1, Bsz=2, chunks=[2000] + [1] * 100,
          dist="t3", vfmt=1)
+
+
+# bucket-relative RoPE (Dual-QK sec. 3.4 / C.4): keys stored relative to their bucket's anchor,
+# one query record and mask per bucket, one softmax over all buckets
+@pytest.mark.parametrize("d,kfmt,rot,ch0,G,keep,ns,T,nr,vfmt,rope,chunks", [
+    (128, 0, 0, 1, 4, 5, 4, 1000, 0, 0, 128, [999, 1]),
+    (128, 0, 0, 1, 4, 5, 64, 1100, 256, 1, 256, [700, 1, 399]),
+    (128, 0, 0, 0, 4, 0, 0, 700, 0, 0, 128, None),
+    (128, 1, 0, 0, 8, 3, 2, 520, 0, 0, 128, [257, 263]),
+    (128, 2, 1, 0, 4, 6, 0, 900, 0, 0, 256, None),
+    (128, 2, 0, 0, 2, 0, 0, 300, 100, 0, 128, [150, 150]),
+    (64, 0, 0, 1, 1, 3, 3, 640, 200, 0, 128, [300, 340]),
+    (64, 2, 1, 0, 8, 2, 0, 333, 0, 1, 1024, None),
+])
+def test_rope_buckets(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, nr, vfmt, rope, chunks):
+    _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, keep=keep, ns=ns, T=T, nr=nr, vfmt=vfmt, rope=rope,
+         chunks=chunks, dtype=torch.float32 if d == 64 else torch.bfloat16)
+
+
+def test_rope_buckets_teams(oracle_mod):
+    """Long context on one unit (wave teams, striped, tiles drawn across buckets), heavy tails,
+    a window spanning a bucket edge; and forced splits."""
+    _run(oracle_mod, d=128, kfmt=0, ch0=1, G=4, keep=5, ns=4, T=9000, Hkv=1, Bsz=1, dist="t3", vfmt=1, nr=256,
+         rope=2048, chunks=[8100, 1, 899])
+    for tps in (1, 3):
+        B.set_split_tiles(tps)
+        try:
+            _run(oracle_mod, d=128, kfmt=0, G=4, keep=4, T=4000, Hkv=2, Bsz=1, seed=3, rope=512)
+        finally:
+            B.set_split_tiles(0)
