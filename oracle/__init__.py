@@ -32,7 +32,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
           "-fopenmp", "-Wall", "-Wextra"]
 
 K_ASYM2, K_ASYM4, K_LLOYD4, K_ASYM8 = 0, 1, 2, 3
-V_ASYM4_G32, V_ASYM2_TOKEN = 0, 1
+V_ASYM4_G32, V_ASYM2_TOKEN, V_KQV = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -72,7 +72,7 @@ def lib():
         L.oracle_tree_sum_f32.argtypes = [P, i]
         L.oracle_lloyd_max_gaussian.restype = i
         L.oracle_lloyd_max_gaussian.argtypes = [i, ctypes.c_double, i, P, P]
-        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, i, P, P, P, P, P, P, P, P, P, P, i, P]
+        cache_args = [i, i, i, i, i, i, i, ctypes.c_float, i, P, P, P, P, P, P, P, P, P, P, i, P, P, P, P]
         L.oracle_quant_append.argtypes = cache_args + [P, P, i, i, i, P, P]
         L.oracle_prune_mask.restype = ctypes.c_uint32
         L.oracle_prune_mask.argtypes = [P, i, i, i]
@@ -188,9 +188,12 @@ class Geometry:
 class OracleCache:
     """Host-side packed cache with the same byte layout the format defines."""
 
-    def __init__(self, geo: Geometry, units: int | None = None, rope_table: np.ndarray | None = None):
+    def __init__(self, geo: Geometry, units: int | None = None, rope_table: np.ndarray | None = None,
+                 qjl_signs: np.ndarray | None = None):
         """rope_table: bucket-relative RoPE's anchor (cos, sin) table, fp32
-        [geo.rope_buckets][d/2][2] (an input, like the keys)."""
+        [geo.rope_buckets][d/2][2] (an input, like the keys).  qjl_signs: KQV values' random
+        sign diagonal of the sketch, uint32 [d/32], bit i set = channel i negated (an input,
+        the random draw the method makes)."""
         self.geo = geo
         U = geo.units if units is None else units
         self.U = U
@@ -201,8 +204,9 @@ class OracleCache:
         self.k_sz = np.zeros((U, d // 32, cap), dtype=np.uint32)
         self.k_norm = np.zeros((U, cap), dtype=np.uint16)
         self.k_ch0 = np.zeros((U, cap), dtype=np.uint16)
-        per_token = geo.v_format == V_ASYM2_TOKEN
-        self.v_codes = np.zeros((U, cap // 2, d // 8 if per_token else d // 4), dtype=np.uint32)
+        per_token = geo.v_format in (V_ASYM2_TOKEN, V_KQV)
+        int2_tok = geo.v_format == V_ASYM2_TOKEN
+        self.v_codes = np.zeros((U, cap // 2, d // 8 if int2_tok else d // 4), dtype=np.uint32)
         self.v_sz = np.zeros((U, 1 if per_token else d // 32, cap), dtype=np.uint32)
         self.sink_k = np.zeros((U, ns, d), dtype=np.uint16)
         self.sink_v = np.zeros((U, ns, d), dtype=np.uint16)
@@ -216,6 +220,13 @@ class OracleCache:
             self.rope_cs = np.ascontiguousarray(rope_table, dtype=np.float32).reshape(geo.rope_buckets, d // 2, 2)
         else:
             self.rope_cs = np.zeros((1, 1, 2), dtype=np.float32)
+        self.vcent, self.vthr = codebook_f32(8)
+        if geo.v_format == V_KQV:
+            if qjl_signs is None:
+                raise ValueError("KQV values need the sketch's random signs")
+            self.qjl = np.ascontiguousarray(qjl_signs, dtype=np.uint32).reshape(d // 32)
+        else:
+            self.qjl = np.zeros(d // 32, dtype=np.uint32)
         if geo.k_format == K_LLOYD4:
             self.cent, self.thr = codebook_f32(16)
         else:
@@ -227,7 +238,8 @@ class OracleCache:
         return [g.head_dim, g.capacity, g.n_sink, g.k_format, g.k_hadamard, g.k_ch0_bf16,
                 g.v_format, float(g.v_clip), g.n_recent, _p(self.k_codes), _p(self.k_sz), _p(self.k_norm),
                 _p(self.k_ch0), _p(self.v_codes), _p(self.v_sz), _p(self.sink_k), _p(self.sink_v),
-                _p(self.recent_k), _p(self.recent_v), g.rope_bucket, _p(self.rope_cs)]
+                _p(self.recent_k), _p(self.recent_v), g.rope_bucket, _p(self.rope_cs),
+                _p(self.vcent), _p(self.vthr), _p(self.qjl)]
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):
         """k_new, v_new: fp32 [U, n_new, d]; writes positions [len, len+n_new)."""

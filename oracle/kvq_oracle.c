@@ -26,7 +26,10 @@
  *     query energy summed over the group's heads (Dual-QK sec. 3.2, sec. C.2, App. A);
  *   - values as asymmetric INT4 per 32-channel group, or as per-token asymmetric INT2
  *     with a clipping ratio (Dual-QK sec. 3.3 and sec. B.2: per-token INT2 values with
- *     0.92 clipping);
+ *     0.92 clipping), or KQV's value side: Walsh-Hadamard rotation, 3-bit Lloyd-Max codes
+ *     with an FP16 norm and a 1-bit QJL sketch of the residual through a randomised
+ *     Hadamard transform (KV-quantisation statistics, "Quantisierungsschemata" KQV and the
+ *     QJL variance statement; TurboQuant on Quantized Models, abstract: SRHT-QJL);
  *   - attention over the decoded cache with one softmax over all positions
  *     (Dual-QK sec. 3.4: bucket scores share one global softmax);
  *   - bucket-relative RoPE (Dual-QK sec. 3.4 and C.4): keys, given with their rotary
@@ -46,6 +49,7 @@
  * other than itself (library conversions, explicit Hadamard matrices, brute-force code
  * search, exhaustive subset search, closed forms, published Lloyd-Max tables).
  */
+#define _DEFAULT_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -61,7 +65,7 @@
  * check that 8-bit codes approach dense attention).  Value format ids: 0 = asymmetric INT4
  * per 32-channel group, 1 = per-token asymmetric INT2 with a clipping ratio.            */
 enum { OK_ASYM2 = 0, OK_ASYM4 = 1, OK_LLOYD4 = 2, OK_ASYM8 = 3 };
-enum { OV_ASYM4_G32 = 0, OV_ASYM2_TOKEN = 1 };
+enum { OV_ASYM4_G32 = 0, OV_ASYM2_TOKEN = 1, OV_KQV = 2 };
 
 static int key_bits(int kfmt) { return kfmt == OK_ASYM2 ? 2 : kfmt == OK_ASYM8 ? 8 : 4; }
 
@@ -293,6 +297,8 @@ typedef struct {
     int len; /* positions stored (decode: where the recent window starts) */
     int rope_w; /* bucket-relative RoPE: bucket width w (0: off) */
     const float *rope_cs; /* (cos, sin) of each bucket anchor's angles [bucket][d/2][2] */
+    const float *vcent, *vthr; /* KQV values: 8 centroids, 7 thresholds (fp32) */
+    const uint32_t *qjl; /* KQV values: the sketch's random signs, bit i set = channel i negated */
 } ocache;
 
 /* Bucket-relative RoPE (Dual-QK sec. 3.4 and C.4).  Reading: the rotary embedding pairs
@@ -463,6 +469,52 @@ static void quant_stored(const ocache *c, size_t u, int t, const float *y, const
     }
 
     uint8_t vc[256];
+    if (c->vfmt == OV_KQV) {
+        /* KQV values (KV-quantisation statistics, "Quantisierungsschemata": WHT, (n-1)-bit
+         * scalar MSE codes, 1-bit QJL sketch of the residual; TurboQuant on Quantized Models:
+         * the sketch matrix is a randomised Hadamard transform S = H D).  fp32 throughout:
+         *   y = FWHT(v); rho = fp16(sqrt(tree_sum(y^2) / d)); z = y / rho; code = number of
+         *   the 7 thresholds strictly below z; y^ = rho * cent[code]; r = y - y^;
+         *   sketch bit i = 1 when (H D r)_i < 0; gamma = fp16(sqrt(tree_sum(r^2))).
+         * Stored: nibble i = code_i | bit_i << 3 in the INT4 pair layout; v_sz = rho | gamma<<16. */
+        float y2[256], sq[256], r[256], w[256];
+        memcpy(y2, v, sizeof(float) * (size_t)d);
+        oracle_fwht_f32(y2, d);
+        for (int i = 0; i < d; i++)
+            sq[i] = y2[i] * y2[i];
+        float s2 = oracle_tree_sum_f32(sq, d);
+        uint16_t rh = oracle_f32_to_f16(sqrtf(s2 / (float)d));
+        float rf = oracle_f16_to_f32(rh);
+        float inv = rf > 0.0f ? 1.0f / rf : 0.0f;
+        for (int i = 0; i < d; i++) {
+            float z = y2[i] * inv;
+            int cnt = 0;
+            for (int j = 0; j < 7; j++)
+                if (z > c->vthr[j])
+                    cnt++;
+            vc[i] = (uint8_t)cnt;
+            float yh = rf * c->vcent[cnt];
+            r[i] = y2[i] - yh;
+            w[i] = ((c->qjl[i / 32] >> (i % 32)) & 1u) ? -r[i] : r[i];
+            sq[i] = r[i] * r[i];
+        }
+        oracle_fwht_f32(w, d);
+        float g2 = oracle_tree_sum_f32(sq, d);
+        uint16_t gh = oracle_f32_to_f16(sqrtf(g2));
+        for (int i = 0; i < d; i++)
+            vc[i] |= (uint8_t)((w[i] < 0.0f ? 1u : 0u) << 3);
+        c->v_sz[u * cap + (size_t)t] = (uint32_t)rh | ((uint32_t)gh << 16);
+        const size_t W4 = (size_t)(d / 4);
+        uint32_t *prow = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * W4;
+        const int s16 = (t & 1) ? 16 : 0;
+        for (size_t j = 0; j < W4; j++) {
+            uint32_t half = 0;
+            for (int k2 = 0; k2 < 4; k2++)
+                half |= (uint32_t)vc[4 * j + (size_t)k2] << (4 * k2);
+            prow[j] = (prow[j] & ~(0xFFFFu << s16)) | (half << s16);
+        }
+        return;
+    }
     if (c->vfmt == OV_ASYM2_TOKEN) {
         /* values: per-token asymmetric INT2 with clipping, pair-interleaved words */
         uint16_t sh, zh;
@@ -554,11 +606,12 @@ void oracle_quant_append(int d, int cap, int n_sink, int kfmt, int rotate, int c
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
                          uint16_t *recent_k, uint16_t *recent_v, int rope_w, const float *rope_cs,
+                         const float *vcent, const float *vthr, const uint32_t *qjl,
                          const float *cent, const float *thr, int n_units, int t0, int n_new,
                          const float *k_new, const float *v_new)
 {
     ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, thr, t0 + n_new, rope_w, rope_cs};
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, thr, t0 + n_new, rope_w, rope_cs, vcent, vthr, qjl};
 #pragma omp parallel for schedule(static)
     for (int u = 0; u < n_units; u++)
         for (int i = 0; i < n_new; i++) {
@@ -677,6 +730,28 @@ static void decode_value(const ocache *c, size_t u, int t, double *vh)
         return;
     }
     const int sh16 = (t & 1) ? 16 : 0;
+    if (c->vfmt == OV_KQV) {
+        /* y~ = rho cent[code] + sqrt(pi/2)/d * gamma * D H sigma (sigma_i = -1 for a set
+         * sketch bit: S^T sign(S r) with S = H D), then v^ = H y~ / d.  fp64.              */
+        const uint32_t *prow = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * (size_t)(d / 4);
+        uint32_t sz = c->v_sz[u * cap + (size_t)t];
+        double rf = (double)oracle_f16_to_f32((uint16_t)(sz & 0xFFFFu));
+        double gf = (double)oracle_f16_to_f32((uint16_t)(sz >> 16));
+        double hs[256];
+        for (int i = 0; i < d; i++) {
+            int nib = (int)(((prow[i / 4] >> sh16) >> (4 * (i % 4))) & 0xFu);
+            vh[i] = rf * (double)c->vcent[nib & 7];
+            hs[i] = (nib & 8) ? -1.0 : 1.0;
+        }
+        oracle_fwht_f64(hs, d);
+        const double k = sqrt(M_PI / 2.0) / (double)d * gf;
+        for (int i = 0; i < d; i++)
+            vh[i] += k * (((c->qjl[i / 32] >> (i % 32)) & 1u) ? -hs[i] : hs[i]);
+        oracle_fwht_f64(vh, d);
+        for (int i = 0; i < d; i++)
+            vh[i] /= (double)d;
+        return;
+    }
     if (c->vfmt == OV_ASYM2_TOKEN) {
         const uint32_t *row2 = c->v_codes + (u * (cap / 2) + (size_t)(t / 2)) * (size_t)(d / 8);
         uint32_t sz = c->v_sz[u * cap + (size_t)t];
@@ -708,10 +783,11 @@ void oracle_dequant_unit(int d, int cap, int n_sink, int kfmt, int rotate, int c
                          uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                          uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
                          uint16_t *recent_k, uint16_t *recent_v, int rope_w, const float *rope_cs,
+                         const float *vcent, const float *vthr, const uint32_t *qjl,
                          const float *cent, int unit, int len, double *kh, double *vh)
 {
     ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len, rope_w, rope_cs};
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len, rope_w, rope_cs, vcent, vthr, qjl};
     for (int t = 0; t < len; t++) {
         decode_key(&c, (size_t)unit, t, kh + (size_t)t * (size_t)d);
         decode_value(&c, (size_t)unit, t, vh + (size_t)t * (size_t)d);
@@ -737,12 +813,13 @@ void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch
                         uint32_t *k_codes, uint32_t *k_sz, uint16_t *k_norm, uint16_t *k_ch0,
                         uint32_t *v_codes, uint32_t *v_sz, uint16_t *sink_k, uint16_t *sink_v,
                          uint16_t *recent_k, uint16_t *recent_v, int rope_w, const float *rope_cs,
+                         const float *vcent, const float *vthr, const uint32_t *qjl,
                         const float *cent, int n_units, int len, int G, const float *q,
                         double sm, int keep_groups, double *out, uint8_t *mask_out,
                         double *logits_out)
 {
     ocache c = {d, cap, n_sink, kfmt, rotate, ch0, vfmt, vclip, n_recent, k_codes, k_sz, v_codes, v_sz,
-                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len, rope_w, rope_cs};
+                k_norm, k_ch0, sink_k, sink_v, recent_k, recent_v, cent, 0, len, rope_w, rope_cs, vcent, vthr, qjl};
 #pragma omp parallel for schedule(dynamic, 1)
     for (int u = 0; u < n_units; u++) {
         const float *qu = q + (size_t)u * (size_t)G * (size_t)d;
