@@ -68,7 +68,7 @@ def decode_bytes_unit(w, length, mask, bf16=True):
             k_tok += 4 * sum(1 for g in range(d // 32) if kept[2 * g] or kept[2 * g + 1])
             if w.k_ch0_bf16 and kept[0]:
                 k_tok += 2
-        v_tok = d // 4 + 4 if w.v_format == 1 else d // 2 + 4 * (d // 32)
+        v_tok = {1: d // 4 + 4, 2: d // 2 + 4}.get(w.v_format, d // 2 + 4 * (d // 32))
         return k_tok + v_tok
 
     ns = min(w.n_sink, length)
@@ -174,7 +174,8 @@ def cpu_baseline(w, length, budget_s):
                           n_sink=w.n_sink, k_format=w.k_format, k_hadamard=w.k_hadamard,
                           k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip, n_recent=w.n_recent,
                           rope_bucket=w.rope_bucket)
-    oc = oracle.OracleCache(geo, rope_table=synth.rope_table(w, geo.capacity))
+    oc = oracle.OracleCache(geo, rope_table=synth.rope_table(w, geo.capacity),
+                            qjl_signs=synth.qjl_signs(w.head_dim) if w.v_format == 2 else None)
     prefill_len = length - (1 if w.steps else 0)
     k, v = synth.prefill(w, device="cpu", context=prefill_len, batch=nseq)
     oc.append(k.float().numpy().reshape(nseq * H, prefill_len, w.head_dim),
@@ -224,7 +225,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=128)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -294,7 +295,8 @@ def main():
     cap = w.capacity(appends)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
                 k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, device=dev, v_format=w.v_format,
-                v_clip=w.v_clip, n_recent=w.n_recent, rope_bucket=w.rope_bucket, rope_table=synth.rope_table(w, cap))
+                v_clip=w.v_clip, n_recent=w.n_recent, rope_bucket=w.rope_bucket, rope_table=synth.rope_table(w, cap),
+                qjl_signs=synth.qjl_signs(w.head_dim) if w.v_format == 2 else None)
     log(f"workload {w.name}: capacity {cap}, building cache ...")
     k, v = synth.prefill(w, device=dev)
     c.append(k, v)
@@ -392,7 +394,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.context, "positions_attended_last_step": lens[-1],
                    "key_format": ["asym_int2", "asym_int4", "wht_lloyd4"][w.k_format],
-                   "value_format": "asym_int2_token_clip%.2f" % w.v_clip if w.v_format == 1 else "asym_int4_g32",
+                   "value_format": {1: "asym_int2_token_clip%.2f" % w.v_clip, 2: "kqv_wht_lloyd3_qjl1"}.get(
+                       w.v_format, "asym_int4_g32"),
                    "channel0_bf16": bool(w.k_ch0_bf16), "sink_tokens": w.n_sink, "recent_bf16_tokens": w.n_recent,
                    "rope_bucket": w.rope_bucket,
                    "keep_groups": w.keep_groups, "appends_per_step": 1 if w.steps else 0,

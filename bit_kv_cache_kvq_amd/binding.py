@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -18,9 +19,10 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY = 0, -1, -2, -3
 KVQ_ERR_WORKSPACE, KVQ_ERR_ALIGN, KVQ_ERR_HIP = -4, -5, -6
 KVQ_F32, KVQ_BF16 = 0, 1
 K_ASYM2, K_ASYM4, K_LLOYD4 = 0, 1, 2
-V_ASYM4_G32, V_ASYM2_TOKEN = 0, 1
+V_ASYM4_G32, V_ASYM2_TOKEN, V_KQV = 0, 1, 2
 BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", "sink_v",
-             "codebook", "thresholds", "recent_k", "recent_v", "rope_cs"]  # KVQ_BUF_* order
+             "codebook", "thresholds", "recent_k", "recent_v", "rope_cs",
+             "v_codebook", "v_thresholds", "v_qjl_signs"]  # KVQ_BUF_* order
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles", "kvq_set_deterministic",
            "kvq_set_decode_events", "kvq_probe_stream_read",
@@ -33,7 +35,8 @@ class KvqCacheC(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in BUF_NAMES[:10]] + \
                [("v_format", ctypes.c_int32), ("v_clip", ctypes.c_float), ("n_recent", ctypes.c_int32)] + \
                [(n, ctypes.c_void_p) for n in BUF_NAMES[10:12]] + \
-               [("rope_bucket", ctypes.c_int32), ("rope_cs", ctypes.c_void_p)]
+               [("rope_bucket", ctypes.c_int32), ("rope_cs", ctypes.c_void_p)] + \
+               [(n, ctypes.c_void_p) for n in BUF_NAMES[13:]]
 
 
 class KvqError(RuntimeError):
@@ -140,10 +143,11 @@ class Cache:
 
     def __init__(self, batch, n_kv_heads, head_dim, capacity, n_sink=0, k_format=K_ASYM2,
                  k_hadamard=0, k_ch0_bf16=0, device="cuda", v_format=V_ASYM4_G32, v_clip=1.0, n_recent=0,
-                 rope_bucket=0, rope_table=None):
+                 rope_bucket=0, rope_table=None, qjl_signs=None):
         """rope_bucket: bucket width w of bucket-relative RoPE (0: off); rope_table: the model's
         (cos, sin) of every bucket anchor, float32 [ceil(capacity / w)][head_dim / 2][2]
-        (copied into the cache's rope_cs buffer)."""
+        (copied into the cache's rope_cs buffer).  qjl_signs: KQV values' random sign diagonal,
+        uint32 [head_dim / 32], bit i set = channel i negated (copied into v_qjl_signs)."""
         self.c = KvqCacheC(batch, n_kv_heads, head_dim, capacity, n_sink, k_format, k_hadamard,
                            k_ch0_bf16, 0)
         self.c.v_format = int(v_format)
@@ -163,6 +167,14 @@ class Cache:
             cent, thr = codebook_gaussian(4)
             self.buffers["codebook"].view(torch.float32).copy_(torch.tensor(cent, dtype=torch.float32))
             self.buffers["thresholds"].view(torch.float32).copy_(torch.tensor(thr, dtype=torch.float32))
+        if v_format == V_KQV:
+            if qjl_signs is None:
+                raise ValueError("KQV values need the sketch's random signs")
+            cent, thr = codebook_gaussian(3)
+            self.buffers["v_codebook"].view(torch.float32).copy_(torch.tensor(cent, dtype=torch.float32))
+            self.buffers["v_thresholds"].view(torch.float32).copy_(torch.tensor(thr, dtype=torch.float32))
+            sg = torch.as_tensor(np.asarray(qjl_signs, dtype=np.uint32).view(np.int32).reshape(-1))
+            self.buffers["v_qjl_signs"].view(torch.int32).copy_(sg.to(self.device))
         if rope_bucket:
             if rope_table is None:
                 raise ValueError("bucket-relative RoPE needs its anchor table")

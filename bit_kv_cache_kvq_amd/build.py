@@ -15,7 +15,8 @@ LIB = os.path.join(HERE, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_v2.hip", "kvq_probe.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_v2.hip", "kvq_decode_v3.hip",
+           "kvq_probe.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are disabled for all device code
@@ -28,6 +29,7 @@ FLAGS = [
 SOURCE_FLAGS: dict[str, list[str]] = {
     "kvq_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
     "kvq_decode_v2.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+    "kvq_decode_v3.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 BUILD_DIR = os.path.join(HERE, "_build")
 

@@ -46,7 +46,7 @@ kvq_status check_geometry(const kvq_cache *c)
         return KVQ_ERR_ARG;
     if (c->k_ch0_bf16 && (c->k_hadamard || c->k_format == KVQ_K_LLOYD4))
         return KVQ_ERR_UNSUPPORTED;
-    if (c->v_format != KVQ_V_ASYM4_G32 && c->v_format != KVQ_V_ASYM2_TOKEN)
+    if (c->v_format != KVQ_V_ASYM4_G32 && c->v_format != KVQ_V_ASYM2_TOKEN && c->v_format != KVQ_V_KQV)
         return KVQ_ERR_ARG;
     if (c->v_format == KVQ_V_ASYM2_TOKEN && !(c->v_clip > 0.0f && c->v_clip <= 1.0f))
         return KVQ_ERR_ARG;
@@ -100,7 +100,7 @@ size_t buffer_bytes(const kvq_cache *c, int which)
     case KVQ_BUF_K_NORM: return lloyd ? U * cap * 2 : 0;
     case KVQ_BUF_K_CH0: return c->k_ch0_bf16 ? U * cap * 2 : 0;
     case KVQ_BUF_V_CODES: return U * (cap / 2) * (c->v_format == KVQ_V_ASYM2_TOKEN ? d / 8 : d / 4) * 4;
-    case KVQ_BUF_V_SZ: return U * (c->v_format == KVQ_V_ASYM2_TOKEN ? 1 : d / 32) * cap * 4;
+    case KVQ_BUF_V_SZ: return U * (c->v_format == KVQ_V_ASYM4_G32 ? d / 32 : 1) * cap * 4;
     case KVQ_BUF_SINK_K:
     case KVQ_BUF_SINK_V: return U * ns * d * 2;
     case KVQ_BUF_CODEBOOK: return lloyd ? 16 * 4 : 0;
@@ -108,16 +108,20 @@ size_t buffer_bytes(const kvq_cache *c, int which)
     case KVQ_BUF_RECENT_K:
     case KVQ_BUF_RECENT_V: return U * (size_t)c->n_recent * d * 2;
     case KVQ_BUF_ROPE_CS: return c->rope_bucket > 0 ? (size_t)rope_buckets(c) * (d / 2) * 2 * 4 : 0;
+    case KVQ_BUF_V_CODEBOOK: return c->v_format == KVQ_V_KQV ? 8 * 4 : 0;
+    case KVQ_BUF_V_THRESHOLDS: return c->v_format == KVQ_V_KQV ? 7 * 4 : 0;
+    case KVQ_BUF_V_QJL_SIGNS: return c->v_format == KVQ_V_KQV ? d / 32 * 4 : 0;
     default: return 0;
     }
 }
 
 kvq_status check_buffers(const kvq_cache *c)
 {
-    const void *ptrs[13] = {c->k_codes,  c->k_sz,       c->k_norm,   c->k_ch0,    c->v_codes,
-                            c->v_sz,     c->sink_k,     c->sink_v,   c->codebook, c->thresholds,
-                            c->recent_k, c->recent_v,   c->rope_cs};
-    for (int i = 0; i < 13; i++) {
+    const void *ptrs[16] = {c->k_codes,  c->k_sz,       c->k_norm,     c->k_ch0,      c->v_codes,
+                            c->v_sz,     c->sink_k,     c->sink_v,     c->codebook,   c->thresholds,
+                            c->recent_k, c->recent_v,   c->rope_cs,    c->v_codebook, c->v_thresholds,
+                            c->v_qjl_signs};
+    for (int i = 0; i < 16; i++) {
         if (buffer_bytes(c, i) == 0)
             continue;
         if (!ptrs[i])
@@ -248,6 +252,9 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
     p.e0 = 0;
     p.rope_cs = c->rope_cs;
     p.rope_lw = rope_log2(c);
+    p.v_codebook = c->v_codebook;
+    p.v_thresholds = c->v_thresholds;
+    p.v_qjl = c->v_qjl_signs;
     // recent window: first quantise the ring positions that leave it (their slots are
     // overwritten by the new positions of the second launch)
     const int q_old = quant_end(c, c->len);
@@ -366,6 +373,8 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.n_cu = device_cus();
     p.rope_cs = c->rope_cs;
     p.rope_lw = rope_log2(c);
+    p.v_codebook = c->v_codebook;
+    p.v_qjl = c->v_qjl_signs;
     p.n_rb = rope_buckets(c);
     p.n_qb = c->rope_bucket > 0 && c->len > 0 ? (c->len + c->rope_bucket - 1) / c->rope_bucket : 1;
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};

@@ -242,6 +242,71 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
             p.k_codes[((size_t)u * (size_t)rows + (size_t)(lane / lanes)) * cap + (size_t)t] = word;
     }
 
+    // ---- values, KQV (Statistical Inference ... Inspired by TurboQuant, scheme KQV; TurboQuant
+    // on Quantized Models, abstract: SRHT-QJL): y = FWHT(v), 3-bit Lloyd-Max codes of y / rho
+    // (rho = RMS of y, fp16, as for keys), residual r = y - rho cent[code], sketch bits = signs
+    // of FWHT(D r), residual norm in fp16; nibble = code | bit << 3 in the INT4 pair layout
+    if (p.vfmt == KVQ_V_KQV) {
+        float y[CPL], sq[CPL], r[CPL], w[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            y[s] = v[s];
+        fwht<CPL>(y, lane);
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            sq[s] = y[s] * y[s];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                sq[s] = sq[s] + __shfl_xor(sq[s], m);
+        }
+        float s2 = sq[0];
+        if constexpr (CPL == 2)
+            s2 = sq[0] + sq[1];
+        const uint32_t rh = f32_to_f16(__builtin_sqrtf(s2 / (float)D));
+        const float rf = f16_to_f32(rh);
+        const float inv = rf > 0.0f ? 1.0f / rf : 0.0f;
+        uint32_t vc[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++) {
+            const float z = y[s] * inv;
+            uint32_t c = 0;
+#pragma unroll
+            for (int j = 0; j < 7; j++)
+                c += (z > p.v_thresholds[j]) ? 1u : 0u;
+            vc[s] = c;
+            const float yh = rf * p.v_codebook[c];
+            r[s] = y[s] - yh;
+            const int ch = lane * CPL + s;
+            w[s] = ((p.v_qjl[ch / 32] >> (ch % 32)) & 1u) ? -r[s] : r[s];
+            sq[s] = r[s] * r[s];
+        }
+        fwht<CPL>(w, lane);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                sq[s] = sq[s] + __shfl_xor(sq[s], m);
+        }
+        float g2 = sq[0];
+        if constexpr (CPL == 2)
+            g2 = sq[0] + sq[1];
+        const uint32_t gh = f32_to_f16(__builtin_sqrtf(g2));
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            vc[s] |= (w[s] < 0.0f ? 1u : 0u) << 3;
+        if (lane == 0)
+            p.v_sz[(size_t)u * cap + (size_t)t] = rh | (gh << 16);
+        const int lanes = 16 / (4 * CPL); // lanes forming one 16-bit half (4 channels)
+        const uint32_t half = pack_run<CPL>(vc, 4, lanes, lane);
+        if ((lane % lanes) == 0) {
+            const size_t word = ((size_t)u * (cap / 2) + (size_t)(t >> 1)) * (D / 4) + (size_t)(lane / lanes);
+            reinterpret_cast<uint16_t *>(p.v_codes)[word * 2 + (size_t)(t & 1)] = (uint16_t)half;
+        }
+        return;
+    }
+
     // ---- values, per-token INT2: range [c*min, c*max] over the whole token, codes against
     // the fp16 scale and zero, 8 channels per 16-bit half of a token-pair word
     if (p.vfmt == KVQ_V_ASYM2_TOKEN) {

@@ -69,8 +69,9 @@ struct Cfg {
     static constexpr int TILE = 64 * TPL;
     static constexpr int PAIRS = TILE / 2;
     static constexpr int NGV = VF == KVQ_V_ASYM4_G32 ? D / 32 : 1;  // value scale groups
-    static constexpr int WPP = VF == KVQ_V_ASYM4_G32 ? D / 4 : D / 8; // value words per position pair
-    static constexpr int VW = VF == KVQ_V_ASYM4_G32 ? 2 : 1;          // value words per lane per iteration
+    static constexpr int NWG = VF == KVQ_V_KQV ? 2 : NGV;              // weight sets (KQV: rho, residual norm)
+    static constexpr int WPP = VF == KVQ_V_ASYM2_TOKEN ? D / 8 : D / 4; // value words per position pair
+    static constexpr int VW = VF == KVQ_V_ASYM2_TOKEN ? 1 : 2;          // value words per lane per iteration
     static_assert(WPP / VW * 8 == D, "a value lane owns 8 channels");
     static constexpr int LPP = WPP / VW;           // value lanes per pair
     static constexpr int PPI = 64 / LPP;           // pairs per value iteration
@@ -560,9 +561,10 @@ template <int D, int G, int KF, int VF>
 struct Smem {
     using C = Cfg<D, G, KF, VF>;
     uint32_t lut[KF == KVQ_K_LLOYD4 ? 256 : 1];      // Lloyd-Max code-pair table (fp16x2)
+    uint32_t vlut[VF == KVQ_V_KQV ? 256 : 1];        // KQV values: (cent[lo & 7], cent[hi & 7]) per byte
     float sink_p[G][kMaxSink];
     union {
-        uint4 w[C::NGV][C::PAIRS + 1][C::WV];        // fp16 weight pairs: [group][pair][heads]
+        uint4 w[C::NWG][C::PAIRS + 1][C::WV];        // fp16 weight pairs: [group][pair][heads]
         float4 red[2 * kWave];                       // end of the tiles: 64 lanes x 8 floats
     };
 };
@@ -948,9 +950,62 @@ __device__ __forceinline__ void combine_stripe(const DecodeParams &p, int first,
 // per-unit counter that the query-prep kernel zeroes.  A unit served by one wave gets its
 // normalised output from it; otherwise each member writes one partial softmax state
 // (m, l, o) in the slot of its place, and the last member to finish combines them.
+// Unnormalised Walsh-Hadamard transform of D values held 8 per lane by lanes 0 .. D/8 - 1
+// (lane l: values 8l .. 8l + 7): in-lane stages, then xor shuffles between lanes.  Every lane
+// of the wave takes part (lanes past D/8 exchange among themselves only).
+template <int D>
+__device__ __forceinline__ void fwht8_lanes(float (&v)[8], int lane)
+{
+#pragma unroll
+    for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if ((j & hs) == 0) {
+                const float a = v[j], b = v[j + hs];
+                v[j] = a + b;
+                v[j + hs] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < D / 8; m <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float other = __shfl_xor(v[j], m);
+            v[j] = (lane & m) ? other - v[j] : v[j] + other;
+        }
+}
+
+// KQV values: the weighted sums over a wave's positions, in the rotated coordinates, are
+// A = sum_t p_t rho_t cent[code_t] (o on entry) and, per channel, the sketch-bit sums
+// b_j = sum_t p_t gamma_t bit_t (scaled by the halves' place values) with g = sum_t p_t gamma_t.
+// The QJL estimator and the inverse rotation are linear, so they apply once here:
+//   o = FWHT(A + sqrt(pi/2)/D * D_qjl FWHT(g - 2 b)) / D.
+template <int D>
+__device__ __forceinline__ void kqv_out(float (&o)[8], const float (&b)[8], float g, int lane, const uint32_t *qjl)
+{
+    constexpr int LPP = D / 8;
+    float h[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float place = (j & 3) == 0 ? 2097152.0f : (j & 3) == 1 ? 131072.0f : 8192.0f; // 2^21, 2^17, 2^13
+        h[j] = lane < LPP ? g - 2.0f * (b[j] * place) : 0.0f;
+    }
+    fwht8_lanes<D>(h, lane);
+    const float c = 1.2533141373155003f / (float)D; // sqrt(pi / 2) / D
+    const uint32_t sw = lane < LPP ? qjl[lane / 4] >> (8 * (lane % 4)) : 0u; // this lane's 8 sign bits
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        o[j] = fmaf(c, ((sw >> j) & 1u) ? -h[j] : h[j], lane < LPP ? o[j] : 0.0f);
+    fwht8_lanes<D>(o, lane);
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        o[j] *= 1.0f / (float)D;
+}
+
 template <int D, int G, int KF, int VF>
 __global__ __launch_bounds__(kWave)
-__attribute__((amdgpu_waves_per_eu((G < 4 || (G == 4 && KF != KVQ_K_ASYM4)) ? 3 : 2)))
+// (KQV values keep a second set of per-channel sums: fewer waves, no spills)
+__attribute__((amdgpu_waves_per_eu(VF == KVQ_V_KQV ? (G <= 2 ? 3 : G == 4 ? 2 : 1)
+                                                   : (G < 4 || (G == 4 && KF != KVQ_K_ASYM4)) ? 3 : 2)))
 void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 {
     using C = Cfg<D, G, KF, VF>;
@@ -958,6 +1013,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     constexpr int TPL = C::TPL, TILE = C::TILE, WPP = C::WPP, LPP = C::LPP, PPI = C::PPI;
     constexpr int VIT = C::VIT, VW = C::VW, WV = C::WV;
     constexpr bool V2 = VF == KVQ_V_ASYM2_TOKEN; // per-token INT2 values
+    constexpr bool KQ = VF == KVQ_V_KQV;         // KQV values (3-bit codes + sketch bits)
     using VWord = std::conditional_t<V2, uint32_t, uint2>; // a lane's value words of one pair
     __shared__ Smem<D, G, KF, VF> sm;
 
@@ -976,9 +1032,15 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             sm.lut[e] = pack_f16x2(p.codebook[e & 15], p.codebook[e >> 4]);
         __syncthreads();
     }
+    if constexpr (KQ) {
+        // byte (code nibble of token 2P, code nibble of token 2P+1) -> fp16 centroid pair
+        for (int e = lane; e < 256; e += kWave)
+            sm.vlut[e] = pack_f16x2(p.v_codebook[e & 7], p.v_codebook[(e >> 4) & 7]);
+        __syncthreads();
+    }
 
     const int vs = lane % LPP;         // value slot: channels 8*vs .. 8*vs+7
-    const int vgrp = V2 ? 0 : vs / 4;  // its scale group
+    const int vgrp = (V2 || KQ) ? 0 : vs / 4;  // its scale group (one per token for INT2 and KQV)
     const uint32_t vvo = ((uint32_t)(lane / LPP) * WPP + (uint32_t)(VW * vs)) * 4u; // value word offset
     const int q_lo = p.n_sink, q_hi = p.q_end; // quantized positions [q_lo, q_hi)
 
@@ -1005,6 +1067,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 
     // ---- running softmax state of the current unit
     float acc[G][8];
+    float bacc[G][KQ ? 8 : 1]; // KQV: sketch-bit sums per channel
     float zacc[G][NGV];
     float lsum[G];
     float mrun[G], mthr[G];
@@ -1020,6 +1083,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
             for (int g = 0; g < NGV; g++)
                 zacc[h][g] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < (KQ ? 8 : 1); j++)
+                bacc[h][j] = 0.0f;
         }
     };
 
@@ -1058,14 +1124,36 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
             for (int g = 0; g < NGV; g++)
                 zs[g] = wave_sum_dpp(zacc[h][g]);
+            float o[8] = {acc[h][0], acc[h][1], acc[h][2], acc[h][3], acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
             if (lane < LPP) {
-                float o[8] = {acc[h][0], acc[h][1], acc[h][2], acc[h][3], acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
 #pragma unroll
                 for (int k = 1; k < 64 / LPP; k++) {
                     const float4 a0 = red[2 * (lane + k * LPP)], a1 = red[2 * (lane + k * LPP) + 1];
                     o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
                     o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
                 }
+            }
+            if constexpr (KQ) {
+                // the sketch-bit sums, reduced the same way, then the estimator and the
+                // inverse rotation (every lane takes part in the shuffles)
+                __syncthreads();
+                red[2 * lane] = make_float4(bacc[h][0], bacc[h][1], bacc[h][2], bacc[h][3]);
+                red[2 * lane + 1] = make_float4(bacc[h][4], bacc[h][5], bacc[h][6], bacc[h][7]);
+                __syncthreads();
+                float bs[8] = {bacc[h][0], bacc[h][1], bacc[h][2], bacc[h][3],
+                               bacc[h][4], bacc[h][5], bacc[h][6], bacc[h][7]};
+                if (lane < LPP) {
+#pragma unroll
+                    for (int k = 1; k < 64 / LPP; k++) {
+                        const float4 a0 = red[2 * (lane + k * LPP)], a1 = red[2 * (lane + k * LPP) + 1];
+                        bs[0] += a0.x; bs[1] += a0.y; bs[2] += a0.z; bs[3] += a0.w;
+                        bs[4] += a1.x; bs[5] += a1.y; bs[6] += a1.z; bs[7] += a1.w;
+                    }
+                }
+                kqv_out<D>(o, bs, zs[0], lane, p.v_qjl);
+            }
+            if (lane < LPP) {
+                if constexpr (!KQ) {
                 // INT4: even slots summed code_even + 16 code_odd, odd slots 16 code_odd.
                 // INT2: slots 4k..4k+3 summed c0 + 4 c1, 4 c1, 16 c2 + 64 c3, 64 c3.  Either
                 // way an even slot takes out the next slot's sums, and the scales undo the
@@ -1081,6 +1169,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     else
                         sc = (j & 1) ? 1048576.0f : 16777216.0f; // undo 2^-20 / 2^-24
                     o[j] = o[j] * sc + zs[V2 ? 0 : (8 * lane + j) / 32];
+                }
                 }
                 if (whole) {
                     // fold in the sink positions' state, then normalise
@@ -1311,6 +1400,11 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
                     for (int gg = 0; gg < NGV; gg++)
                         zacc[h][gg] *= alpha;
+                    if constexpr (KQ) {
+#pragma unroll
+                        for (int j = 0; j < 8; j++)
+                            bacc[h][j] *= alpha;
+                    }
                 }
             }
             // (a running maximum still at -inf means every logit so far, this tile's included,
@@ -1349,6 +1443,15 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
                 for (int v4 = 0; v4 < WV; v4++)
                     sm.w[gg][lane][v4] = make_uint4(wq[4 * v4], wq[4 * v4 + 1], wq[4 * v4 + 2], wq[4 * v4 + 3]);
+                if constexpr (KQ) {
+                    // KQV: the second weight set, p * (residual norm), for the sketch bits
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        wq[h] = mul_f16x2(ph[h], zp);
+#pragma unroll
+                    for (int v4 = 0; v4 < WV; v4++)
+                        sm.w[1][lane][v4] = make_uint4(wq[4 * v4], wq[4 * v4 + 1], wq[4 * v4 + 2], wq[4 * v4 + 3]);
+                }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -1369,7 +1472,38 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     wv[4 * v4 + 2] = t4.z;
                     wv[4 * v4 + 3] = t4.w;
                 }
-                if constexpr (V2) {
+                if constexpr (KQ) {
+                    // KQV: nibble k of each half = 3-bit code | sketch bit << 3 of channel
+                    // 8*vs + 4*q2 + k.  Centroid pairs of the two positions from the LDS table;
+                    // the sketch bits masked in place are exact fp16 halves 2^-21, 2^-17, 2^-13
+                    // (nibble 3 moved down by 4 bits) summed with the p * gamma weights.
+                    uint32_t wb[4 * WV];
+#pragma unroll
+                    for (int v4 = 0; v4 < WV; v4++) {
+                        const uint4 t4 = sm.w[1][pl][v4];
+                        wb[4 * v4 + 0] = t4.x;
+                        wb[4 * v4 + 1] = t4.y;
+                        wb[4 * v4 + 2] = t4.z;
+                        wb[4 * v4 + 3] = t4.w;
+                    }
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; q2++) {
+                        const uint32_t x = q2 == 0 ? vv.x : vv.y;
+                        uint32_t cp[4];
+#pragma unroll
+                        for (int k = 0; k < 4; k++)
+                            cp[k] = sm.vlut[((x >> (4 * k)) & 0xFu) | ((x >> (12 + 4 * k)) & 0xF0u)];
+                        const uint32_t sb[4] = {x & 0x00080008u, x & 0x00800080u, x & 0x08000800u,
+                                                (x >> 4) & 0x08000800u};
+#pragma unroll
+                        for (int h = 0; h < G; h++)
+#pragma unroll
+                            for (int k = 0; k < 4; k++) {
+                                acc[h][4 * q2 + k] = dot2(cp[k], wv[h], acc[h][4 * q2 + k]);
+                                bacc[h][4 * q2 + k] = dot2(sb[k], wb[h], bacc[h][4 * q2 + k]);
+                            }
+                    }
+                } else if constexpr (V2) {
                     // per-token INT2: the word holds channels 8*vs .. +7 of both positions
                     // (halves), 4 two-bit codes per byte.  c0 = x & 0x000F000F is code0 +
                     // 4 code1, c1 = 4 code1, c2 = 16 code2 + 64 code3, c3 = 64 code3 (all

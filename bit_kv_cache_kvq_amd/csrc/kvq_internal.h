@@ -37,6 +37,8 @@ struct AppendParams {
     int e0;       // evict: first position to quantise; n_new positions from there
     const float *rope_cs; // bucket-relative RoPE: (cos, sin) of each bucket's anchor [bucket][D/2][2]
     int rope_lw;          // log2 of the bucket width, 0: off
+    const float *v_codebook, *v_thresholds; // KQV values: 8 centroids, 7 thresholds
+    const uint32_t *v_qjl;                  // KQV values: the sketch's sign diagonal (bit set: -1)
 };
 
 struct DecodeParams {
@@ -62,6 +64,8 @@ struct DecodeParams {
     int rope_lw;        // log2 of the bucket width, 0: off
     int n_rb;           // query records per unit: one per bucket of the capacity (1 without RoPE)
     int n_qb;           // buckets holding positions < len (query records the prep writes per unit)
+    const float *v_codebook; // KQV values: 8 centroids
+    const uint32_t *v_qjl;   // KQV values: the sketch's sign diagonal (bit set: -1)
 };
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);
@@ -72,6 +76,10 @@ hipError_t launch_decode(int head_dim, int group, int kfmt, int vfmt, int units,
 hipError_t launch_decode_v2(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
                             hipEvent_t const ev[2], hipStream_t s);
 const void *decode_kernel_v2(int head_dim, int group, int kfmt);
+// the KQV value instantiations (compiled apart)
+hipError_t launch_decode_v3(int head_dim, int group, int kfmt, int units, const DecodeParams &p,
+                            hipEvent_t const ev[2], hipStream_t s);
+const void *decode_kernel_v3(int head_dim, int group, int kfmt);
 // Streaming-read probe over `bytes` (a multiple of 16) at p; out holds `blocks` words.
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *out, int blocks, hipStream_t s);
 // u32 words of one unit's query record (query-prep output read by the decode kernel).

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the quantized-KV decode workloads.
 
 This module holds no arithmetic of the method: it only draws random keys, values and
-queries with the shapes and distributions of the seven workloads, from torch generators
+queries with the shapes and distributions of the eight workloads, from torch generators
 seeded by a stable hash of (seed, workload, tensor, step).  Both the HIP path and the
 CPU oracle consume what it produces; nothing here quantizes, rotates or attends.
 
@@ -114,6 +114,10 @@ WORKLOADS = {
     7: Workload(7, "b4_gqa32x8_d128_t131072_int2ch0_prune5of8_sink64_recent256_int2tok_clip092_rope2048", 4,
                 32, 8, 128, 131072, 0, k_ch0_bf16=1, n_sink=64, keep_groups=5, v_format=1, v_clip=0.92,
                 n_recent=256, rope_bucket=2048),
+    # the KQV scheme at the 4-bit budget (KV-quantisation statistics, "Quantisierungsschemata"):
+    # WHT + 4-bit Lloyd-Max keys as workload 3, values WHT + 3-bit Lloyd-Max + 1-bit QJL sketch
+    8: Workload(8, "b16_gqa32x8_d128_t32768_wht_lloyd4_kqv3qjl1", 16, 32, 8, 128, 32768, 2, k_hadamard=1,
+                v_format=2),
 }
 
 
@@ -128,6 +132,16 @@ def rope_table(w: Workload, capacity: int):
     if not w.rope_bucket:
         return None
     return rope_anchor_table(w.head_dim, w.rope_bucket, capacity, w.rope_theta)
+
+
+def qjl_signs(head_dim: int, seed: int = 0):
+    """KQV values' random sign diagonal (the sketch's one random draw): uint32 [head_dim / 32],
+    bit i set = channel i negated, seeded like every other input."""
+    import numpy as np
+
+    g = _gen("cpu", seed, 9000, head_dim)
+    bits = torch.randint(0, 2, (head_dim,), generator=g).numpy().astype(np.uint64)
+    return (bits.reshape(-1, 32) << np.arange(32, dtype=np.uint64)).sum(1).astype(np.uint32)
 
 
 def rope_anchor_table(head_dim: int, bucket: int, capacity: int, theta: float = 10000.0):

@@ -14,7 +14,12 @@
  *     (Dual-QK sec. 3.3).
  *   - Values: asymmetric INT4 with an FP16 scale and zero per 32-channel group, or
  *     per-token asymmetric INT2 with a clipping ratio and one FP16 scale and zero per token
- *     (Dual-QK sec. 3.3 and B.2: per-token INT2 values with a 0.92 clipping ratio).
+ *     (Dual-QK sec. 3.3 and B.2: per-token INT2 values with a 0.92 clipping ratio), or
+ *     KQV's value side: Walsh-Hadamard-rotated values as 3-bit Lloyd-Max codes with an FP16
+ *     norm plus a 1-bit QJL sketch of the residual through a randomised Hadamard transform,
+ *     4 bits per channel in all (Statistical Inference and Quality Measures of KV Cache
+ *     Quantisations Inspired by TurboQuant: scheme KQV and the QJL estimator; TurboQuant on
+ *     Quantized Models, abstract: SRHT-QJL).
  *   - The first n_sink positions of every sequence are stored in BF16 (TurboQuant on
  *     Quantized Models, abstract: sink-token preservation; Dual-QK sec. 3.3 / 4.1), and
  *     optionally the n_recent most recent ones too, quantized only when they leave that
@@ -56,8 +61,14 @@
  *            u32 [U][capacity/2][head_dim/8]  per-token INT2 values: word j of pair P holds
  *                                  channels 8j..8j+7, token 2P in bits 0-15, token 2P+1 in
  *                                  bits 16-31, channel 8j+k at bits [2k, 2k+1] of its half.
+ *            KQV values use the INT4 layout; nibble i = 3-bit code | sketch bit << 3.
  *   v_sz     u32 [U][head_dim/32][capacity]  INT4 values: fp16 scale | fp16 zero << 16 per
- *                                  group; per-token INT2 values: [U][1][capacity].
+ *                                  group; per-token INT2 values: [U][1][capacity]; KQV values:
+ *                                  [U][1][capacity], fp16 norm rho | fp16 residual norm << 16.
+ *   v_codebook f32 [8], v_thresholds f32 [7]  KQV values: the 8-level N(0,1) Lloyd-Max
+ *                                  centroids ascending and their thresholds.
+ *   v_qjl_signs u32 [head_dim/32]  KQV values: the sketch's random sign diagonal D (bit i set:
+ *                                  channel i negated), drawn once by the caller.
  *   sink_k   u16 [U][n_sink][head_dim]  bf16 keys of positions < n_sink, in stored
  *                                  coordinates (rotated when k_hadamard = 1).
  *   sink_v   u16 [U][n_sink][head_dim]  bf16 values of positions < n_sink.
@@ -87,6 +98,12 @@
  *   per-token INT2 values: the range is clipped to [c*min, c*max] (c = v_clip, both ends
  *   scaled toward zero), scale = fp16((c*max - c*min) / 3), zero = fp16(c*min), codes as
  *   for the asymmetric groups (entries outside the clipped range saturate at 0 or 3).
+ *   KQV values: y = FWHT(v), rho as for Lloyd-Max keys, code = number of the 7 thresholds
+ *   strictly below y * (1/rho), r = y - rho * cent[code], sketch bit i = 1 when
+ *   (FWHT(D r))_i < 0, residual norm = fp16(sqrt(tree_sum(r*r))).  Decode reads
+ *   v^ = FWHT(rho cent[code] + sqrt(pi/2)/d * ||r|| * D FWHT(sigma)) / d, sigma_i = -1 for
+ *   a set bit (the QJL estimator with S = FWHT * D).  The fp16 weights p*rho and p*||r||
+ *   must stay finite: the values' RMS below about 1000.
  *   bucket-relative RoPE (rotate-half pairing: channel i pairs with i + head_dim/2): with
  *   (c, s) = rope_cs[t / w][i], k'_i = k_i*c + k_{i+d/2}*s and k'_{i+d/2} = k_{i+d/2}*c -
  *   k_i*s (each product rounded, then the sum), before the Walsh-Hadamard rotation.  The
@@ -116,7 +133,7 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
 typedef enum { KVQ_K_ASYM2 = 0, KVQ_K_ASYM4 = 1, KVQ_K_LLOYD4 = 2 } kvq_kfmt;
 
-typedef enum { KVQ_V_ASYM4_G32 = 0, KVQ_V_ASYM2_TOKEN = 1 } kvq_vfmt;
+typedef enum { KVQ_V_ASYM4_G32 = 0, KVQ_V_ASYM2_TOKEN = 1, KVQ_V_KQV = 2 } kvq_vfmt;
 
 /* Cache descriptor.  Geometry and format fields are set once by the caller; `len` is the
  * number of positions stored per sequence (uniform across sequences) and is advanced by
@@ -148,6 +165,9 @@ typedef struct kvq_cache {
     uint16_t *recent_v;
     int32_t rope_bucket;
     const float *rope_cs;
+    const float *v_codebook;
+    const float *v_thresholds;
+    const uint32_t *v_qjl_signs;
 } kvq_cache;
 
 enum {
@@ -163,7 +183,10 @@ enum {
     KVQ_BUF_THRESHOLDS = 9,
     KVQ_BUF_RECENT_K = 10,
     KVQ_BUF_RECENT_V = 11,
-    KVQ_BUF_ROPE_CS = 12
+    KVQ_BUF_ROPE_CS = 12,
+    KVQ_BUF_V_CODEBOOK = 13,
+    KVQ_BUF_V_THRESHOLDS = 14,
+    KVQ_BUF_V_QJL_SIGNS = 15
 };
 
 /* Bytes the caller must allocate for buffer `which` (KVQ_BUF_*) of this geometry; 0 when

@@ -22,7 +22,9 @@ def oracle_geo(oracle_mod, c: B.Cache, units=None):
                             v_format=c.c.v_format, v_clip=float(c.c.v_clip), n_recent=c.c.n_recent,
                             rope_bucket=c.c.rope_bucket)
     table = c.buffers["rope_cs"].view(torch.float32).cpu().numpy() if c.c.rope_bucket else None
-    return oracle_mod.OracleCache(g, units=units, rope_table=table)
+    signs = c.buffers["v_qjl_signs"].view(torch.int32).cpu().numpy().view(np.uint32) \
+        if c.c.v_format == B.V_KQV else None
+    return oracle_mod.OracleCache(g, units=units, rope_table=table, qjl_signs=signs)
 
 
 def gpu_arrays(c: B.Cache, u0=0, u1=None):
@@ -33,7 +35,8 @@ def gpu_arrays(c: B.Cache, u0=0, u1=None):
     R = d * (2 if c.c.k_format == B.K_ASYM2 else 4) // 32
     v2 = c.c.v_format == B.V_ASYM2_TOKEN
     shapes = {"k_codes": (R, cap), "k_sz": (d // 32, cap), "k_norm": (cap,), "k_ch0": (cap,),
-              "v_codes": (cap // 2, d // 8 if v2 else d // 4), "v_sz": (1 if v2 else d // 32, cap),
+              "v_codes": (cap // 2, d // 8 if v2 else d // 4),
+              "v_sz": (d // 32 if c.c.v_format == B.V_ASYM4_G32 else 1, cap),
               "sink_k": (ns, d), "sink_v": (ns, d), "recent_k": (c.c.n_recent, d), "recent_v": (c.c.n_recent, d)}
     dts = {"k_codes": torch.int32, "k_sz": torch.int32, "k_norm": torch.int16, "k_ch0": torch.int16,
            "v_codes": torch.int32, "v_sz": torch.int32, "sink_k": torch.int16, "sink_v": torch.int16,

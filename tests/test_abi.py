@@ -62,6 +62,12 @@ def test_buffer_bytes_follow_layout():
     assert L.kvq_buffer_bytes(ctypes.byref(_cache(rope_bucket=128)), 12) == 4 * (d // 2) * 2 * 4
     assert L.kvq_buffer_bytes(ctypes.byref(_cache(rope_bucket=2048)), 12) == 1 * (d // 2) * 2 * 4
     assert L.kvq_buffer_bytes(ctypes.byref(_cache()), 12) == 0
+    # KQV values: INT4-layout nibbles, one (rho, residual norm) word per token, 8 centroids,
+    # 7 thresholds, d/32 sign words
+    s = _cache(v_format=2)
+    nb = [L.kvq_buffer_bytes(ctypes.byref(s), i) for i in range(16)]
+    assert nb[4:6] == [U * cap // 2 * 32 * 4, U * cap * 4] and nb[13:] == [32, 28, 16]
+    assert [L.kvq_buffer_bytes(ctypes.byref(_cache()), i) for i in (13, 14, 15)] == [0, 0, 0]
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -75,7 +81,7 @@ def test_buffer_bytes_follow_layout():
     (dict(len=513), B.KVQ_ERR_CAPACITY),
     (dict(batch=70000), B.KVQ_ERR_UNSUPPORTED),
     (dict(capacity=(1 << 24) + 256), B.KVQ_ERR_UNSUPPORTED),
-    (dict(v_format=2), B.KVQ_ERR_ARG),
+    (dict(v_format=3), B.KVQ_ERR_ARG),
     (dict(v_format=1, v_clip=0.0), B.KVQ_ERR_ARG),
     (dict(v_format=1, v_clip=1.5), B.KVQ_ERR_ARG),
     (dict(n_recent=-1), B.KVQ_ERR_UNSUPPORTED),

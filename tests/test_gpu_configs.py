@@ -1,4 +1,4 @@
-"""GPU parity on the seven decode workloads at their full sizes, in the launch
+"""GPU parity on the eight decode workloads at their full sizes, in the launch
 configuration the bench times.
 
 The whole cache is built on the GPU; the oracle re-encodes sampled sequences and must match
@@ -21,7 +21,8 @@ def _build(w, extra=0):
     cap = w.capacity(extra)
     c = B.Cache(w.batch, w.n_kv_heads, w.head_dim, cap, n_sink=w.n_sink, k_format=w.k_format,
                 k_hadamard=w.k_hadamard, k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip,
-                n_recent=w.n_recent, rope_bucket=w.rope_bucket, rope_table=synth.rope_table(w, cap))
+                n_recent=w.n_recent, rope_bucket=w.rope_bucket, rope_table=synth.rope_table(w, cap),
+                qjl_signs=synth.qjl_signs(w.head_dim) if w.v_format == 2 else None)
     k, v = synth.prefill(w, device="cuda")
     note(f"workload {w.name}: prefill {tuple(k.shape)} {k.dtype}, capacity {cap}")
     c.append(k, v)
@@ -105,6 +106,15 @@ def test_workload7_rope_buckets_128k(oracle_mod):
     _, mask = _check_decode(c, w, ocs, synth.query(w, 0, device="cuda"), "cfg7")
     m = mask.view(-1, c.rope_buckets)[:, :64].cpu().numpy()
     assert len(np.unique(m)) > 1  # the buckets' masks differ
+
+
+def test_workload8_kqv_values(oracle_mod):
+    """The KQV scheme on workload 3's shape: WHT + Lloyd-Max keys, values as rotated 3-bit
+    Lloyd-Max codes plus a 1-bit QJL sketch of the residual."""
+    w = synth.WORKLOADS[8]
+    c, k, v = _build(w)
+    ocs = _oracle_for(oracle_mod, c, w, k, v, [0, w.batch - 1])
+    _check_decode(c, w, ocs, synth.query(w, 0, device="cuda"), "cfg8")
 
 
 def test_workload5_append_decode_steps(oracle_mod):

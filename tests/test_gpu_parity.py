@@ -36,7 +36,8 @@ def _run(oracle_mod, *, d=128, kfmt=0, rot=0, ch0=0, ns=0, T=300, G=4, Hkv=2, Bs
          f"dtype={dtype} chunks={chunks} dist={dist} vfmt={vfmt} vclip={vclip} nr={nr} rope={rope}")
     c = B.Cache(Bsz, Hkv, d, cap, n_sink=ns, k_format=kfmt, k_hadamard=rot, k_ch0_bf16=ch0,
                 v_format=vfmt, v_clip=vclip, n_recent=nr, rope_bucket=rope,
-                rope_table=synth.rope_anchor_table(d, rope, cap) if rope else None)
+                rope_table=synth.rope_anchor_table(d, rope, cap) if rope else None,
+                qjl_signs=synth.qjl_signs(d, seed) if vfmt == B.V_KQV else None)
     oc = oracle_geo(oracle_mod, c)
     k, v = _inputs(seed, Bsz, Hkv, T, d, dist, dtype, outliers)
     chunks = chunks or [T]
@@ -296,3 +297,25 @@ def test_rope_buckets_teams(oracle_mod):
             _run(oracle_mod, d=128, kfmt=0, G=4, keep=4, T=4000, Hkv=2, Bsz=1, seed=3, rope=512)
         finally:
             B.set_split_tiles(0)
+
+
+# KQV values (Statistical Inference ... Inspired by TurboQuant, scheme KQV): rotated 3-bit codes
+# plus a 1-bit QJL sketch of the residual; the estimator and the inverse rotation run in the
+# decode kernel's flush
+@pytest.mark.parametrize("d,kfmt,rot,ch0,G,keep,ns,T,nr,rope,chunks", [
+    (128, 2, 1, 0, 4, 0, 0, 1000, 0, 0, None),
+    (128, 0, 0, 1, 4, 5, 4, 777, 0, 0, [700, 1, 76]),
+    (128, 0, 0, 0, 8, 0, 64, 300, 100, 0, [150, 150]),
+    (128, 1, 0, 0, 2, 3, 0, 520, 0, 128, None),
+    (128, 0, 0, 1, 1, 0, 2, 257, 0, 0, None),
+    (64, 2, 1, 0, 4, 2, 3, 640, 200, 128, [300, 340]),
+    (64, 0, 0, 1, 8, 0, 0, 333, 0, 0, None),
+])
+def test_kqv_values(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, nr, rope, chunks):
+    _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, keep=keep, ns=ns, T=T, nr=nr, rope=rope, vfmt=B.V_KQV,
+         chunks=chunks, dtype=torch.float32 if d == 64 else torch.bfloat16)
+
+
+def test_kqv_values_teams(oracle_mod):
+    """Long context on one unit (teams of waves, partial states combined after the estimator)."""
+    _run(oracle_mod, d=128, kfmt=0, G=4, ns=4, T=9000, Hkv=1, Bsz=1, dist="t3", vfmt=B.V_KQV)
