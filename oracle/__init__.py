@@ -9,6 +9,8 @@ method's arithmetic.
 The arithmetic lives in ``kvq_oracle.c`` (plain C, fp32 fixed-order encoding, fp64
 decoding and attention); this module builds it with gcc and marshals numpy arrays.
 See ``kvq_oracle.c`` for what each function computes and the passages it follows.
+``quality.py`` builds the quality diagnostics (KL, routing recall, scale and direction
+errors) on top of it.
 
 Parity status: every function is pinned by the CPU tests (``tests/test_oracle_*.py``)
 against library conversions, explicit matrices, brute force, closed forms or the
