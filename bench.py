@@ -170,7 +170,7 @@ def cpu_baseline(w, length, budget_s):
     threads = oracle.num_threads()
     H = w.n_kv_heads
     nseq = max(1, math.ceil(threads / H))
-    geo = oracle.Geometry(batch=nseq, n_kv_heads=H, head_dim=w.head_dim, capacity=w.capacity(512),
+    geo = oracle.Geometry(batch=nseq, n_kv_heads=H, head_dim=w.head_dim, capacity=w.capacity(1280),
                           n_sink=w.n_sink, k_format=w.k_format, k_hadamard=w.k_hadamard,
                           k_ch0_bf16=w.k_ch0_bf16, v_format=w.v_format, v_clip=w.v_clip, n_recent=w.n_recent,
                           rope_bucket=w.rope_bucket)
@@ -182,7 +182,7 @@ def cpu_baseline(w, length, budget_s):
               v.float().numpy().reshape(nseq * H, prefill_len, w.head_dim))
     del k, v
     steps, tokens, t_used = 0, 0, 0.0
-    while t_used < budget_s and steps < 256:
+    while t_used < budget_s and steps < 1024:
         q = synth.query(w, steps, device="cpu", batch=nseq).float().numpy().reshape(nseq * H, w.group, w.head_dim)
         if w.steps:
             kn, vn = synth.append_tokens(w, steps, device="cpu", batch=nseq)
