@@ -319,3 +319,19 @@ def test_kqv_values(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, nr, rope, chu
 def test_kqv_values_teams(oracle_mod):
     """Long context on one unit (teams of waves, partial states combined after the estimator)."""
     _run(oracle_mod, d=128, kfmt=0, G=4, ns=4, T=9000, Hkv=1, Bsz=1, dist="t3", vfmt=B.V_KQV)
+
+
+@pytest.mark.parametrize("rope,vfmt,nr", [(128, 0, 0), (0, B.V_KQV, 0), (256, B.V_KQV, 16), (128, 1, 3)])
+def test_empty_and_short_caches_of_the_newer_formats(oracle_mod, rope, vfmt, nr):
+    """len = 0 writes zeros; sink-only, one-quantised-position and window-only caches match
+    the oracle with RoPE buckets, KQV values and recent windows."""
+    d = 128
+    c = B.Cache(2, 2, d, 256, n_sink=4, v_format=vfmt, v_clip=0.92, n_recent=nr, rope_bucket=rope,
+                rope_table=synth.rope_anchor_table(d, rope, 256) if rope else None,
+                qjl_signs=synth.qjl_signs(d) if vfmt == B.V_KQV else None)
+    q = torch.randn(2, 8, d, device="cuda")
+    out, _ = c.decode(q, 0.088)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    for T in (1, 4, 5, 4 + nr + 1):
+        _run(oracle_mod, ns=4, T=T, rope=rope, vfmt=vfmt, nr=nr, keep=5)
