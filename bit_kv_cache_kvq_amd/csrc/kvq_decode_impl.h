@@ -561,7 +561,7 @@ template <int D, int G, int KF, int VF>
 struct Smem {
     using C = Cfg<D, G, KF, VF>;
     uint32_t lut[KF == KVQ_K_LLOYD4 ? 256 : 1];      // Lloyd-Max code-pair table (fp16x2)
-    uint32_t vlut[VF == KVQ_V_KQV ? 256 : 1];        // KQV values: (cent[lo & 7], cent[hi & 7]) per byte
+    uint32_t vlut[VF == KVQ_V_KQV ? 256 : 1];        // KQV values: byte (2 nibbles) -> (cent[lo & 7], cent[hi & 7])
     float sink_p[G][kMaxSink];
     union {
         uint4 w[C::NWG][C::PAIRS + 1][C::WV];        // fp16 weight pairs: [group][pair][heads]
@@ -1033,7 +1033,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         __syncthreads();
     }
     if constexpr (KQ) {
-        // byte (code nibble of token 2P, code nibble of token 2P+1) -> fp16 centroid pair
+        // byte (code nibbles of two channels of one position) -> fp16 centroid pair
         for (int e = lane; e < 256; e += kWave)
             sm.vlut[e] = pack_f16x2(p.v_codebook[e & 7], p.v_codebook[(e >> 4) & 7]);
         __syncthreads();
@@ -1489,10 +1489,15 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
                     for (int q2 = 0; q2 < 2; q2++) {
                         const uint32_t x = q2 == 0 ? vv.x : vv.y;
-                        uint32_t cp[4];
-#pragma unroll
-                        for (int k = 0; k < 4; k++)
-                            cp[k] = sm.vlut[((x >> (4 * k)) & 0xFu) | ((x >> (12 + 4 * k)) & 0xF0u)];
+                        // a byte holds two channels of one position: its table entry is their
+                        // centroid pair; two permutes regroup the entries by channel across the
+                        // position pair
+                        const uint32_t r0 = sm.vlut[x & 0xFFu], r1 = sm.vlut[(x >> 8) & 0xFFu];
+                        const uint32_t r2 = sm.vlut[(x >> 16) & 0xFFu], r3 = sm.vlut[x >> 24];
+                        const uint32_t cp[4] = {__builtin_amdgcn_perm(r2, r0, 0x05040100u),
+                                                __builtin_amdgcn_perm(r2, r0, 0x07060302u),
+                                                __builtin_amdgcn_perm(r3, r1, 0x05040100u),
+                                                __builtin_amdgcn_perm(r3, r1, 0x07060302u)};
                         const uint32_t sb[4] = {x & 0x00080008u, x & 0x00800080u, x & 0x08000800u,
                                                 (x >> 4) & 0x08000800u};
 #pragma unroll
