@@ -60,8 +60,8 @@ struct Cfg {
     static constexpr int KB = (KF == KVQ_K_ASYM2) ? 2 : 4;
     static constexpr int KROWS = D * KB / 32;      // key code rows (words per position)
     static constexpr int PPW = 16 / KB;            // fp16 pairs per key word (Lloyd-Max)
-    static constexpr int NREG = 8 / KB;            // byte-spread registers per key word (asym)
-    static constexpr int QW = (KF == KVQ_K_LLOYD4) ? 4 : 2 * NREG; // query words per (row, head)
+    // query words per (row, head): fp16 pairs (Lloyd-Max), spread registers (asym, spread_asym)
+    static constexpr int QW = (KF == KVQ_K_LLOYD4) ? 4 : (KB == 2 ? 8 : 4);
     static constexpr int NG = D / 32;              // scale groups
     static constexpr int NP = D / 16;              // prune groups
     static constexpr int RPP = 16 * KB / 32;       // key rows per prune group
@@ -78,16 +78,19 @@ struct Cfg {
     static constexpr int VIT = PAIRS / PPI;        // value iterations per tile
     static constexpr int CPL = D / 64;             // channels per lane in the query prep
     static constexpr int WV = (G + 3) / 4;         // uint4 of fp16 weight pairs per (group, pair)
-    // query record, u32 words per unit: mask; per head the accumulator unit (log2-logit
-    // per accumulator step) and the channel-0 coefficient; zero-term sums [G][NG]; query
-    // operands [KROWS][G][QW]; the softmax state (m, l, o[D]) of the BF16 sink positions
-    // per head [G][D + 2]
+    // query record, u32 words per unit: mask; the sharp-query flag; per head the accumulator
+    // unit (log2-logit per accumulator step) and the channel-0 coefficient; zero-term sums
+    // [G][NG]; query operands [KROWS][G][QW] (fp16 halves), and their residual halves of the
+    // same layout (sharp queries only); the softmax state (m, l, o[D]) of the BF16 sink
+    // positions per head [G][D + 2]
     static constexpr int OFF_MASK = 0;
+    static constexpr int OFF_SHARP = 1;
     static constexpr int OFF_QSC = 4;
     static constexpr int OFF_Q0 = OFF_QSC + G;
     static constexpr int OFF_QZ = OFF_Q0 + G;
     static constexpr int OFF_QP = (OFF_QZ + G * NG + 7) / 8 * 8;
-    static constexpr int OFF_SINK = OFF_QP + KROWS * G * QW;
+    static constexpr int OFF_QPL = OFF_QP + KROWS * G * QW;
+    static constexpr int OFF_SINK = OFF_QPL + KROWS * G * QW;
     static constexpr int QREC = (OFF_SINK + G * (D + 2) + 63) / 64 * 64;
     static_assert(TILE == kTile, "host and device tile must agree");
 };
@@ -167,6 +170,23 @@ constexpr int kNonTemporal = 2;
 constexpr uint32_t kNoAccess = 0x80000000u;
 // log2 slack of the lazily raised softmax maximum (weights stay below 2^kSlack)
 constexpr float kSlack = 2.0f;
+// Largest value-weight exponent (see the decode kernel): the weights 2^(l - m + vexp) stay
+// below 2^(kSlack + kVexpMax) = 2^15 in fp16.
+constexpr int kVexpMax = 13;
+// fp16 bits of the largest value scale s allowed with exponent e (s * 2^e < 2^13), in both
+// halves; e = -3 allows every finite fp16.
+__device__ __forceinline__ uint32_t vexp_thr(int e)
+{
+    const uint32_t b = ((uint32_t)(28 - e) << 10) - 1u;
+    return b | (b << 16);
+}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// per-half unsigned maximum of two fp16 pairs (non-negative halves order as their bits)
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -191,6 +211,48 @@ __device__ __forceinline__ std::conditional_t<ONE, uint32_t, uint2> vload(rsrc_t
         return bload2(r, voff, soff);
 }
 
+// ===================================================================== asymmetric key spread
+// A key word of an asymmetric format holds 32/KB channels of one position; its two 16-bit
+// halves hold channels 0 .. 16/KB - 1 and 16/KB .. 32/KB - 1 of the word.  Spread register
+// k (QW of them) keeps one field of each half in place, or after one right shift for the
+// fields above bit 9, so each half is the subnormal fp16 integer P * code (value
+// P * code * 2^-24, P = the field's place factor, at most 3 * 256 or 15 * 16, below 1024).
+// Register k holds word-local channels (k, k + 16/KB); asym_place is P of channel c.
+template <int KB>
+__host__ __device__ constexpr int asym_qw() { return KB == 2 ? 8 : 4; }
+template <int KB>
+__device__ __forceinline__ int asym_chan(int r, int k, int hi)
+{
+    return r * (32 / KB) + hi * (16 / KB) + k;
+}
+template <int KB>
+__device__ __forceinline__ float asym_place(int c)
+{
+    constexpr int FIELDS = 16 / KB;          // fields per half
+    constexpr int DIRECT = KB == 2 ? 5 : 2;  // fields within bits 0..9 of a half
+    const int j = c % FIELDS;
+    return (float)(1u << (KB * (j < DIRECT ? j : j - DIRECT)));
+}
+template <int KB>
+__device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB>()])
+{
+    if constexpr (KB == 2) {
+        const uint32_t y = x >> 10;
+#pragma unroll
+        for (int k = 0; k < 5; k++)
+            o[k] = x & (0x00030003u << (2 * k));
+#pragma unroll
+        for (int k = 5; k < 8; k++)
+            o[k] = y & (0x00030003u << (2 * (k - 5)));
+    } else {
+        const uint32_t y = x >> 8;
+        o[0] = x & 0x000F000Fu;
+        o[1] = x & 0x00F000F0u;
+        o[2] = y & 0x000F000Fu;
+        o[3] = y & 0x00F000F0u;
+    }
+}
+
 // ===================================================================== query prep
 // One workgroup per unit, one wave per query head of the GQA group: stored-coordinate query
 // (FWHT when keys are rotated), 16-channel group energies (fp32 stride-halving tree, the
@@ -202,9 +264,11 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
     constexpr int CPL = C::CPL, QW = C::QW;
     __shared__ float sq_[G][D];
+    __shared__ float su_[G][D]; // the masked query before the softmax scale (operand source)
     __shared__ float se[G][NP];
     __shared__ float sam[G][NP];
     __shared__ float sp[G][kWave];
+    __shared__ int ssharp[G];
 
     const int lane = threadIdx.x % kWave;
     const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
@@ -255,6 +319,36 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         }
     }
     const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
+
+    // Sharp query (Dual-QK sec. 1 and 3.2: query energy concentrated in a few channels): the
+    // head's largest |q_c| above 8 times its fifth largest, in the coordinates the query is
+    // given in (channel 0 left out when it is scored from its BF16 copy).  A unit with a
+    // sharp head gets a second, residual fp16 half per channel (about 22 bits per channel in
+    // all); one half keeps 11 bits relative to each channel, which the logits of a few very
+    // large channels outgrow.
+    {
+        float v[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            v[s] = (p.ch0 && lane * CPL + s == 0) ? 0.0f : fabsf(yq[s]);
+        float m1 = 0.0f, m5 = 0.0f;
+#pragma unroll
+        for (int it = 0; it < 5; it++) {
+            float lm = v[0];
+#pragma unroll
+            for (int s = 1; s < CPL; s++)
+                lm = fmaxf(lm, v[s]);
+            const float wm = wave_max_dpp(lm);
+            if (it == 0)
+                m1 = wm;
+            m5 = wm;
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                v[s] = v[s] == wm ? -1.0f : v[s]; // (ties leave together: m5 only gets smaller)
+        }
+        if (lane == 0)
+            ssharp[h] = m1 > 8.0f * fmaxf(m5, 0.0f) ? 1 : 0;
+    }
 
     // The query of bucket bq in stored coordinates (rotated back by the bucket's anchor under
     // bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys are rotated),
@@ -326,6 +420,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         for (int s = 0; s < CPL; s++) {
             const int c = lane * CPL + s;
             const bool kept = (mask >> (c / 16)) & 1u;
+            su_[h][c] = kept ? sq_[h][c] : 0.0f;
             qr[s] = kept ? sq_[h][c] * qscale : 0.0f;
             sq_[h][c] = qr[s];
         }
@@ -333,6 +428,10 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         return mask;
     };
     const uint32_t mask = prep(bk);
+    bool sharp = false; // (ssharp is visible after prep's barriers)
+#pragma unroll
+    for (int hh = 0; hh < G; hh++)
+        sharp = sharp || ssharp[hh] != 0;
 
     if (state) {
         // the decode kernel's tile and arrival counters of this unit's stripes, at the places
@@ -347,13 +446,15 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     }
     if (threadIdx.x == 0) {
         rec[C::OFF_MASK] = mask;
+        rec[C::OFF_SHARP] = sharp ? 1u : 0u;
         if (p.mask_out)
             p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
     }
 
     // ---- the query operands of this record
     if constexpr (KF == KVQ_K_LLOYD4) {
-        // fp16 pairs scaled so the largest kept |q| of the group lands in [2^12, 2^13);
+        // fp16 pairs of the query before the softmax scale (which goes into the fp32
+        // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
         // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
         float amax = 0.0f;
 #pragma unroll
@@ -362,73 +463,74 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
             for (int g = 0; g < NP; g++)
                 if (mask >> g & 1u)
                     amax = fmaxf(amax, sam[hh][g]);
-        amax *= qscale;
         int ex = 0;
         (void)frexpf(amax, &ex);
         const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
         if (lane < KROWS * PPW) {
             const int r = lane / PPW, j = lane % PPW;
             const int ca = 8 * r + 2 * j;
-            rec[C::OFF_QP + (r * G + h) * QW + j] = pack_f16x2(sq_[h][ca] * g2, sq_[h][ca + 1] * g2);
+            const float a = su_[h][ca] * g2, b2 = su_[h][ca + 1] * g2;
+            const uint32_t hi = pack_f16x2(a, b2);
+            rec[C::OFF_QP + (r * G + h) * QW + j] = hi;
+            rec[C::OFF_QPL + (r * G + h) * QW + j] = sharp ? pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi)) : 0u;
         }
         if (lane == 0) {
-            recf[C::OFF_QSC + h] = 1.0f / g2;
+            recf[C::OFF_QSC + h] = qscale / g2;
             recf[C::OFF_Q0 + h] = 0.0f;
         }
     } else {
-        // Integer query: q ~= qi * unit, written as 256*hi + lo with signed bytes hi, lo.
-        // INT2 keys: the decode kernel spreads a code word into bytes holding code or
-        // 4*code (masks without shifts for half of them), so the plane entries of the
-        // unscaled codes carry 4*qi; every sum is then 4*(q_int . code), |qi| <= 8159.
-        // 4-bit keys: plain codes, |qi| <= 32639.  Channel 0 is scored from its BF16 copy.
+        // fp16 query halves.  The decode kernel spreads a key word into registers whose two
+        // halves hold the codes of channels (c, c + 32/KB/2) as subnormal integers
+        // P(c) * code * 2^-24 (place factor P, see spread_asym), and multiplies them with
+        // v_dot2_f32_f16 against halves q_c * g2 / P(c).  Every product is then
+        // q~_c * g2 * code_c * 2^-24 with q~ the query rounded to fp16: each channel keeps
+        // 11 bits relative to its own magnitude, so one sharp query channel costs the others
+        // nothing.  The halves hold the query before the softmax scale (which goes into the
+        // fp32 accumulator unit), and g2 (a power of two) puts the head's largest kept |q| in
+        // [2^12, 2^13): a bf16 query is then carried exactly.  Channel 0 (when protected) is
+        // scored from its BF16 copy: its half is 0.
         float am = 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < CPL; s2++) {
             const int c = lane * CPL + s2;
             if (!(p.ch0 && c == 0))
-                am = fmaxf(am, fabsf(qr[s2]));
+                am = fmaxf(am, fabsf(su_[h][c]));
         }
         am = wave_max_dpp(am);
-        constexpr int F = KB == 2 ? 4 : 1;
-        const float unit_q = am > 0.0f ? am / (KB == 2 ? 8159.0f : 32639.0f) : 1.0f;
-        const float inv = 1.0f / unit_q;
-        // key word r, spread register k: byte m holds channel r*(32/KB) + m*(KB==2 ? 4 : 2) + k;
-        // words per (row, head): hi planes of registers 0..NREG-1, then the lo planes
-        if (lane < KROWS * C::NREG) {
-            const int r = lane / C::NREG, k = lane % C::NREG;
-            uint32_t hi = 0, lo = 0;
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                const int c = (KB == 2) ? 16 * r + 4 * m + k : 8 * r + 2 * m + k;
-                const float qv = (p.ch0 && c == 0) ? 0.0f : sq_[h][c];
-                const int qi = (int)__builtin_rintf(qv * inv) * ((KB == 2 && k % 2 == 0) ? 4 : 1);
-                const int h8 = (qi + 128) >> 8;
-                const int l8 = qi - 256 * h8;
-                hi |= (uint32_t)(h8 & 0xFF) << (8 * m);
-                lo |= (uint32_t)(l8 & 0xFF) << (8 * m);
-            }
-            rec[C::OFF_QP + (r * G + h) * QW + k] = hi;
-            rec[C::OFF_QP + (r * G + h) * QW + C::NREG + k] = lo;
+        int ex = 0;
+        (void)frexpf(am, &ex);
+        const float g2 = am > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
+        // the half of channel c (0 for the protected channel 0) and, for a sharp query, the
+        // half of what it leaves (the residual, exact in fp32); g2 and the place factors are
+        // powers of two
+        auto qval = [&](int c) { return (p.ch0 && c == 0) ? 0.0f : su_[h][c] * (g2 / asym_place<KB>(c)); };
+        auto qhi = [&](int c) -> uint32_t { return f32_to_f16(qval(c)); };
+        auto qlo = [&](int c) -> uint32_t { return sharp ? f32_to_f16(qval(c) - f16_to_f32(qhi(c))) : 0u; };
+        // key word r, spread register k: halves hold channels asym_chan<KB>(r, k, 0 / 1)
+        if (lane < KROWS * QW) {
+            const int r = lane / QW, k = lane % QW;
+            const int c0 = asym_chan<KB>(r, k, 0), c1 = asym_chan<KB>(r, k, 1);
+            rec[C::OFF_QP + (r * G + h) * QW + k] = qhi(c0) | (qhi(c1) << 16);
+            rec[C::OFF_QPL + (r * G + h) * QW + k] = qlo(c0) | (qlo(c1) << 16);
         }
-        // zero-term sums: integer query summed over each 32-channel group (lanes of a
-        // group: 32/CPL consecutive lanes; integer-valued floats below 2^24, exact)
+        // zero-term sums: the query as the halves carry it, in accumulator units g2 * 2^-24,
+        // summed over each 32-channel group (lanes of a group: 32/CPL consecutive lanes)
         {
             float si = 0.0f;
 #pragma unroll
             for (int s2 = 0; s2 < CPL; s2++) {
                 const int c = lane * CPL + s2;
-                if (!(p.ch0 && c == 0))
-                    si += __builtin_rintf(qr[s2] * inv);
+                si += (f16_to_f32(qhi(c)) + f16_to_f32(qlo(c))) * (asym_place<KB>(c) * 0x1p-24f);
             }
 #pragma unroll
             for (int m = 16 / CPL; m >= 1; m >>= 1)
                 si += __shfl_xor(si, m);
             if (lane % (32 / CPL) == 0)
-                recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si * F;
+                recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si;
         }
         if (lane == 0) {
-            recf[C::OFF_QSC + h] = unit_q / F;
-            recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? sq_[h][0] * inv * F : 0.0f;
+            recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
+            recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[h][0] * (g2 * 0x1p-24f) : 0.0f;
         }
     }
     if (!state)
@@ -561,6 +663,7 @@ template <int D, int G, int KF, int VF>
 struct Smem {
     using C = Cfg<D, G, KF, VF>;
     uint32_t lut[KF == KVQ_K_LLOYD4 ? 256 : 1];      // Lloyd-Max code-pair table (fp16x2)
+    uint32_t lutl[KF == KVQ_K_LLOYD4 ? 256 : 1];     // its residuals: centroid - fp16(centroid) (fp16x2)
     uint32_t vlut[VF == KVQ_V_KQV ? 256 : 1];        // KQV values: byte (2 nibbles) -> (cent[lo & 7], cent[hi & 7])
     float sink_p[G][kMaxSink];
     union {
@@ -612,77 +715,64 @@ __device__ __forceinline__ void load_ktile(KTile<D, G, KF, VF> &k, const Slabs &
         k.vsz[g] = bload2(sl.vsz, vo, ((uint32_t)g * cap + (uint32_t)t0) * 4u);
 }
 
-// Asymmetric-key logits of this lane's TPL positions in accumulator units:
-//   lg = sum_g s_g * (q_int . code)_g + z_g * sum_{c in g} q_int_c  (+ k0 * q0)
+// Asymmetric-key logits of this lane's TPL positions in accumulator units (g2 * 2^-24 per
+// log2-logit unit, see the query prep):
+//   lg = sum_g s_g * (q~ . code)_g + z_g * sum_{c in g} q~_c  (+ k0 * q0)
 // ALL: every 16-channel row is kept (no pruning), so the row tests fold away.
-// Per (group, head, position) one int32 sum collects the hi-plane products, is shifted
-// by 8, then collects the lo-plane products: sum = 256 * hi.code + lo.code = q_int.code.
-// The query operands are uniform loads from the unit's record.
-template <int D, int G, int KF, int VF, bool ALL, bool CH0>
+// Per (group, head, position) one fp32 sum collects the dot2 products of the group's spread
+// registers with the fp16 query halves (exact products, fp32 sums), then takes the group's
+// scale and zero.  PREC (sharp queries): the residual halves go through the same spread
+// registers too.  The query operands are uniform loads from the unit's record.
+template <int D, int G, int KF, int VF, bool ALL, bool CH0, bool PREC>
 __device__ __forceinline__ void score_asym(const KTile<D, G, KF, VF> &cur, const uint32_t *__restrict__ rec,
                                            uint32_t mask, float (&lg)[Cfg<D, G, KF>::TPL][G])
 {
     using C = Cfg<D, G, KF>;
-    constexpr int KB = C::KB, KROWS = C::KROWS, NG = C::NG, TPL = C::TPL, NREG = C::NREG, QW = C::QW;
+    constexpr int KB = C::KB, KROWS = C::KROWS, NG = C::NG, TPL = C::TPL, QW = C::QW;
     constexpr int RPG = KROWS / NG; // key rows per scale group
     const float *recf = reinterpret_cast<const float *>(rec);
 #pragma unroll
     for (int g = 0; g < NG; g++) {
         if (!ALL && !(mask >> (2 * g) & 3u))
             continue;
-        uint32_t bsp[RPG][TPL][NREG];
+        float a[G][TPL];
 #pragma unroll
         for (int rr = 0; rr < RPG; rr++) {
             const int r = g * RPG + rr;
+            if (!ALL && !(mask >> (r / C::RPP) & 1u)) {
+                if (rr == 0) {
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+#pragma unroll
+                        for (int i = 0; i < TPL; i++)
+                            a[h][i] = 0.0f;
+                }
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < TPL; i++) {
-                const uint32_t x = i == 0 ? cur.kc[r].x : cur.kc[r].y;
-                if constexpr (KB == 2) {
-                    // bytes hold code (registers 0, 2) or 4*code (1, 3); the query planes
-                    // of registers 0 and 2 carry the matching factor 4
-                    const uint32_t y = x >> 4;
-                    bsp[rr][i][0] = x & 0x03030303u;
-                    bsp[rr][i][1] = x & 0x0C0C0C0Cu;
-                    bsp[rr][i][2] = y & 0x03030303u;
-                    bsp[rr][i][3] = y & 0x0C0C0C0Cu;
-                } else {
-                    bsp[rr][i][0] = x & 0x0F0F0F0Fu;
-                    bsp[rr][i][1] = (x >> 4) & 0x0F0F0F0Fu;
+                uint32_t sp[QW];
+                spread_asym<KB>(i == 0 ? cur.kc[r].x : cur.kc[r].y, sp);
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+#pragma unroll
+                    for (int k = 0; k < QW; k++)
+                        a[h][i] = dot2(sp[k], rec[C::OFF_QP + (r * G + h) * QW + k], (rr == 0 && k == 0) ? 0.0f : a[h][i]);
+                    if constexpr (PREC) {
+#pragma unroll
+                        for (int k = 0; k < QW; k++)
+                            a[h][i] = dot2(sp[k], rec[C::OFF_QPL + (r * G + h) * QW + k], a[h][i]);
+                    }
                 }
             }
         }
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            int acc[TPL];
-#pragma unroll
-            for (int i = 0; i < TPL; i++)
-                acc[i] = 0;
-#pragma unroll
-            for (int plane = 0; plane < 2; plane++) {
-                if (plane == 1) {
-#pragma unroll
-                    for (int i = 0; i < TPL; i++)
-                        acc[i] <<= 8;
-                }
-#pragma unroll
-                for (int rr = 0; rr < RPG; rr++) {
-                    const int r = g * RPG + rr;
-                    if (!ALL && !(mask >> (r / C::RPP) & 1u))
-                        continue;
-#pragma unroll
-                    for (int k = 0; k < NREG; k++) {
-                        const int qv = (int)rec[C::OFF_QP + (r * G + h) * QW + plane * NREG + k];
-#pragma unroll
-                        for (int i = 0; i < TPL; i++)
-                            acc[i] = __builtin_amdgcn_sdot4(qv, (int)bsp[rr][i][k], acc[i], false);
-                    }
-                }
-            }
             const float qz = recf[C::OFF_QZ + h * NG + g];
 #pragma unroll
             for (int i = 0; i < TPL; i++) {
                 const uint32_t szw = i == 0 ? cur.ksz[g].x : cur.ksz[g].y;
-                lg[i][h] = fmaf(hi_f16(szw), qz, fmaf(lo_f16(szw), (float)acc[i], lg[i][h]));
+                lg[i][h] = fmaf(hi_f16(szw), qz, fmaf(lo_f16(szw), a[h][i], lg[i][h]));
             }
         }
     }
@@ -1028,8 +1118,12 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 
     if constexpr (KF == KVQ_K_LLOYD4) {
         // code-pair table: byte (lo nibble a, hi nibble b) -> fp16 (cent[a], cent[b])
-        for (int e = lane; e < 256; e += kWave)
-            sm.lut[e] = pack_f16x2(p.codebook[e & 15], p.codebook[e >> 4]);
+        for (int e = lane; e < 256; e += kWave) {
+            const float a = p.codebook[e & 15], b2 = p.codebook[e >> 4];
+            const uint32_t hi = pack_f16x2(a, b2);
+            sm.lut[e] = hi;
+            sm.lutl[e] = pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi));
+        }
         __syncthreads();
     }
     if constexpr (KQ) {
@@ -1071,12 +1165,22 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     float zacc[G][NGV];
     float lsum[G];
     float mrun[G], mthr[G];
+    // Value weights carry a power of two 2^vexp (wave-uniform): the fp16 products p * s
+    // (p < 2^kSlack, s a value scale) must stay finite and normal whatever the values'
+    // magnitude.  vexp starts at kVexpMax and is lowered (the state rescaled, as for a raised
+    // maximum) whenever a scale with s * 2^vexp >= 2^13 arrives, so p * s * 2^vexp < 2^15;
+    // sthr holds the fp16 bits of the largest scale allowed, in both halves.  The weights
+    // are 2^(l - msub) with msub = m - vexp, and the wave's state is (m - vexp, l, o).
+    float msub[G];
+    int vexp = kVexpMax;
+    uint32_t sthr = vexp_thr(kVexpMax);
     auto reset = [&]() {
 #pragma unroll
         for (int h = 0; h < G; h++) {
             lsum[h] = 0.0f;
             mrun[h] = -__builtin_inff();
             mthr[h] = -__builtin_inff();
+            msub[h] = -(float)kVexpMax;
 #pragma unroll
             for (int j = 0; j < 8; j++)
                 acc[h][j] = 0.0f;
@@ -1120,6 +1224,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             red[2 * lane + 1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
             __syncthreads();
             const float ls = wave_sum_dpp(lsum[h]);
+            // the state's maximum in the weights' units (they carry 2^vexp)
+            const float mst = mrun[h] == -__builtin_inff() ? mrun[h] : mrun[h] - (float)vexp;
             float zs[NGV];
 #pragma unroll
             for (int g = 0; g < NGV; g++)
@@ -1175,8 +1281,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     // fold in the sink positions' state, then normalise
                     const float *sk = reinterpret_cast<const float *>(rec) + C::OFF_SINK + h * (D + 2);
                     const float ms = sk[0];
-                    const float M = fmaxf(mrun[h], ms);
-                    const float fw = mrun[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mrun[h] - M);
+                    const float M = fmaxf(mst, ms);
+                    const float fw = mst == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mst - M);
                     const float fs = ms == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
                     const float L = fmaf(ls, fw, sk[1] * fs);
                     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -1190,7 +1296,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     const rsrc_t pr = make_rsrc(p.part, (uint32_t)p.n_waves * G * part_rec<D>() * 4u);
                     const uint32_t rb = ((uint32_t)x * G + h) * part_rec<D>() * 4u;
                     if (lane == 0)
-                        store_shared2(pr, rb, mrun[h], ls);
+                        store_shared2(pr, rb, mst, ls);
                     store_shared4(pr, rb + (4u + 8u * lane) * 4u, o[0], o[1], o[2], o[3]);
                     store_shared4(pr, rb + (8u + 8u * lane) * 4u, o[4], o[5], o[6], o[7]);
                 }
@@ -1250,10 +1356,11 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         ask = draw_tile(ctr);
     // the tile loop, compiled for every-row-kept or not (ALL) and channel 0 apart or not
     // (CH0), so that neither costs a branch per tile
-    auto tiles = [&](auto all_c, auto ch0_c, auto rope_c) {
+    auto tiles = [&](auto all_c, auto ch0_c, auto rope_c, auto prec_c) {
         constexpr bool ALL = decltype(all_c)::value;
         constexpr bool CH0 = decltype(ch0_c)::value;
-        constexpr bool RP = decltype(rope_c)::value; // per-bucket records (bucket-relative RoPE)
+        constexpr bool RP = decltype(rope_c)::value;   // per-bucket records (bucket-relative RoPE)
+        constexpr bool PREC = decltype(prec_c)::value; // sharp query: residual query halves too
         // mask of the tile in `cur` (its bucket's; without RoPE the unit's)
         uint32_t mcur = mask;
         {
@@ -1296,19 +1403,24 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 for (int h = 0; h < G; h++)
                     lg[i][h] = 0.0f;
             if constexpr (KF != KVQ_K_LLOYD4) {
-                score_asym<D, G, KF, VF, ALL, CH0>(cur, rq, mcur, lg);
+                score_asym<D, G, KF, VF, ALL, CH0, PREC>(cur, rq, mcur, lg);
             } else {
 #pragma unroll
                 for (int r = 0; r < KROWS; r++) {
                     if (!ALL && !(mcur >> (r / C::RPP) & 1u))
                         continue;
-                    uint32_t pr[TPL][4];
+                    // (a sharp query also takes the centroids' fp16 residuals: the products
+                    // hi.hi + hi.lo + lo.hi carry about 22 bits on either side)
+                    uint32_t pr[TPL][4], prl[TPL][PREC ? 4 : 1];
 #pragma unroll
                     for (int i = 0; i < TPL; i++) {
                         const uint32_t x = i == 0 ? cur.kc[r].x : cur.kc[r].y;
 #pragma unroll
-                        for (int j = 0; j < 4; j++)
+                        for (int j = 0; j < 4; j++) {
                             pr[i][j] = sm.lut[(x >> (8 * j)) & 0xFFu];
+                            if constexpr (PREC)
+                                prl[i][j] = sm.lutl[(x >> (8 * j)) & 0xFFu];
+                        }
                     }
 #pragma unroll
                     for (int h = 0; h < G; h++)
@@ -1318,6 +1430,12 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
                             for (int i = 0; i < TPL; i++)
                                 lg[i][h] = dot2(pr[i][j], qv, lg[i][h]);
+                            if constexpr (PREC) {
+                                const uint32_t ql = rq[C::OFF_QPL + (r * G + h) * C::QW + j];
+#pragma unroll
+                                for (int i = 0; i < TPL; i++)
+                                    lg[i][h] = dot2(prl[i][j], qv, dot2(pr[i][j], ql, lg[i][h]));
+                            }
                         }
                 }
 #pragma unroll
@@ -1361,17 +1479,33 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 mcur = more ? rec[(size_t)(tn >> tlw) * C::QREC + C::OFF_MASK] : mask;
             load_ktile<D, G, KF, VF, ALL, CH0>(cur, sl, ucap, lane, tn * TILE, mcur, noff);
 
+            // ---- value scales of this lane's positions as fp16 pairs (s0, s1), and the zero
+            // points (z0, z1) (KQV: residual norms); is any scale too large for vexp?
+            uint32_t spair[NGV], zpair[NGV];
+#pragma unroll
+            for (int gg = 0; gg < NGV; gg++) {
+                spair[gg] = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x05040100u);
+                zpair[gg] = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x07060302u);
+            }
+            uint32_t smx = spair[0];
+#pragma unroll
+            for (int gg = 1; gg < NGV; gg++)
+                smx = max_u16x2(smx, spair[gg]);
+            if constexpr (KQ)
+                smx = max_u16x2(smx, zpair[0]);
+            const uint64_t s_above = __ballot(max_u16x2(smx, sthr) != sthr);
+
             // ---- online softmax (log2 units), per head.  The running maximum m is raised
             // (wave-wide DPP max, rescale of that head's state) only when a logit exceeds
-            // m + kSlack; otherwise weights 2^(l - m) may reach 2^kSlack, which keeps every
-            // fp16 weight p*s finite (s < 2^14 for inputs below 65504) and makes the raise
+            // m + kSlack; otherwise weights 2^(l - m) may reach 2^kSlack, and the raise is
             // rare after the first tile.  The test runs in accumulator units against
-            // mthr = (m + kSlack) / acc_to_logit; a rounding miss is harmless.
+            // mthr = (m + kSlack) / acc_to_logit; a rounding miss is harmless.  A value scale
+            // beyond sthr lowers vexp in the same branch (every head's state rescaled).
             // One branch per tile covers all heads: one per head splits the tile's code into
             // blocks the compiler cannot schedule across, which costs far more than the
             // raises themselves (about one per two tiles over all heads).
             uint64_t above[G];
-            uint64_t any_above = 0;
+            uint64_t any_above = s_above;
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 above[h] = 0;
@@ -1381,18 +1515,34 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 any_above |= above[h];
             }
             if (any_above) {
+                int enew = vexp;
+                if (s_above) {
+                    // the wave's largest scale: 2^(e-15) <= s < 2^(e-14) for exponent field e,
+                    // so vexp = 27 - e keeps s * 2^vexp below 2^13
+                    const uint32_t lm = (smx & 0xFFFFu) > (smx >> 16) ? (smx & 0xFFFFu) : (smx >> 16);
+                    const int e = (int)wave_max_dpp((float)lm) >> 10;
+                    enew = min(vexp, 27 - e);
+                }
+                const float fe = ldexpf(1.0f, enew - vexp);
 #pragma unroll
                 for (int h = 0; h < G; h++) {
-                    if (!above[h])
+                    if (!above[h] && enew == vexp)
                         continue;
-                    float mt = lg[0][h];
+                    float mnew = mrun[h];
+                    if (above[h]) {
+                        float mt = lg[0][h];
 #pragma unroll
-                    for (int i = 1; i < TPL; i++)
-                        mt = fmaxf(mt, lg[i][h]);
-                    const float mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
-                    const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);
+                        for (int i = 1; i < TPL; i++)
+                            mt = fmaxf(mt, lg[i][h]);
+                        mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
+                    }
+                    // (a state still empty, m = -inf, is all zeros: any finite factor keeps it)
+                    const float alpha = mrun[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mrun[h] - mnew) * fe;
                     mrun[h] = mnew;
                     mthr[h] = (mnew + kSlack) * logit_to_acc[h];
+                    // (a maximum still at -inf means every logit so far, this tile's included,
+                    // is -inf: subtract -vexp instead so the weights come out 0, not NaN)
+                    msub[h] = (mnew == -__builtin_inff() ? 0.0f : mnew) - (float)enew;
                     lsum[h] *= alpha;
 #pragma unroll
                     for (int j = 0; j < 8; j++)
@@ -1406,17 +1556,15 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                             bacc[h][j] *= alpha;
                     }
                 }
+                vexp = enew;
+                sthr = vexp_thr(enew);
             }
-            // (a running maximum still at -inf means every logit so far, this tile's included,
-            // is -inf: subtract 0 instead so the weights come out 0, not NaN)
             float pw[TPL][G];
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                const float msub = mrun[h] == -__builtin_inff() ? 0.0f : mrun[h];
+            for (int h = 0; h < G; h++)
 #pragma unroll
                 for (int i = 0; i < TPL; i++)
-                    pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -msub));
-            }
+                    pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -msub[h]));
             // zero-point term and the fp16 weights p*s of this lane's position pair (-> LDS),
             // from the weights rounded to fp16 pairs: one packed product and one dot2 per
             // (group, head)
@@ -1429,8 +1577,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             }
 #pragma unroll
             for (int gg = 0; gg < NGV; gg++) {
-                const uint32_t sp = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x05040100u); // (s0, s1)
-                const uint32_t zp = __builtin_amdgcn_perm(vsw[1][gg], vsw[0][gg], 0x07060302u); // (z0, z1)
+                const uint32_t sp = spair[gg], zp = zpair[gg];
                 uint32_t wq[4 * WV];
 #pragma unroll
                 for (int h = 0; h < G; h++) {
@@ -1551,22 +1698,26 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         }
     };
     // (bucket-relative RoPE takes the pruned-rows variant whatever the masks: they differ
-    // by bucket)
+    // by bucket; a sharp query takes the pruned-rows variant with the residual halves)
+    constexpr bool ASYM = KF != KVQ_K_LLOYD4;
+    const bool sharp = rec[C::OFF_SHARP] != 0u;
+    const BoolC<true> T_;
+    const BoolC<false> F_;
     if (p.rope_lw) {
-        if (KF != KVQ_K_LLOYD4 && p.ch0)
-            tiles(BoolC<false>(), BoolC<KF != KVQ_K_LLOYD4>(), BoolC<true>());
+        if (ASYM && p.ch0)
+            sharp ? tiles(F_, BoolC<ASYM>(), T_, T_) : tiles(F_, BoolC<ASYM>(), T_, F_);
         else
-            tiles(BoolC<false>(), BoolC<false>(), BoolC<true>());
-    } else if (mask == (1u << NP) - 1u) {
-        if (KF != KVQ_K_LLOYD4 && p.ch0)
-            tiles(BoolC<true>(), BoolC<KF != KVQ_K_LLOYD4>(), BoolC<false>());
+            sharp ? tiles(F_, F_, T_, T_) : tiles(F_, F_, T_, F_);
+    } else if (mask == (1u << NP) - 1u && !sharp) {
+        if (ASYM && p.ch0)
+            tiles(T_, BoolC<ASYM>(), F_, F_);
         else
-            tiles(BoolC<true>(), BoolC<false>(), BoolC<false>());
+            tiles(T_, F_, F_, F_);
     } else {
-        if (KF != KVQ_K_LLOYD4 && p.ch0)
-            tiles(BoolC<false>(), BoolC<KF != KVQ_K_LLOYD4>(), BoolC<false>());
+        if (ASYM && p.ch0)
+            sharp ? tiles(F_, BoolC<ASYM>(), F_, T_) : tiles(F_, BoolC<ASYM>(), F_, F_);
         else
-            tiles(BoolC<false>(), BoolC<false>(), BoolC<false>());
+            sharp ? tiles(F_, F_, F_, T_) : tiles(F_, F_, F_, F_);
     }
     flush();
 }

@@ -102,8 +102,7 @@
  *   strictly below y * (1/rho), r = y - rho * cent[code], sketch bit i = 1 when
  *   (FWHT(D r))_i < 0, residual norm = fp16(sqrt(tree_sum(r*r))).  Decode reads
  *   v^ = FWHT(rho cent[code] + sqrt(pi/2)/d * ||r|| * D FWHT(sigma)) / d, sigma_i = -1 for
- *   a set bit (the QJL estimator with S = FWHT * D).  The fp16 weights p*rho and p*||r||
- *   must stay finite: the values' RMS below about 1000.
+ *   a set bit (the QJL estimator with S = FWHT * D).
  *   bucket-relative RoPE (rotate-half pairing: channel i pairs with i + head_dim/2): with
  *   (c, s) = rope_cs[t / w][i], k'_i = k_i*c + k_{i+d/2}*s and k'_{i+d/2} = k_{i+d/2}*c -
  *   k_i*s (each product rounded, then the sum), before the Walsh-Hadamard rotation.  The
@@ -196,6 +195,23 @@ size_t kvq_buffer_bytes(const kvq_cache *c, int32_t which);
 /* Host-side check of a descriptor (geometry, format flags, pointers and their 16-byte
  * alignment, 0 <= len <= capacity).  Returns KVQ_OK or the first error found.             */
 kvq_status kvq_validate(const kvq_cache *c);
+
+/* Numerical domain (what the parity tests cover).  Every stored parameter is an fp16, so
+ * inputs must be finite with |x| < 65504, and the parameters that are norms must stay below
+ * 65504 too: Lloyd-Max keys need ||k||_2 < 65504 (rho is the key's L2 norm when rotated),
+ * KQV values need ||v||_2 below about 3e4 (their residual norm is about 2.1 ||v||_2 at
+ * head_dim 128).  Decode scores the query as fp16 halves of the query before the softmax
+ * scale (a power-of-two scale puts the largest kept |q| in [2^12, 2^13)): a bf16 query over
+ * unrotated keys is carried exactly, any other keeps 11 bits relative to each channel.  A
+ * sharp query -- some head's largest |q_c| above 8 times its fifth largest, in the
+ * coordinates the query is given in -- also takes each channel's residual half (about 22
+ * bits), and Lloyd-Max centroids their fp16 residuals.  Value weights p * s (p the softmax
+ * weight, s a value scale or KQV norm) are fp16 products carrying a running power of two per
+ * decode wave, lowered whenever a larger scale arrives, so any finite scale is supported; a
+ * scale more than 2^26 below the largest one a wave has met earlier loses relative precision
+ * (its weights become fp16 subnormals).  Within this domain, outputs stay within 2e-3 of the
+ * row norm of exact attention over the decoded cache for logits of moderate size (the error
+ * of a logit grows with sm * sum_c |q_c k_c|, which also grows the softmax's sensitivity).  */
 
 /* Append n_new tokens to every sequence: quantize and pack k_new / v_new
  * ([batch][n_kv_heads][n_new][head_dim], dtype KVQ_F32 or KVQ_BF16, row-major, device)
