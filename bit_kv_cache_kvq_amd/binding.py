@@ -132,6 +132,16 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _dtype_code(t) -> int:
+    """KVQ_F32 / KVQ_BF16 for a float32 / bfloat16 tensor; any other dtype is refused (the
+    library would read the wrong number of bytes)."""
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    if t.dtype == torch.bfloat16:
+        return KVQ_BF16
+    raise TypeError(f"libkvq takes float32 or bfloat16 tensors, not {t.dtype}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -201,11 +211,20 @@ class Cache:
     def view(self, name, dtype):
         return self.buffers[name].view(dtype)
 
+    def _on_device(self, *ts):
+        want = self.device
+        if want.type == "cuda" and want.index is None:
+            want = torch.device("cuda", torch.cuda.current_device())
+        for t in ts:
+            if t is not None and t.device != want:
+                raise ValueError(f"tensor on {t.device}, the cache lives on {want}")
+
     def append(self, k, v, stream=None):
         """k, v: [batch, n_kv_heads, n_new, head_dim] fp32 or bf16 contiguous device tensors."""
         assert k.shape == v.shape and k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
         assert k.shape[0] == self.c.batch and k.shape[1] == self.c.n_kv_heads and k.shape[3] == self.c.head_dim
-        dt = KVQ_BF16 if k.dtype == torch.bfloat16 else KVQ_F32
+        self._on_device(k, v)
+        dt = _dtype_code(k)
         st = lib().kvq_quant_append(ctypes.byref(self.c), _ptr(k), _ptr(v), dt, int(k.shape[2]), _stream(stream))
         if st != KVQ_OK:
             raise KvqError(st, "kvq_quant_append")
@@ -225,8 +244,11 @@ class Cache:
         if mask_out is None:
             mask_out = torch.zeros(self.c.batch * self.c.n_kv_heads * self.rope_buckets, dtype=torch.uint8,
                                    device=q.device)
+        self._on_device(q, out, mask_out)
+        if out.dtype != torch.float32 or mask_out.dtype != torch.uint8:
+            raise TypeError("out must be float32 and mask_out uint8")
         ws = self.workspace(hq)
-        dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
+        dt = _dtype_code(q)
         st = lib().kvq_decode_attn(ctypes.byref(self.c), _ptr(q), dt, hq, float(sm_scale), int(keep_groups),
                                    _ptr(out), _ptr(mask_out), _ptr(ws), ws.numel(), _stream(stream))
         if st != KVQ_OK:

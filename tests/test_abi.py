@@ -193,3 +193,16 @@ def test_probe_argument_errors():
     assert L.kvq_probe_stream_read(FAKE, 1000, FAKE, 4, None) == B.KVQ_ERR_ARG
     assert L.kvq_probe_stream_read(FAKE, 1024, FAKE, 0, None) == B.KVQ_ERR_ARG
     assert L.kvq_probe_stream_read(FAKE + 8, 1024, FAKE, 4, None) == B.KVQ_ERR_ALIGN
+
+
+def test_binding_refuses_other_dtypes_and_devices():
+    import torch
+
+    c = B.Cache(1, 1, 64, 256, device="cpu")
+    k = torch.zeros(1, 1, 2, 64, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        c.append(k, k)
+    with pytest.raises(TypeError):
+        c.decode(torch.zeros(1, 2, 64, dtype=torch.float64), 0.1)
+    with pytest.raises(ValueError):
+        c.append(torch.zeros(1, 1, 2, 64, device="meta"), torch.zeros(1, 1, 2, 64, device="meta"))
