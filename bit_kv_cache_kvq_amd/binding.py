@@ -24,7 +24,7 @@ BUF_NAMES = ["k_codes", "k_sz", "k_norm", "k_ch0", "v_codes", "v_sz", "sink_k", 
              "codebook", "thresholds", "recent_k", "recent_v", "rope_cs",
              "v_codebook", "v_thresholds", "v_qjl_signs"]  # KVQ_BUF_* order
 EXPORTS = ["kvq_buffer_bytes", "kvq_validate", "kvq_quant_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles", "kvq_set_deterministic",
+           "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_noalloc_scratch_bytes", "kvq_decode_splits", "kvq_codebook_gaussian", "kvq_set_split_tiles", "kvq_set_deterministic",
            "kvq_set_decode_events", "kvq_probe_stream_read",
            "kvq_status_string"]
 
@@ -66,6 +66,10 @@ def lib():
         L.kvq_decode_workspace_bytes.argtypes = [cp, i32]
         L.kvq_decode_attn.restype = i32
         L.kvq_decode_attn.argtypes = [cp, P, i32, i32, ctypes.c_float, i32, P, P, P, sz, P]
+        L.kvq_decode_attn_noalloc.restype = i32
+        L.kvq_decode_attn_noalloc.argtypes = [cp, P, i32, i32, ctypes.c_float, i32, P, P, P]
+        L.kvq_decode_noalloc_scratch_bytes.restype = sz
+        L.kvq_decode_noalloc_scratch_bytes.argtypes = [cp, i32]
         L.kvq_decode_splits.restype = i32
         L.kvq_decode_splits.argtypes = [cp, i32]
         L.kvq_codebook_gaussian.restype = i32
@@ -254,6 +258,28 @@ class Cache:
         if st != KVQ_OK:
             raise KvqError(st, "kvq_decode_attn")
         return out, mask_out
+
+    def decode_noalloc(self, q, sm_scale, keep_groups=0, out=None, mask_out=None, stream=None):
+        """kvq_decode_attn_noalloc: as decode(), with the library's device-resident workspace."""
+        assert q.is_contiguous() and q.shape[0] == self.c.batch and q.shape[2] == self.c.head_dim
+        hq = int(q.shape[1])
+        if out is None:
+            out = torch.empty(q.shape[0], hq, q.shape[2], dtype=torch.float32, device=q.device)
+        if mask_out is None:
+            mask_out = torch.zeros(self.c.batch * self.c.n_kv_heads * self.rope_buckets, dtype=torch.uint8,
+                                   device=q.device)
+        self._on_device(q, out, mask_out)
+        if out.dtype != torch.float32 or mask_out.dtype != torch.uint8:
+            raise TypeError("out must be float32 and mask_out uint8")
+        dt = _dtype_code(q)
+        st = lib().kvq_decode_attn_noalloc(ctypes.byref(self.c), _ptr(q), dt, hq, float(sm_scale), int(keep_groups),
+                                           _ptr(out), _ptr(mask_out), _stream(stream))
+        if st != KVQ_OK:
+            raise KvqError(st, "kvq_decode_attn_noalloc")
+        return out, mask_out
+
+    def noalloc_scratch_bytes(self, n_q_heads) -> int:
+        return int(lib().kvq_decode_noalloc_scratch_bytes(ctypes.byref(self.c), n_q_heads))
 
     def splits(self, n_q_heads) -> int:
         return int(lib().kvq_decode_splits(ctypes.byref(self.c), n_q_heads))

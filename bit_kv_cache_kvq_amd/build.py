@@ -16,7 +16,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_v2.hip", "kvq_decode_v3.hip",
-           "kvq_probe.hip"]
+           "kvq_probe.hip", "kvq_noalloc.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are disabled for all device code

@@ -310,9 +310,10 @@ int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
     return plan_splits(c, quant_end(c, c->len), decode_slots(c->head_dim, G, c->k_format, c->v_format)).n_waves;
 }
 
-kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
-                           float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
-                           void *ws, size_t ws_bytes, void *stream)
+// Everything kvq_decode_attn and kvq_decode_attn_noalloc check before the workspace: the
+// descriptor, the query, the output and the grouping.  *G receives the GQA group size.
+static kvq_status check_decode_args(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
+                                    float sm_scale, int32_t keep_groups, const float *out, int *G)
 {
     kvq_status st = kvq_validate(c);
     if (st != KVQ_OK)
@@ -321,20 +322,55 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
         return KVQ_ERR_ARG;
     if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
         return KVQ_ERR_ARG;
-    const int G = n_q_heads / c->n_kv_heads;
-    if (G != 1 && G != 2 && G != 4 && G != 8)
+    *G = n_q_heads / c->n_kv_heads;
+    if (*G != 1 && *G != 2 && *G != 4 && *G != 8)
         return KVQ_ERR_UNSUPPORTED;
     if (keep_groups < 0 || !isfinite(sm_scale))
         return KVQ_ERR_ARG;
     if (!aligned16(q) || !aligned16(out))
         return KVQ_ERR_ALIGN;
-    const size_t need = kvq_decode_workspace_bytes(c, n_q_heads);
-    if (!ws || ws_bytes < need)
-        return KVQ_ERR_WORKSPACE;
-    if (!aligned16(ws))
-        return KVQ_ERR_ALIGN;
+    return KVQ_OK;
+}
 
-    const Plan pl = plan_splits(c, quant_end(c, c->len), decode_slots(c->head_dim, G, c->k_format, c->v_format));
+// The workspace regions of one decode call: partial states [part_slots][G][D + 4] fp32, the
+// query records, the counters.
+struct WsLayout {
+    size_t part, qrec, ctr; // byte offsets
+    size_t total;           // bytes
+};
+
+// Layout for any len up to the capacity (kvq_decode_workspace_bytes): partial-state slots for
+// the most waves a call of this geometry can use.
+static WsLayout layout_bound(const kvq_cache *c, int G)
+{
+    const size_t U = units_of(c);
+    const size_t places = part_slots(c) > U ? part_slots(c) : U;
+    WsLayout l;
+    l.part = 0;
+    l.qrec = part_region_bytes(c, G);
+    l.ctr = l.qrec + qrec_region_bytes(c, G);
+    l.total = l.ctr + round256((2 * places + U) * sizeof(uint32_t));
+    return l;
+}
+
+// Layout of one call with n_waves decode waves (the allocation-free entry point): partial
+// states for those waves only.
+static WsLayout layout_exact(const kvq_cache *c, int G, int n_waves)
+{
+    const size_t U = units_of(c);
+    WsLayout l;
+    l.part = 0;
+    l.qrec = round256((size_t)n_waves * (size_t)G * (size_t)(c->head_dim + 4) * sizeof(float));
+    l.ctr = l.qrec + qrec_region_bytes(c, G);
+    l.total = l.ctr + round256((2 * (size_t)n_waves + U) * sizeof(uint32_t));
+    return l;
+}
+
+// The launches of one decode call on a workspace laid out as `l` at ws (checked by the caller).
+static kvq_status decode_launch(const kvq_cache *c, const void *q, int32_t q_dtype, int G, float sm_scale,
+                                int32_t keep_groups, float *out, uint8_t *mask_out, void *ws, const WsLayout &l,
+                                const Plan &pl, void *stream)
+{
     const size_t U = units_of(c);
     DecodeParams p;
     p.k_codes = c->k_codes;
@@ -351,10 +387,9 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     p.q = q;
     p.out = out;
     p.mask_out = mask_out;
-    p.part = static_cast<float *>(ws);
-    p.qprep = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + part_region_bytes(c, G));
-    p.tile_ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + part_region_bytes(c, G) +
-                                              qrec_region_bytes(c, G));
+    p.part = reinterpret_cast<float *>(static_cast<char *>(ws) + l.part);
+    p.qprep = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + l.qrec);
+    p.tile_ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + l.ctr);
     p.n_kv_heads = c->n_kv_heads;
     p.cap = c->capacity;
     p.len = c->len;
@@ -383,6 +418,55 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
     if (launch_decode(c->head_dim, G, c->k_format, c->v_format, (int)U, p, ev, (hipStream_t)stream) != hipSuccess)
         return KVQ_ERR_HIP;
     return KVQ_OK;
+}
+
+static Plan plan_of(const kvq_cache *c, int G)
+{
+    return plan_splits(c, quant_end(c, c->len), decode_slots(c->head_dim, G, c->k_format, c->v_format));
+}
+
+kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
+                           float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
+                           void *ws, size_t ws_bytes, void *stream)
+{
+    int G = 0;
+    kvq_status st = check_decode_args(c, q, q_dtype, n_q_heads, sm_scale, keep_groups, out, &G);
+    if (st != KVQ_OK)
+        return st;
+    const WsLayout l = layout_bound(c, G);
+    if (!ws || ws_bytes < l.total)
+        return KVQ_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return KVQ_ERR_ALIGN;
+    return decode_launch(c, q, q_dtype, G, sm_scale, keep_groups, out, mask_out, ws, l, plan_of(c, G), stream);
+}
+
+size_t kvq_decode_noalloc_scratch_bytes(const kvq_cache *c, int32_t n_q_heads)
+{
+    if (check_geometry(c) != KVQ_OK || n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+        return 0;
+    const int G = n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return 0;
+    return layout_exact(c, G, plan_of(c, G).n_waves).total;
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
+                                   float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
+                                   void *stream)
+{
+    int G = 0;
+    kvq_status st = check_decode_args(c, q, q_dtype, n_q_heads, sm_scale, keep_groups, out, &G);
+    if (st != KVQ_OK)
+        return st;
+    const Plan pl = plan_of(c, G);
+    const WsLayout l = layout_exact(c, G, pl.n_waves);
+    if (l.total > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+        return KVQ_ERR_WORKSPACE;
+    void *scratch = nullptr;
+    if (noalloc_scratch(&scratch) != hipSuccess || !scratch)
+        return KVQ_ERR_HIP;
+    return decode_launch(c, q, q_dtype, G, sm_scale, keep_groups, out, mask_out, scratch, l, pl, stream);
 }
 
 void kvq_set_split_tiles(int32_t tiles_per_split) { g_split_tiles.store(tiles_per_split > 0 ? tiles_per_split : 0); }

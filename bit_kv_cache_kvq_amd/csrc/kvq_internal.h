@@ -88,5 +88,8 @@ int decode_qrec_words(int head_dim, int group, int kfmt);
 int decode_slots(int head_dim, int group, int kfmt, int vfmt);
 // Compute units of the current device (256 when the runtime cannot be asked).
 int device_cus();
+// Device address of the current device's allocation-free decode workspace
+// (KVQ_NOALLOC_SCRATCH_BYTES bytes, looked up once per device).
+hipError_t noalloc_scratch(void **ptr);
 
 } // namespace kvq

@@ -254,6 +254,27 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const void *q, int32_t q_dtype, i
                            float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same as
+ * kvq_decode_attn -- same kernels, outputs, masks, status codes and argument checks -- but
+ * the workspace is a device-resident array of KVQ_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per GPU, held until the process ends.  A call needs
+ * kvq_decode_noalloc_scratch_bytes(c, n_q_heads) bytes of it (the partial states of the
+ * waves this call launches, the query records and the counters); beyond the array's size it
+ * returns KVQ_ERR_WORKSPACE before anything is enqueued.  Nothing is allocated: the array's
+ * device address is looked up once per device (on the first call with that device
+ * current), and the query-prep kernel clears the counters on every call.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.                                              */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_cache *c, const void *q, int32_t q_dtype, int32_t n_q_heads,
+                                   float sm_scale, int32_t keep_groups, float *out, uint8_t *mask_out,
+                                   void *stream);
+/* Bytes of the array one kvq_decode_attn_noalloc call of this geometry, len and n_q_heads
+ * needs; 0 for an invalid geometry.  Host-only apart from querying the device's occupancy
+ * once.                                                                                   */
+size_t kvq_decode_noalloc_scratch_bytes(const kvq_cache *c, int32_t n_q_heads);
+
 /* Number of decode waves kvq_decode_attn uses for the current len: one per resident wave
  * slot of the device, at most one per 128-position tile and at least one per (sequence,
  * KV head); wave w serves (sequence, KV head) number w mod (batch * n_kv_heads).  Host-only

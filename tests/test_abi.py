@@ -195,6 +195,19 @@ def test_probe_argument_errors():
     assert L.kvq_probe_stream_read(FAKE + 8, 1024, FAKE, 4, None) == B.KVQ_ERR_ALIGN
 
 
+def test_noalloc_entry_refuses_workspace_beyond_its_array():
+    """kvq_decode_attn_noalloc sizes the call's workspace on the host and refuses it beyond
+    KVQ_NOALLOC_SCRATCH_BYTES before any HIP call."""
+    L = B.lib()
+    s = _cache(batch=512, n_kv_heads=8, capacity=256)
+    need = L.kvq_decode_noalloc_scratch_bytes(ctypes.byref(s), 64)
+    assert need > 32 << 20
+    st = L.kvq_decode_attn_noalloc(ctypes.byref(s), FAKE, B.KVQ_BF16, 64, 0.088, 0, FAKE, None, None)
+    assert st == B.KVQ_ERR_WORKSPACE
+    assert L.kvq_decode_attn_noalloc(ctypes.byref(s), None, B.KVQ_BF16, 64, 0.088, 0, FAKE, None, None) == B.KVQ_ERR_ARG
+    assert L.kvq_decode_noalloc_scratch_bytes(ctypes.byref(_cache(head_dim=96)), 4) == 0
+
+
 def test_binding_refuses_other_dtypes_and_devices():
     import torch
 
