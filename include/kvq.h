@@ -304,11 +304,12 @@ void kvq_set_deterministic(int32_t on);
  * turns it off.  Process-wide; meant for benchmarks, not for concurrent callers.          */
 void kvq_set_decode_events(void *start_event, void *stop_event);
 
-/* Measurement probe: reads `bytes` of device memory at `p` once (16-byte non-temporal loads,
- * grid-stride over `blocks` workgroups of 256 threads) and writes one XOR word per block to
- * `out` (device, `blocks` u32).  Its rate is the practical HBM read ceiling the decode
- * kernel is compared with.  bytes must be a positive multiple of 16, p and out 16-byte
- * aligned, 1 <= blocks <= 65535.                                                         */
+/* Measurement probe: reads `bytes` of device memory at `p` once and writes one XOR word per
+ * workgroup to `out` (device, `blocks` u32): `blocks` one-wave workgroups each read one
+ * contiguous share with 16-byte non-temporal loads (1 KiB per wave and instruction, 8 in
+ * flight), the way decode waves read their units' tiles.  Its rate is the practical HBM
+ * read ceiling the decode kernel is compared with.  bytes must be a positive multiple of
+ * 16, p and out 16-byte aligned, 1 <= blocks <= 65535.                                   */
 kvq_status kvq_probe_stream_read(const void *p, size_t bytes, uint32_t *out, int32_t blocks, void *stream);
 
 const char *kvq_status_string(kvq_status s);

@@ -81,6 +81,7 @@ def lib():
         L.oracle_dequant_unit.argtypes = cache_args + [P, i, i, P, P]
         L.oracle_decode_attn.argtypes = cache_args + [P, i, i, i, P, ctypes.c_double, i, P, P, P]
         L.oracle_num_threads.restype = i
+        L.oracle_set_num_threads.argtypes = [i]
         _lib = L
     return _lib
 
@@ -287,3 +288,7 @@ class OracleCache:
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))

@@ -902,6 +902,17 @@ void oracle_decode_attn(int d, int cap, int n_sink, int kfmt, int rotate, int ch
     }
 }
 
+/* Thread count of the OpenMP loops (the benchmark times the oracle with all host threads
+ * and with one); no arithmetic depends on it. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
