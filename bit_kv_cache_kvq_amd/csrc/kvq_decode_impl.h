@@ -49,6 +49,8 @@
 #include <atomic>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -232,6 +234,14 @@ __device__ __forceinline__ float asym_place(int c)
     constexpr int DIRECT = KB == 2 ? 5 : 2;  // fields within bits 0..9 of a half
     const int j = c % FIELDS;
     return (float)(1u << (KB * (j < DIRECT ? j : j - DIRECT)));
+}
+// a * b (fp16 pairs, fp32 sum) into a fresh register: the VOP3P form with an inline 0 (the
+// compiler would build it from the two-address form and a v_mov of 0)
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b)
+{
+    float r;
+    asm("v_dot2_f32_f16 %0, %2, %1, 0" : "=v"(r) : "v"(a), "s"(b));
+    return r;
 }
 template <int KB>
 __device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB>()])
@@ -757,7 +767,8 @@ __device__ __forceinline__ void score_asym(const KTile<D, G, KF, VF> &cur, const
                 for (int h = 0; h < G; h++) {
 #pragma unroll
                     for (int k = 0; k < QW; k++)
-                        a[h][i] = dot2(sp[k], rec[C::OFF_QP + (r * G + h) * QW + k], (rr == 0 && k == 0) ? 0.0f : a[h][i]);
+                        a[h][i] = (rr == 0 && k == 0) ? dot2_first(sp[k], rec[C::OFF_QP + (r * G + h) * QW + k])
+                                                      : dot2(sp[k], rec[C::OFF_QP + (r * G + h) * QW + k], a[h][i]);
                     if constexpr (PREC) {
 #pragma unroll
                         for (int k = 0; k < QW; k++)
@@ -810,12 +821,12 @@ __device__ __forceinline__ Slabs unit_slabs(const DecodeParams &p, int u)
 
 // Work split (one wave per workgroup, W waves, U units, W >= U).  Wave w takes the place
 // x = team_slot(w): it serves unit x mod U as member x / U of that unit's team; the team has
-// W / U members, one more for the first W mod U units.  Member k scores tile k first; every
-// further tile comes from the unit's counter (tiles team_size, team_size + 1, ... in the
-// order the members ask), so a member that gets more issue slots takes more tiles and the
-// whole team ends together.  Teams of more than kStripe members work the same way on
-// stripes of the unit (see the decode kernel).  In the deterministic mode member k takes
-// tiles k, k + n, ... of a team (stripe) of n instead.
+// W / U members, one more for the first W mod U units.  Member k of n scores the k-th of n
+// contiguous shares of the unit's first three quarters of tiles; the rest come from the
+// unit's counter in the order the members ask, so a member that gets more issue slots takes
+// more of them and the whole team ends together.  Teams of more than kStripe members work
+// the same way on stripes of the unit (see the decode kernel).  In the deterministic mode
+// the shares cover all the tiles.
 __device__ __forceinline__ int team_size(int u, int U, int W) { return W / U + (u < W % U ? 1 : 0); }
 
 // Most waves drawing from one counter: draws on one address are serialized where the atomic
@@ -1147,14 +1158,13 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     const int tlw = p.rope_lw ? p.rope_lw - 7 : 31; // log2 of the tiles per bucket
     static_assert(C::TILE == 1 << 7, "tiles per bucket");
     const uint32_t mask = rec[C::OFF_MASK];
-    float acc_to_logit[G], logit_to_acc[G];
-    int qbk = 0; // bucket whose scales acc_to_logit / logit_to_acc hold
+    float acc_to_logit[G];
+    int qbk = 0; // bucket whose scales acc_to_logit hold
     auto load_scales = [&](int bq) {
         const float *recf = reinterpret_cast<const float *>(rec + (size_t)bq * C::QREC);
 #pragma unroll
         for (int h = 0; h < G; h++) {
             acc_to_logit[h] = recf[C::OFF_QSC + h];
-            logit_to_acc[h] = 1.0f / acc_to_logit[h];
         }
     };
     load_scales(0);
@@ -1164,7 +1174,10 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     float bacc[G][KQ ? 8 : 1]; // KQV: sketch-bit sums per channel
     float zacc[G][NGV];
     float lsum[G];
-    float mrun[G], mthr[G];
+    // Softmax state per head: the raise threshold mthr (accumulator units; -inf while the
+    // state is empty) and msub = m - vexp, the running maximum m in the weights' units, so
+    // m = msub + vexp (no register of its own).
+    float mthr[G];
     // Value weights carry a power of two 2^vexp (wave-uniform): the fp16 products p * s
     // (p < 2^kSlack, s a value scale) must stay finite and normal whatever the values'
     // magnitude.  vexp starts at kVexpMax and is lowered (the state rescaled, as for a raised
@@ -1178,7 +1191,6 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
         for (int h = 0; h < G; h++) {
             lsum[h] = 0.0f;
-            mrun[h] = -__builtin_inff();
             mthr[h] = -__builtin_inff();
             msub[h] = -(float)kVexpMax;
 #pragma unroll
@@ -1225,7 +1237,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             __syncthreads();
             const float ls = wave_sum_dpp(lsum[h]);
             // the state's maximum in the weights' units (they carry 2^vexp)
-            const float mst = mrun[h] == -__builtin_inff() ? mrun[h] : mrun[h] - (float)vexp;
+            const float mst = mthr[h] == -__builtin_inff() ? -__builtin_inff() : msub[h];
             float zs[NGV];
 #pragma unroll
             for (int g = 0; g < NGV; g++)
@@ -1339,20 +1351,38 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         }
     };
 
-    // this wave's tiles: tile `member` first, then those the unit's counter hands out.  The
-    // counter is asked one tile ahead of the answer's use (lane 0's atomic; its return
-    // travels with the tile loads), so the next tile's loads can still go out a whole tile
-    // before its scoring: key-side words and value words of the current tile are in
-    // registers, and value word pair `it` is reloaded with the next tile's right after its
-    // last use.
+    // this wave's tiles.  A stripe's first NS tiles are cut into contiguous shares, member k
+    // of nst taking share k; the rest are drawn from the stripe's counter by whichever member
+    // asks (tile ts0 + NS + draw), which evens out the members' unequal issue rates.  Only
+    // the tail draws: a draw per tile costs read bandwidth (every tile's loads would wait on
+    // an atomic's return).  The counter is asked one tile ahead of the answer's use (lane
+    // 0's atomic; its return travels with the tile loads), so the next tile's loads can
+    // still go out a whole tile before its scoring: key-side words and value words of the
+    // current tile are in registers, and value word pair `it` is reloaded with the next
+    // tile's right after its last use.  In the deterministic mode every tile is static.
     KTile<D, G, KF, VF> cur;
     VWord vcur[VIT];
     reset();
     const Slabs sl = unit_slabs<D, G, KF, VF>(p, u);
     uint32_t *const ctr = p.tile_ctr + (u + m0 * p.n_units);
     const bool dynamic = p.dynamic && nst > 1;
+    const int NT = ts1 - ts0;                                        // the stripe's tiles
+    // its static tiles: all of them in the deterministic mode or when there are no more than
+    // members, else three quarters but at least one per member
+    const int NS = sgpr(dynamic && NT > nst ? max((NT * 3) / 4, nst) : NT);
+    const int r0 = sgpr(ts0 + (int)((long long)smem * NS / nst));    // this member's share
+    const int r1 = sgpr(ts0 + (int)((long long)(smem + 1) * NS / nst));
     uint32_t ask = 0;
-    if (dynamic && lane == 0)
+    int t_first = r0;
+    if (r0 >= r1) {
+        // no static tile (fewer static tiles than members): the first tile is drawn
+        uint32_t a0 = 0;
+        if (dynamic && lane == 0)
+            a0 = draw_tile(ctr);
+        t_first = dynamic ? ts0 + NS + (int)uniform(a0) : ts1;
+    }
+    // the tile after this one's needs a draw: ask now
+    if (dynamic && lane == 0 && t_first < ts1 && (t_first + 1 >= r1))
         ask = draw_tile(ctr);
     // the tile loop, compiled for every-row-kept or not (ALL) and channel 0 apart or not
     // (CH0), so that neither costs a branch per tile
@@ -1364,7 +1394,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
         // mask of the tile in `cur` (its bucket's; without RoPE the unit's)
         uint32_t mcur = mask;
         {
-            const int t = ts0 + smem;
+            const int t = t_first;
             const uint32_t off = t < ts1 ? 0u : kNoAccess;
             if (RP && t < ts1)
                 mcur = rec[(size_t)(t >> tlw) * C::QREC + C::OFF_MASK];
@@ -1373,14 +1403,17 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             for (int it = 0; it < VIT; it++)
                 vcur[it] = vload<V2>(sl.vc, vvo + off, ((uint32_t)(t * TILE / 2 + it * PPI) * WPP) * 4u);
         }
-        for (int t = ts0 + smem; t < ts1;) {
+        for (int t = t_first; t < ts1;) {
             const int t0 = t * TILE;
             const int tl = t0 + lane * TPL;
-            const int tn = dynamic ? ts0 + nst + (int)uniform(ask) : t + nst; // the tile after this one
+            // the tile after this one: the next of the share, else a drawn one (or none)
+            const int tn = t + 1 < r1 ? t + 1 : dynamic ? ts0 + NS + (int)uniform(ask) : ts1;
             const bool more = tn < ts1;
-            if (dynamic && more && lane == 0)
+            if (dynamic && more && lane == 0 && tn + 1 >= r1)
                 ask = draw_tile(ctr);
-            set_priority_for(t - ts0, ts1 - ts0);
+            // progress through the stripe: through the share in the static part (scaled to
+            // it), the tile itself in the drawn part
+            set_priority_for(t < r1 ? (int)((long long)(t - r0) * NS / (r1 - r0)) : t - ts0, NT);
 
             // ---- scores (accumulator units; log2 logit = lg * acc_to_logit[h]).  The query
             // operands are read through an address that depends on the tile number (the
@@ -1394,7 +1427,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 qbk = bt;
 #pragma unroll
                 for (int h = 0; h < G; h++)
-                    mthr[h] = (mrun[h] + kSlack) * logit_to_acc[h];
+                    if (mthr[h] != -__builtin_inff())
+                        mthr[h] = (msub[h] + (float)vexp + kSlack) / acc_to_logit[h];
             }
             float lg[TPL][G];
 #pragma unroll
@@ -1528,18 +1562,18 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                 for (int h = 0; h < G; h++) {
                     if (!above[h] && enew == vexp)
                         continue;
-                    float mnew = mrun[h];
+                    const float mold = mthr[h] == -__builtin_inff() ? -__builtin_inff() : msub[h] + (float)vexp;
+                    float mnew = mold;
                     if (above[h]) {
                         float mt = lg[0][h];
 #pragma unroll
                         for (int i = 1; i < TPL; i++)
                             mt = fmaxf(mt, lg[i][h]);
-                        mnew = fmaxf(mrun[h], wave_max_dpp(mt * acc_to_logit[h]));
+                        mnew = fmaxf(mold, wave_max_dpp(mt * acc_to_logit[h]));
                     }
                     // (a state still empty, m = -inf, is all zeros: any finite factor keeps it)
-                    const float alpha = mrun[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mrun[h] - mnew) * fe;
-                    mrun[h] = mnew;
-                    mthr[h] = (mnew + kSlack) * logit_to_acc[h];
+                    const float alpha = mold == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mold - mnew) * fe;
+                    mthr[h] = mnew == -__builtin_inff() ? mnew : (mnew + kSlack) / acc_to_logit[h];
                     // (a maximum still at -inf means every logit so far, this tile's included,
                     // is -inf: subtract -vexp instead so the weights come out 0, not NaN)
                     msub[h] = (mnew == -__builtin_inff() ? 0.0f : mnew) - (float)enew;
@@ -1733,14 +1767,16 @@ hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (ev[0] && (e = hipEventRecord(ev[0], s)) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((decode_kernel<D, G, KF, VF>), dim3((unsigned)p.n_waves), dim3(kWave), 0, s, p,
-                       static_cast<const uint32_t *>(p.qprep));
-    e = hipGetLastError();
-    if (e == hipSuccess && ev[1])
-        e = hipEventRecord(ev[1], s);
-    return e;
+    const uint32_t *qrec = static_cast<const uint32_t *>(p.qprep);
+    if (ev[0] && ev[1]) {
+        // measurement: the events are taken by the dispatch itself, at the start and the end
+        // of the kernel's execution
+        void *args[] = {const_cast<DecodeParams *>(&p), &qrec};
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<D, G, KF, VF>),
+                                  dim3((unsigned)p.n_waves), dim3(kWave), args, 0, s, ev[0], ev[1], 0);
+    }
+    hipLaunchKernelGGL((decode_kernel<D, G, KF, VF>), dim3((unsigned)p.n_waves), dim3(kWave), 0, s, p, qrec);
+    return hipGetLastError();
 }
 
 template <int D, int G, int VF>

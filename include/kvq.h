@@ -291,17 +291,20 @@ kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *threshol
  * decode calls only.                                                                     */
 void kvq_set_split_tiles(int32_t tiles_per_split);
 
-/* 1: every decode wave takes a fixed set of tiles (member k of a team of n waves takes tiles
- * k, k + n, k + 2n, ...), so kvq_decode_attn gives bit-identical outputs for identical
- * inputs; 0 (default): tiles go to whichever wave of the team asks first, which balances
- * waves that get unequal shares of their SIMD.  Process-wide; affects later calls only.    */
+/* 1: every decode wave takes a fixed set of tiles (member k of a team of n waves takes the
+ * k-th of n contiguous shares of its stripe's tiles), so kvq_decode_attn gives bit-identical
+ * outputs for identical inputs; 0 (default): the first three quarters of a stripe's tiles
+ * are shared that way and the rest go to whichever wave of the team asks first, which
+ * balances waves that get unequal shares of their SIMD.  Process-wide; affects later calls
+ * only.                                                                                  */
 void kvq_set_deterministic(int32_t on);
 
 /* Measurement hook: while both handles are non-NULL (hipEvent_t, created and owned by the
- * caller), every kvq_decode_attn records start_event on its stream immediately before the
- * main decode kernel and stop_event immediately after it, so hipEventElapsedTime gives that
- * kernel's duration alone (the query-prep kernel falls outside).  NULL, NULL
- * turns it off.  Process-wide; meant for benchmarks, not for concurrent callers.          */
+ * caller), every kvq_decode_attn launches its main decode kernel with start_event and
+ * stop_event attached to the dispatch (hipExtLaunchKernel): they record the start and the
+ * end of that kernel's execution, so hipEventElapsedTime gives its duration alone (the
+ * query-prep kernel falls outside).  NULL, NULL turns it off.  Process-wide; meant for
+ * benchmarks, not for concurrent callers.                                                 */
 void kvq_set_decode_events(void *start_event, void *stop_event);
 
 /* Measurement probe: reads `bytes` of device memory at `p` once and writes one XOR word per
