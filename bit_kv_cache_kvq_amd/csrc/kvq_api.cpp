@@ -282,6 +282,15 @@ static size_t part_region_bytes(const kvq_cache *c, int G)
     return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 4) * sizeof(float));
 }
 
+// BF16 chunk states (query prep -> decode): [unit][1 + ceil(n_recent / 64)][G][D + 4] fp32
+static int bf16_chunk_records(const kvq_cache *c) { return 1 + (c->n_recent + 63) / 64; }
+
+static size_t bstate_region_bytes(const kvq_cache *c, int G)
+{
+    return round256(units_of(c) * (size_t)bf16_chunk_records(c) * (size_t)G * (size_t)(c->head_dim + 4) *
+                    sizeof(float));
+}
+
 static size_t qrec_region_bytes(const kvq_cache *c, int G)
 {
     return round256(units_of(c) * (size_t)rope_buckets(c) *
@@ -297,7 +306,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads)
     // counters: two per wave place (a stripe's tiles drawn and members done, at the place of
     // its first member), then one per unit (members or stripes done)
     const size_t places = part_slots(c) > U ? part_slots(c) : U;
-    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + round256((2 * places + U) * sizeof(uint32_t));
+    return part_region_bytes(c, (int)G) + qrec_region_bytes(c, (int)G) + bstate_region_bytes(c, (int)G) +
+           round256((2 * places + U) * sizeof(uint32_t));
 }
 
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads)
@@ -335,7 +345,7 @@ static kvq_status check_decode_args(const kvq_cache *c, const void *q, int32_t q
 // The workspace regions of one decode call: partial states [part_slots][G][D + 4] fp32, the
 // query records, the counters.
 struct WsLayout {
-    size_t part, qrec, ctr; // byte offsets
+    size_t part, qrec, bstate, ctr; // byte offsets
     size_t total;           // bytes
 };
 
@@ -348,7 +358,8 @@ static WsLayout layout_bound(const kvq_cache *c, int G)
     WsLayout l;
     l.part = 0;
     l.qrec = part_region_bytes(c, G);
-    l.ctr = l.qrec + qrec_region_bytes(c, G);
+    l.bstate = l.qrec + qrec_region_bytes(c, G);
+    l.ctr = l.bstate + bstate_region_bytes(c, G);
     l.total = l.ctr + round256((2 * places + U) * sizeof(uint32_t));
     return l;
 }
@@ -361,7 +372,8 @@ static WsLayout layout_exact(const kvq_cache *c, int G, int n_waves)
     WsLayout l;
     l.part = 0;
     l.qrec = round256((size_t)n_waves * (size_t)G * (size_t)(c->head_dim + 4) * sizeof(float));
-    l.ctr = l.qrec + qrec_region_bytes(c, G);
+    l.bstate = l.qrec + qrec_region_bytes(c, G);
+    l.ctr = l.bstate + bstate_region_bytes(c, G);
     l.total = l.ctr + round256((2 * (size_t)n_waves + U) * sizeof(uint32_t));
     return l;
 }
@@ -412,6 +424,14 @@ static kvq_status decode_launch(const kvq_cache *c, const void *q, int32_t q_dty
     p.v_qjl = c->v_qjl_signs;
     p.n_rb = rope_buckets(c);
     p.n_qb = c->rope_bucket > 0 && c->len > 0 ? (c->len + c->rope_bucket - 1) / c->rope_bucket : 1;
+    // BF16 positions: the sinks (chunk 0), then the recent window [wlo, len) 64 per chunk
+    p.bstate = reinterpret_cast<float *>(static_cast<char *>(ws) + l.bstate);
+    p.bch_max = bf16_chunk_records(c);
+    {
+        const int ns = c->n_sink < c->len ? c->n_sink : c->len;
+        const int wlo = p.q_end > ns ? p.q_end : ns;
+        p.n_bch = 1 + (c->len > wlo ? (c->len - wlo + 63) / 64 : 0);
+    }
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
     if (!ev[0] || !ev[1])
         ev[0] = ev[1] = nullptr;

@@ -83,8 +83,7 @@ struct Cfg {
     // query record, u32 words per unit: mask; the sharp-query flag; per head the accumulator
     // unit (log2-logit per accumulator step) and the channel-0 coefficient; zero-term sums
     // [G][NG]; query operands [KROWS][G][QW] (fp16 halves), and their residual halves of the
-    // same layout (sharp queries only); the softmax state (m, l, o[D]) of the BF16 sink
-    // positions per head [G][D + 2]
+    // same layout (sharp queries only)
     static constexpr int OFF_MASK = 0;
     static constexpr int OFF_SHARP = 1;
     static constexpr int OFF_QSC = 4;
@@ -92,10 +91,14 @@ struct Cfg {
     static constexpr int OFF_QZ = OFF_Q0 + G;
     static constexpr int OFF_QP = (OFF_QZ + G * NG + 7) / 8 * 8;
     static constexpr int OFF_QPL = OFF_QP + KROWS * G * QW;
-    static constexpr int OFF_SINK = OFF_QPL + KROWS * G * QW;
-    static constexpr int QREC = (OFF_SINK + G * (D + 2) + 63) / 64 * 64;
+    static constexpr int QREC = (OFF_QPL + KROWS * G * QW + 63) / 64 * 64;
     static_assert(TILE == kTile, "host and device tile must agree");
 };
+
+// Partial softmax state record of one (wave or BF16 chunk, head): m, l, two unused words,
+// o[D] (16-byte aligned).
+template <int D>
+constexpr int part_rec() { return D + 4; }
 
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ float dpp_max_step(float x)
@@ -264,9 +267,13 @@ __device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB
 }
 
 // ===================================================================== query prep
-// One workgroup per unit, one wave per query head of the GQA group: stored-coordinate query
-// (FWHT when keys are rotated), 16-channel group energies (fp32 stride-halving tree, the
-// order the format fixes), the group's mask, and the head's query operands and sink state.
+// One wave per query head of the GQA group in every workgroup.  Record workgroups, one per
+// (bucket, unit): stored-coordinate query (FWHT when keys are rotated), 16-channel group
+// energies (fp32 stride-halving tree, the order the format fixes), the group's mask, and the
+// head's query operands.  Chunk workgroups, one per (unit, chunk of up to 64 BF16
+// positions): chunk 0 the sinks, chunk c >= 1 the recent window's positions from
+// 64 (c - 1) on; each writes the softmax state (m, l, o) of its positions per head, which
+// the decode kernel folds into the unit's result.
 template <int D, int G, int KF, int SB>
 __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
 {
@@ -282,26 +289,29 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
 
     const int lane = threadIdx.x % kWave;
     const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
-    // workgroups of bucket 0 first: they also compute the BF16 positions' softmax state, the
-    // longest work of the kernel, so they start before the other buckets' records
-    const int bk = (int)blockIdx.x / p.n_units; // bucket of this record (0 without RoPE)
-    const int unit = (int)blockIdx.x % p.n_units;
+    // the chunk workgroups first (the longest work of the kernel), then the records
+    const int nchw = p.n_units * p.n_bch;
+    const bool state = (int)blockIdx.x < nchw; // a chunk workgroup: BF16 positions' state
+    const int bid = state ? (int)blockIdx.x : (int)blockIdx.x - nchw;
+    const int bk = state ? 0 : bid / p.n_units; // bucket of this record (0 without RoPE)
+    const int unit = bid % p.n_units;
+    const int ch = state ? bid / p.n_units : 0; // BF16 chunk: 0 the sinks, c >= 1 the window's
     const int b = unit / p.n_kv_heads;
     const int kvh = unit % p.n_kv_heads;
     const int n_q_heads = p.n_kv_heads * G;
-    const bool state = bk == 0; // this workgroup also computes the BF16 positions' state
     uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
     float *recf = reinterpret_cast<float *>(rec);
 
     // BF16 sink rows, SB at a time (the last row repeated past n_sink); the first batch of
     // keys and values is loaded here, with the query, so its latency overlaps the query's.
     // SB is 8, or 32 for more than 8 sinks (64 sinks then cost two rounds of latency).
-    const int n_sink = p.n_sink < p.len ? p.n_sink : p.len;
+    // (a chunk of the window sees no sinks)
+    const int n_sink = (state && ch > 0) ? 0 : (p.n_sink < p.len ? p.n_sink : p.len);
     auto load_sinks = [&](const uint16_t *base, int t0, float (&dst)[SB][CPL]) {
 #pragma unroll
         for (int j = 0; j < SB; j++) {
             const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
-            const uint16_t *row = base + ((size_t)unit * p.n_sink + t) * D + lane * CPL;
+            const uint16_t *row = base + ((size_t)unit * p.n_sink + (t > 0 ? t : 0)) * D + lane * CPL;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
                 dst[j][s] = bf16_to_f32(row[s]);
@@ -443,7 +453,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     for (int hh = 0; hh < G; hh++)
         sharp = sharp || ssharp[hh] != 0;
 
-    if (state) {
+    if (!state && bk == 0) {
         // the decode kernel's tile and arrival counters of this unit's stripes, at the places
         // u + k * units
         for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         if (threadIdx.x == 0)
             p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
     }
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && !state) {
         rec[C::OFF_MASK] = mask;
         rec[C::OFF_SHARP] = sharp ? 1u : 0u;
         if (p.mask_out)
@@ -462,7 +472,9 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     }
 
     // ---- the query operands of this record
-    if constexpr (KF == KVQ_K_LLOYD4) {
+    if (state) {
+        // (a chunk workgroup writes no record)
+    } else if constexpr (KF == KVQ_K_LLOYD4) {
         // fp16 pairs of the query before the softmax scale (which goes into the fp32
         // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
         // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
@@ -546,11 +558,11 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     if (!state)
         return;
 
-    // BF16 sink positions (t < min(n_sink, len), all in bucket 0): dense dot over the kept
-    // channels, then the head's softmax state over them -- log2 max m, sum l and
+    // Chunk 0: the BF16 sink positions (t < min(n_sink, len), all in bucket 0): dense dot over
+    // the kept channels, then the head's softmax state over them -- log2 max m, sum l and
     // o = sum_t 2^(l_t - m) v_t -- which the decode kernel folds into the unit's result.
     // Lanes own channels; one wave-wide sum per sink gives its logit, lane t keeps that of
-    // sink t.
+    // sink t.  (A window chunk has n_sink = 0 here: an empty state.)
     {
         float mine = -__builtin_inff();
         for (int t0 = 0; t0 < n_sink; t0 += SB) {
@@ -589,16 +601,19 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
                     o[s] = fmaf(sp[h][t0 + j], vv[j][s], o[s]);
             }
         }
-        // recent BF16 window, positions [wlo, len) in ring slots t mod W (Dual-QK sec. 3.3 /
-        // 4.1), one bucket's positions at a time (the query of that bucket), 64 positions per
-        // chunk, lane j scoring position c0 + j over all channels from its ring row, folded
-        // into the state (m, l, o) online
+        // chunk c >= 1: recent BF16 window positions [wlo, len) from 64 (c - 1) on, 64 at most,
+        // in ring slots t mod W (Dual-QK sec. 3.3 / 4.1), one bucket's positions at a time
+        // (the query of that bucket), lane j scoring position c0 + j over all channels from
+        // its ring row, folded into the state (m, l, o) online
         float M = m, L = l;
-        const int wlo = p.q_end > n_sink ? p.q_end : n_sink;
+        const int ns_all = p.n_sink < p.len ? p.n_sink : p.len;
+        const int wlo = p.q_end > ns_all ? p.q_end : ns_all;
+        const int wa = ch > 0 ? wlo + kWave * (ch - 1) : p.len;
+        const int wb = min(p.len, wa + kWave);
         int qb = 0; // bucket whose query qr / sq_ hold
-        for (int s0 = wlo; s0 < p.len;) {
+        for (int s0 = wa; s0 < wb;) {
             const int bs = p.rope_lw ? s0 >> p.rope_lw : 0;
-            const int s1 = p.rope_lw ? min(p.len, (bs + 1) << p.rope_lw) : p.len;
+            const int s1 = p.rope_lw ? min(wb, (bs + 1) << p.rope_lw) : wb;
             if (bs != qb) {
                 (void)prep(bs);
                 qb = bs;
@@ -658,13 +673,15 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
             }
             s0 = s1;
         }
+        // the chunk's state, in the partial-state layout (m, l, two unused words, o[D])
+        float *st = p.bstate + ((size_t)(unit * p.bch_max + ch) * G + h) * part_rec<D>();
         if (lane == 0) {
-            recf[C::OFF_SINK + h * (D + 2)] = M;
-            recf[C::OFF_SINK + h * (D + 2) + 1] = L;
+            st[0] = M;
+            st[1] = L;
         }
 #pragma unroll
         for (int s = 0; s < CPL; s++)
-            recf[C::OFF_SINK + h * (D + 2) + 2 + lane * CPL + s] = o[s];
+            st[4 + lane * CPL + s] = o[s];
     }
 }
 
@@ -907,12 +924,9 @@ __device__ __forceinline__ float load_shared(rsrc_t r, uint32_t byte_off)
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherent));
 }
-// Partial state record of one (wave, head): m, l, two unused words, o[D] (16-byte aligned).
-template <int D>
-constexpr int part_rec() { return D + 4; }
 
 // Combine the partial softmax states (m, l, o) of a unit's team, member k in slot u + k * U,
-// with the sink positions' state: one global softmax over all positions (Dual-QK sec. 3.4),
+// with the states of its BF16 chunks: one global softmax over all positions (Dual-QK sec. 3.4),
 // normalised into out_u[h][D].  Run by one wave; lane j holds channels j, j + 64 of every
 // head.  Members go in batches of NB, all heads at once (48 o loads per lane per batch),
 // and the next batch's loads are issued before the current batch is folded in, so a team
@@ -949,17 +963,16 @@ __device__ __forceinline__ void load_batch(CombineBatch<D, G> &b, rsrc_t r, uint
                                              : 0.0f;
 }
 
-// Fold `count` partial states (slots first, first + step, ... in units of records) into the
-// state (M, L, O), which holds the sink state or an empty one on entry.
+// Fold `count` partial states (slots first, first + step, ... in units of records, of an
+// array of `slots` records at `base`) into the state (M, L, O).
 template <int D, int G>
-__device__ __forceinline__ void fold_states(const DecodeParams &p, int first, int step, int count, int lane,
+__device__ __forceinline__ void fold_states(const float *base, int slots, int first, int step, int count, int lane,
                                             float (&M)[G], float (&L)[G], float (&O)[G][D / 64])
 {
     using CB = CombineBatch<D, G>;
     constexpr int CPL = CB::CPL, NB = CB::NB, PR = part_rec<D>();
     const uint32_t stride = (uint32_t)step * G * PR * 4u; // bytes between the states
-    // all slots are below the number of waves
-    const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
+    const rsrc_t r = make_rsrc(base, (uint32_t)slots * G * PR * 4u);
     const uint32_t ub = (uint32_t)first * G * PR * 4u;    // first state, head 0
     CB cur, nxt;
     load_batch<D, G>(cur, r, ub, stride, 0, count, lane);
@@ -988,24 +1001,24 @@ __device__ __forceinline__ void fold_states(const DecodeParams &p, int first, in
     }
 }
 
-// The unit's team, last step: fold `count` states (stripe or member states) into the sink
-// positions' state and write the normalised output out_u[h][D].
+// The unit's team, last step: fold unit u's BF16 chunk states and `count` states (stripe or
+// member states) and write the normalised output out_u[h][D].
 template <int D, int G>
-__device__ __forceinline__ void combine_unit(const DecodeParams &p, const float *sink, int first, int step, int count,
-                                             int lane, float *out_u)
+__device__ __forceinline__ void combine_unit(const DecodeParams &p, int u, int first, int step, int count, int lane,
+                                             float *out_u)
 {
     constexpr int CPL = D / 64;
     float M[G], L[G], O[G][CPL];
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const float *sk = sink + h * (D + 2);
-        M[h] = sk[0];
-        L[h] = sk[1];
+        M[h] = -__builtin_inff();
+        L[h] = 0.0f;
 #pragma unroll
         for (int s = 0; s < CPL; s++)
-            O[h][s] = sk[2 + lane + 64 * s];
+            O[h][s] = 0.0f;
     }
-    fold_states<D, G>(p, first, step, count, lane, M, L, O);
+    fold_states<D, G>(p.bstate, p.n_units * p.bch_max, u * p.bch_max, 1, p.n_bch, lane, M, L, O);
+    fold_states<D, G>(p.part, p.n_waves, first, step, count, lane, M, L, O);
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
@@ -1028,7 +1041,7 @@ __device__ __forceinline__ void combine_stripe(const DecodeParams &p, int first,
         for (int s = 0; s < CPL; s++)
             O[h][s] = 0.0f;
     }
-    fold_states<D, G>(p, first, step, count, lane, M, L, O);
+    fold_states<D, G>(p.part, p.n_waves, first, step, count, lane, M, L, O);
     const rsrc_t r = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -1289,63 +1302,61 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     o[j] = o[j] * sc + zs[V2 ? 0 : (8 * lane + j) / 32];
                 }
                 }
-                if (whole) {
-                    // fold in the sink positions' state, then normalise
-                    const float *sk = reinterpret_cast<const float *>(rec) + C::OFF_SINK + h * (D + 2);
-                    const float ms = sk[0];
-                    const float M = fmaxf(mst, ms);
-                    const float fw = mst == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mst - M);
-                    const float fs = ms == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-                    const float L = fmaf(ls, fw, sk[1] * fs);
-                    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 8; j++)
-                        o[j] = fmaf(o[j], fw, sk[2 + 8 * lane + j] * fs) * inv;
-                    float4 *dst = reinterpret_cast<float4 *>(p.out + ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + 8 * lane);
-                    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-                    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-                } else {
-                    const rsrc_t pr = make_rsrc(p.part, (uint32_t)p.n_waves * G * part_rec<D>() * 4u);
-                    const uint32_t rb = ((uint32_t)x * G + h) * part_rec<D>() * 4u;
-                    if (lane == 0)
-                        store_shared2(pr, rb, mst, ls);
-                    store_shared4(pr, rb + (4u + 8u * lane) * 4u, o[0], o[1], o[2], o[3]);
-                    store_shared4(pr, rb + (8u + 8u * lane) * 4u, o[4], o[5], o[6], o[7]);
-                }
+                const rsrc_t pr = make_rsrc(p.part, (uint32_t)p.n_waves * G * part_rec<D>() * 4u);
+                const uint32_t rb = ((uint32_t)x * G + h) * part_rec<D>() * 4u;
+                if (lane == 0)
+                    store_shared2(pr, rb, mst, ls);
+                store_shared4(pr, rb + (4u + 8u * lane) * 4u, o[0], o[1], o[2], o[3]);
+                store_shared4(pr, rb + (8u + 8u * lane) * 4u, o[4], o[5], o[6], o[7]);
             }
             __syncthreads();
         }
-        if (!whole) {
-            // count this member in once its states are stored (all of the wave's memory
-            // operations complete); the member that arrives last combines the states (in
-            // member order, so the result does not depend on which member that is) with the
-            // sink positions' state.  A striped team does it in two steps: the last member of
-            // each stripe folds the stripe's states into its first member's slot and then
-            // counts the stripe in; the last stripe folds the stripes' states.
-            const float *sink = reinterpret_cast<const float *>(rec) + C::OFF_SINK;
-            float *out_u = p.out + ((size_t)b * n_q_heads + (size_t)kvh * G) * D;
-            __builtin_amdgcn_s_waitcnt(0);
+        // Every wave stores its partial state (m, l, o) in the slot of its place; the unit's
+        // result folds those of its team with the states of its BF16 chunks.  A unit served
+        // by one wave combines at once.  Otherwise each member counts itself in once its
+        // states are stored (all of the wave's memory operations complete); the member that
+        // arrives last combines the states (in member order, so the result does not depend on
+        // which member that is).  A striped team does it in two steps: the last member of
+        // each stripe folds the stripe's states into its first member's slot and then counts
+        // the stripe in; the last stripe folds the stripes' states.
+        // Hand-over between compute units: the states are written and read with the
+        // device-coherence cache policy (sc1) and the arrival atomic is issued only after the
+        // stores have completed (s_waitcnt 0); the release / acquire fences keep the compiler
+        // from moving memory accesses across the atomic.  That the completed sc1 stores are
+        // visible to sc1 loads from any compute unit is a property of this device's caches
+        // (no cache-wide write-back or invalidate is issued).
+        float *out_u = p.out + ((size_t)b * n_q_heads + (size_t)kvh * G) * D;
+        __builtin_amdgcn_s_waitcnt(0);
+        if (whole) {
+            combine_unit<D, G>(p, u, u, p.n_units, 1, lane, out_u);
+        } else {
             uint32_t arrived = 0;
             if (S == 1) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 if (lane == 0)
                     arrived = __hip_atomic_fetch_add(p.tile_ctr + 2 * p.n_waves + u, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                 if ((int)uniform(arrived) == team - 1)
-                    combine_unit<D, G>(p, sink, u, p.n_units, team, lane, out_u);
+                    combine_unit<D, G>(p, u, u, p.n_units, team, lane, out_u);
             } else {
                 const int sfirst = u + m0 * p.n_units; // place of the stripe's first member
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 if (lane == 0)
                     arrived = __hip_atomic_fetch_add(p.tile_ctr + p.n_waves + sfirst, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                 if ((int)uniform(arrived) == nst - 1) {
                     combine_stripe<D, G>(p, sfirst, p.n_units, nst, lane);
                     __builtin_amdgcn_s_waitcnt(0);
                     uint32_t done = 0;
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                     if (lane == 0)
                         done = __hip_atomic_fetch_add(p.tile_ctr + 2 * p.n_waves + u, 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                     if ((int)uniform(done) == S - 1)
-                        combine_unit<D, G>(p, sink, u, B * p.n_units, S, lane, out_u);
+                        combine_unit<D, G>(p, u, u, B * p.n_units, S, lane, out_u);
                 }
             }
         }
@@ -1760,10 +1771,11 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 template <int D, int G, int KF, int VF>
 hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
+    const unsigned qgrid = (unsigned)((p.n_qb + p.n_bch) * units); // records and BF16 chunks
     if (p.n_sink > 8)
-        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 32>), dim3((unsigned)(p.n_qb * units)), dim3(kWave * G), 0, s, p);
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 32>), dim3(qgrid), dim3(kWave * G), 0, s, p);
     else
-        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 8>), dim3((unsigned)(p.n_qb * units)), dim3(kWave * G), 0, s, p);
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 8>), dim3(qgrid), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
