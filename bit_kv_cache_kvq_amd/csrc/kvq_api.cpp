@@ -508,44 +508,111 @@ void kvq_set_decode_events(void *start_event, void *stop_event)
     g_decode_ev[1].store(stop_event);
 }
 
-// Symmetric Lloyd-Max quantiser for N(0,1): iterate centroid = conditional mean of the
-// cell and threshold = midpoint on the positive half, then mirror.  Conditional mean of
-// N(0,1) on (a, b]: (pdf(a) - pdf(b)) / (Q(a) - Q(b)) with Q the upper tail.
+// Symmetric Lloyd-Max quantiser for N(0,1), solved for its positive decision boundaries
+// b_1 < ... < b_{H-1} (b_0 = 0, b_H = inf, H = 2^(bits-1) cells on each side) by Newton's
+// method on the optimality conditions b_i = (c_{i-1} + c_i) / 2, where c_i is the mean of
+// N(0,1) on (b_i, b_{i+1}]: c_i = (pdf(b_i) - pdf(b_{i+1})) / (Q(b_i) - Q(b_{i+1})) with Q
+// the upper tail.  The Jacobian is tridiagonal, with dc_i/db_i = pdf(b_i) (c_i - b_i) / P_i
+// and dc_i/db_{i+1} = pdf(b_{i+1}) (b_{i+1} - c_i) / P_i (P_i the cell's mass).  The start is
+// the equal-mass boundaries; a step is halved until the boundaries stay ordered and the
+// residual shrinks.  Centroids and their midpoints are then rounded to fp32.
+namespace {
+
+double npdf(double x) { return exp(-0.5 * x * x) * 0.39894228040143267794; }
+double nupper(double x) { return 0.5 * erfc(x * 0.70710678118654752440); }
+
+// conditional means of the H positive cells for boundaries b[0..H] (b[0] = 0, b[H] = inf)
+void cell_means(const double *b, int H, double *c, double *mass)
+{
+    for (int i = 0; i < H; i++) {
+        const bool last = i == H - 1;
+        mass[i] = last ? nupper(b[i]) : nupper(b[i]) - nupper(b[i + 1]);
+        c[i] = (last ? npdf(b[i]) : npdf(b[i]) - npdf(b[i + 1])) / mass[i];
+    }
+}
+
+double residual(const double *b, int H, const double *c, double *F)
+{
+    double worst = 0.0;
+    for (int i = 1; i < H; i++) {
+        F[i] = b[i] - 0.5 * (c[i - 1] + c[i]);
+        worst = fmax(worst, fabs(F[i]));
+    }
+    return worst;
+}
+
+} // namespace
+
 kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *thresholds)
 {
     if (bits < 1 || bits > 6 || !centroids || !thresholds)
         return KVQ_ERR_ARG;
     const int L = 1 << bits, H = L / 2;
-    double pos[32], edge[33];
-    for (int i = 0; i < H; i++)
-        pos[i] = 3.0 * (i + 0.5) / H;
-    auto pdf = [](double x) { return exp(-0.5 * x * x) / sqrt(2.0 * M_PI); };
-    auto upper = [](double x) { return 0.5 * erfc(x / sqrt(2.0)); };
-    for (int iter = 0; iter < 200000; iter++) {
-        edge[0] = 0.0;
-        for (int i = 1; i < H; i++)
-            edge[i] = 0.5 * (pos[i - 1] + pos[i]);
-        double worst = 0.0;
-        for (int i = 0; i < H; i++) {
-            const double a = edge[i];
-            const bool last = (i == H - 1);
-            const double num = last ? pdf(a) : pdf(a) - pdf(edge[i + 1]);
-            const double den = last ? upper(a) : upper(a) - upper(edge[i + 1]);
-            const double next = num / den;
-            worst = fmax(worst, fabs(next - pos[i]));
-            pos[i] = next;
+    double b[33], c[32], mass[32], F[33], nb[33], nc[32], nmass[32], nF[33];
+    b[0] = 0.0;
+    for (int i = 1; i < H; i++) { // equal-mass start: Q(b_i) = (1 - i / H) / 2, by bisection
+        const double target = 0.5 * (1.0 - (double)i / H);
+        double lo = 0.0, hi = 12.0;
+        for (int k = 0; k < 200; k++) {
+            const double mid = 0.5 * (lo + hi);
+            (nupper(mid) > target ? lo : hi) = mid;
         }
-        if (worst < 1e-13)
-            break;
+        b[i] = 0.5 * (lo + hi);
     }
-    double full[64];
+    cell_means(b, H, c, mass);
+    double res = residual(b, H, c, F);
+    for (int iter = 0; iter < 200 && res > 1e-15; iter++) {
+        // tridiagonal Jacobian of F over b_1 .. b_{H-1}: sub (a), diagonal (d), super (u)
+        double a[33], d[33], u[33], rhs[33];
+        for (int i = 1; i < H; i++) {
+            const double dprev_di = npdf(b[i]) * (b[i] - c[i - 1]) / mass[i - 1]; // d c_{i-1} / d b_i
+            const double dcur_di = npdf(b[i]) * (c[i] - b[i]) / mass[i];          // d c_i / d b_i
+            d[i] = 1.0 - 0.5 * (dprev_di + dcur_di);
+            a[i] = i > 1 ? -0.5 * npdf(b[i - 1]) * (c[i - 1] - b[i - 1]) / mass[i - 1] : 0.0;
+            u[i] = i + 1 < H ? -0.5 * npdf(b[i + 1]) * (b[i + 1] - c[i]) / mass[i] : 0.0;
+            rhs[i] = -F[i];
+        }
+        for (int i = 2; i < H; i++) { // forward elimination
+            const double w = a[i] / d[i - 1];
+            d[i] -= w * u[i - 1];
+            rhs[i] -= w * rhs[i - 1];
+        }
+        double step[33];
+        for (int i = H - 1; i >= 1; i--)
+            step[i] = (rhs[i] - (i + 1 < H ? u[i] * step[i + 1] : 0.0)) / d[i];
+        double lam = 1.0;
+        for (int tries = 0; tries < 60; tries++, lam *= 0.5) {
+            nb[0] = 0.0;
+            bool ordered = true;
+            for (int i = 1; i < H; i++) {
+                nb[i] = b[i] + lam * step[i];
+                ordered = ordered && nb[i] > nb[i - 1];
+            }
+            if (!ordered)
+                continue;
+            cell_means(nb, H, nc, nmass);
+            const double nres = residual(nb, H, nc, nF);
+            if (nres < res || tries == 59) {
+                for (int i = 0; i < H; i++) {
+                    b[i] = nb[i];
+                    c[i] = nc[i];
+                    mass[i] = nmass[i];
+                }
+                for (int i = 1; i < H; i++)
+                    F[i] = nF[i];
+                res = nres;
+                break;
+            }
+        }
+    }
+    double full[64]; // the whole codebook, ascending
     for (int i = 0; i < H; i++) {
-        full[H + i] = pos[i];
-        full[H - 1 - i] = -pos[i];
+        full[H + i] = c[i];
+        full[H - 1 - i] = -c[i];
     }
     for (int i = 0; i < L; i++)
         centroids[i] = (float)full[i];
-    for (int i = 0; i + 1 < L; i++)
+    for (int i = 0; i + 1 < L; i++) // decision thresholds: the midpoints (in fp64, then rounded)
         thresholds[i] = (float)(0.5 * (full[i] + full[i + 1]));
     return KVQ_OK;
 }
