@@ -283,3 +283,43 @@ class Cache:
 
     def splits(self, n_q_heads) -> int:
         return int(lib().kvq_decode_splits(ctypes.byref(self.c), n_q_heads))
+
+    # ---- save / restore
+
+    GEOMETRY = ("batch", "n_kv_heads", "head_dim", "capacity", "n_sink", "k_format", "k_hadamard",
+                "k_ch0_bf16", "v_format", "v_clip", "n_recent", "rope_bucket")
+
+    def state_dict(self) -> dict:
+        """Everything a cache holds: its geometry and format fields, len, and every buffer as a
+        uint8 tensor (on the cache's device; torch.save moves nothing).  Plain ints, floats
+        and tensors only, so torch.load(..., weights_only=True) restores it."""
+        geo = {n: getattr(self.c, n) for n in self.GEOMETRY}
+        geo["v_clip"] = float(self.c.v_clip)
+        return {"geometry": geo, "len": int(self.c.len), "buffers": dict(self.buffers)}
+
+    @classmethod
+    def from_state_dict(cls, sd: dict, device="cuda") -> "Cache":
+        """A cache on `device` holding exactly the bytes and len of a state_dict()."""
+        geo = dict(sd["geometry"])
+        bufs = sd["buffers"]
+        kw = {}
+        if geo["rope_bucket"]:
+            kw["rope_table"] = bufs["rope_cs"].view(torch.float32).cpu()
+        if geo["v_format"] == V_KQV:
+            kw["qjl_signs"] = bufs["v_qjl_signs"].view(torch.int32).cpu().numpy().view(np.uint32)
+        c = cls(device=device, **geo, **kw)
+        if set(bufs) != set(c.buffers):
+            raise ValueError(f"buffers {sorted(bufs)} do not match the geometry's {sorted(c.buffers)}")
+        for name, t in bufs.items():
+            if t.dtype != torch.uint8 or t.numel() != c.buffers[name].numel():
+                raise ValueError(f"buffer {name}: {t.numel()} bytes of {t.dtype}, the geometry needs "
+                                 f"{c.buffers[name].numel()} bytes")
+            c.buffers[name].copy_(t)
+        n = int(sd["len"])
+        if not 0 <= n <= int(c.c.capacity):
+            raise ValueError(f"len {n} outside [0, {int(c.c.capacity)}]")
+        c.c.len = n
+        st = lib().kvq_validate(ctypes.byref(c.c))
+        if st != KVQ_OK:
+            raise KvqError(st, "kvq_validate")
+        return c

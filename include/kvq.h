@@ -197,7 +197,8 @@ size_t kvq_buffer_bytes(const kvq_cache *c, int32_t which);
 kvq_status kvq_validate(const kvq_cache *c);
 
 /* Numerical domain (what the parity tests cover).  Every stored parameter is an fp16, so
- * inputs must be finite with |x| < 65504, and the parameters that are norms must stay below
+ * inputs must be finite with |x| < 65504 in stored coordinates (see kvq_quant_append), and
+ * the parameters that are norms must stay below
  * 65504 too: Lloyd-Max keys need ||k||_2 < 65504 (rho is the key's L2 norm when rotated),
  * KQV values need ||v||_2 below about 3e4 (their residual norm is about 2.1 ||v||_2 at
  * head_dim 128).  Decode scores the query as fp16 halves of the query before the softmax
@@ -221,8 +222,10 @@ kvq_status kvq_validate(const kvq_cache *c);
  * recent window, new positions go to the ring in BF16 and the positions leaving the window
  * (old ones, and new ones already W behind the new end) are quantized from their BF16
  * copies; this takes two kernel launches, eviction first.  Inputs must be finite with
- * |x| < 65504 so the fp16 parameters stay finite; other inputs give unspecified codes.
- * n_new = 0 is a no-op.                                                                   */
+ * |x| < 65504 in stored coordinates so the fp16 parameters stay finite (the anchor rotation
+ * of bucket-relative RoPE can grow an entry by up to sqrt(2), and the unnormalised
+ * Walsh-Hadamard rotation of asymmetric keys by up to head_dim); other inputs give
+ * unspecified codes.  n_new = 0 is a no-op.                                               */
 kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, int32_t dtype,
                             int32_t n_new, void *stream);
 
@@ -281,9 +284,10 @@ size_t kvq_decode_noalloc_scratch_bytes(const kvq_cache *c, int32_t n_q_heads);
  * apart from querying the device's occupancy once.                                       */
 int32_t kvq_decode_splits(const kvq_cache *c, int32_t n_q_heads);
 
-/* Host helper: the 2^bits-level symmetric Lloyd-Max codebook of N(0,1) (fp64 iteration to
- * 1e-13, rounded to fp32), written to HOST arrays centroids[2^bits], thresholds[2^bits-1].
- * Only bits = 4 is used by the key formats.                                               */
+/* Host helper: the 2^bits-level symmetric Lloyd-Max codebook of N(0,1) (fp64 Newton
+ * iteration on the decision boundaries, rounded to fp32), written to HOST arrays
+ * centroids[2^bits], thresholds[2^bits-1] (the centroids' midpoints); 1 <= bits <= 6.
+ * bits = 4 serves the Lloyd-Max keys and bits = 3 the KQV values.                         */
 kvq_status kvq_codebook_gaussian(int32_t bits, float *centroids, float *thresholds);
 
 /* Tuning override for the work split: target number of 128-position tiles per decode wave,

@@ -219,3 +219,39 @@ def test_binding_refuses_other_dtypes_and_devices():
         c.decode(torch.zeros(1, 2, 64, dtype=torch.float64), 0.1)
     with pytest.raises(ValueError):
         c.append(torch.zeros(1, 1, 2, 64, device="meta"), torch.zeros(1, 1, 2, 64, device="meta"))
+
+
+def test_state_dict_round_trip_host():
+    """Cache.state_dict() goes through torch.save / torch.load(weights_only=True) and
+    from_state_dict() rebuilds a cache with the same geometry, len and bytes (host tensors:
+    the descriptor logic only); mismatched states are refused."""
+    import io
+
+    import torch
+
+    rng = np.random.default_rng(5)
+    c = B.Cache(2, 2, 128, 512, n_sink=4, k_format=B.K_LLOYD4, k_hadamard=1, v_format=B.V_KQV, n_recent=64,
+                rope_bucket=128, rope_table=rng.random((4, 64, 2), dtype=np.float32),
+                qjl_signs=rng.integers(0, 2**32, 4, dtype=np.uint32), device="cpu")
+    for t in c.buffers.values():
+        t.copy_(torch.from_numpy(rng.integers(0, 256, t.numel(), dtype=np.uint8)))
+    c.c.len = 300
+    f = io.BytesIO()
+    torch.save(c.state_dict(), f)
+    f.seek(0)
+    sd = torch.load(f, weights_only=True)
+    r = B.Cache.from_state_dict(sd, device="cpu")
+    assert r.len == 300 and set(r.buffers) == set(c.buffers)
+    for n in B.Cache.GEOMETRY:
+        assert getattr(r.c, n) == getattr(c.c, n), n
+    for k in c.buffers:
+        assert torch.equal(r.buffers[k], c.buffers[k]), k
+    bad = dict(sd, len=513)
+    with pytest.raises(ValueError):
+        B.Cache.from_state_dict(bad, device="cpu")
+    short = dict(sd, buffers=dict(sd["buffers"], k_codes=sd["buffers"]["k_codes"][:-16]))
+    with pytest.raises(ValueError):
+        B.Cache.from_state_dict(short, device="cpu")
+    extra = dict(sd, buffers=dict(sd["buffers"], k_ch0=torch.zeros(1024, dtype=torch.uint8)))
+    with pytest.raises(ValueError):
+        B.Cache.from_state_dict(extra, device="cpu")
