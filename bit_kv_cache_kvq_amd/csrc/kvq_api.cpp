@@ -282,8 +282,10 @@ static size_t part_region_bytes(const kvq_cache *c, int G)
     return round256(part_slots(c) * (size_t)G * (size_t)(c->head_dim + 4) * sizeof(float));
 }
 
-// BF16 chunk states (query prep -> decode): [unit][1 + ceil(n_recent / 64)][G][D + 4] fp32
-static int bf16_chunk_records(const kvq_cache *c) { return 1 + (c->n_recent + 63) / 64; }
+// BF16 chunk states (query prep -> decode): [unit][chunks][G][D + 4] fp32, chunk 0 the sinks,
+// then the window's part of each 64-aligned block of positions it touches (at most
+// ceil(n_recent / 64) + 1 blocks; none without a window)
+static int bf16_chunk_records(const kvq_cache *c) { return 1 + (c->n_recent > 0 ? (c->n_recent + 63) / 64 + 1 : 0); }
 
 static size_t bstate_region_bytes(const kvq_cache *c, int G)
 {
@@ -424,13 +426,14 @@ static kvq_status decode_launch(const kvq_cache *c, const void *q, int32_t q_dty
     p.v_qjl = c->v_qjl_signs;
     p.n_rb = rope_buckets(c);
     p.n_qb = c->rope_bucket > 0 && c->len > 0 ? (c->len + c->rope_bucket - 1) / c->rope_bucket : 1;
-    // BF16 positions: the sinks (chunk 0), then the recent window [wlo, len) 64 per chunk
+    // BF16 positions: the sinks (chunk 0), then the recent window [wlo, len) cut at multiples
+    // of 64 positions (one chunk per 64-aligned block it touches)
     p.bstate = reinterpret_cast<float *>(static_cast<char *>(ws) + l.bstate);
     p.bch_max = bf16_chunk_records(c);
     {
         const int ns = c->n_sink < c->len ? c->n_sink : c->len;
         const int wlo = p.q_end > ns ? p.q_end : ns;
-        p.n_bch = 1 + (c->len > wlo ? (c->len - wlo + 63) / 64 : 0);
+        p.n_bch = 1 + (c->len > wlo ? (c->len - 1) / 64 - wlo / 64 + 1 : 0);
     }
     hipEvent_t ev[2] = {static_cast<hipEvent_t>(g_decode_ev[0].load()), static_cast<hipEvent_t>(g_decode_ev[1].load())};
     if (!ev[0] || !ev[1])

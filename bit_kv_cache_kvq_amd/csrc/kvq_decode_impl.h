@@ -270,12 +270,13 @@ __device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB
 // One wave per query head of the GQA group in every workgroup.  Record workgroups, one per
 // (bucket, unit): stored-coordinate query (FWHT when keys are rotated), 16-channel group
 // energies (fp32 stride-halving tree, the order the format fixes), the group's mask, and the
-// head's query operands.  Chunk workgroups, one per (unit, chunk of up to 64 BF16
-// positions): chunk 0 the sinks, chunk c >= 1 the recent window's positions from
-// 64 (c - 1) on; each writes the softmax state (m, l, o) of its positions per head, which
-// the decode kernel folds into the unit's result.
-template <int D, int G, int KF, int SB>
-__global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
+// head's query operands.  BF16 chunks of up to 64 positions each get the softmax state
+// (m, l, o) of their positions per head, which the decode kernel folds into the unit's
+// result: chunk 0, the sinks, in bucket 0's record workgroup; chunk c >= 1, the recent
+// window's positions from 64 (c - 1) on, in a workgroup of its own (these come first in the
+// grid: the longest work).
+template <int D, int G, int KF>
+__global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
 {
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
@@ -284,60 +285,94 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     __shared__ float su_[G][D]; // the masked query before the softmax scale (operand source)
     __shared__ float se[G][NP];
     __shared__ float sam[G][NP];
-    __shared__ float sp[G][kWave];
     __shared__ int ssharp[G];
 
     const int lane = threadIdx.x % kWave;
     const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
-    // the chunk workgroups first (the longest work of the kernel), then the records
-    const int nchw = p.n_units * p.n_bch;
-    const bool state = (int)blockIdx.x < nchw; // a chunk workgroup: BF16 positions' state
-    const int bid = state ? (int)blockIdx.x : (int)blockIdx.x - nchw;
-    const int bk = state ? 0 : bid / p.n_units; // bucket of this record (0 without RoPE)
+    const int nwin = p.n_units * (p.n_bch - 1);
+    const bool wchunk = (int)blockIdx.x < nwin; // a window chunk's workgroup
+    const int bid = wchunk ? (int)blockIdx.x : (int)blockIdx.x - nwin;
+    const int bk = wchunk ? 0 : bid / p.n_units; // bucket of this record (0 without RoPE)
     const int unit = bid % p.n_units;
-    const int ch = state ? bid / p.n_units : 0; // BF16 chunk: 0 the sinks, c >= 1 the window's
+    const int ch = wchunk ? 1 + bid / p.n_units : 0; // BF16 chunk: 0 the sinks, c >= 1 the window's
+    const bool state = wchunk || bk == 0;            // computes chunk ch's softmax state
     const int b = unit / p.n_kv_heads;
     const int kvh = unit % p.n_kv_heads;
     const int n_q_heads = p.n_kv_heads * G;
     uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
     float *recf = reinterpret_cast<float *>(rec);
 
-    // BF16 sink rows, SB at a time (the last row repeated past n_sink); the first batch of
-    // keys and values is loaded here, with the query, so its latency overlaps the query's.
-    // SB is 8, or 32 for more than 8 sinks (64 sinks then cost two rounds of latency).
-    // (a chunk of the window sees no sinks)
-    const int n_sink = (state && ch > 0) ? 0 : (p.n_sink < p.len ? p.n_sink : p.len);
-    auto load_sinks = [&](const uint16_t *base, int t0, float (&dst)[SB][CPL]) {
-#pragma unroll
-        for (int j = 0; j < SB; j++) {
-            const int t = t0 + j < n_sink ? t0 + j : n_sink - 1;
-            const uint16_t *row = base + ((size_t)unit * p.n_sink + (t > 0 ? t : 0)) * D + lane * CPL;
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                dst[j][s] = bf16_to_f32(row[s]);
-        }
-    };
-    float kv[SB][CPL], vv[SB][CPL];
-    if (state && n_sink > 0) {
-        load_sinks(p.sink_k, 0, kv);
-        load_sinks(p.sink_v, 0, vv);
-    }
-
-    float yq[CPL]; // this head's query as given
+    // this head's query as given: its raw words are loaded first (the first thing waited
+    // for), converted after the row loads below have gone out
+    uint32_t qw[CPL];
     {
         const size_t qoff = ((size_t)b * n_q_heads + (size_t)kvh * G + h) * D + (size_t)lane * CPL;
         if (p.q_bf16) {
+            // (CPL = 2: both bf16 channels in one word, split when converted)
             const uint16_t *qb = static_cast<const uint16_t *>(p.q) + qoff;
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                yq[s] = bf16_to_f32(qb[s]);
+            qw[0] = CPL == 2 ? *reinterpret_cast<const uint32_t *>(qb) : (uint32_t)qb[0];
+            if constexpr (CPL == 2)
+                qw[1] = 0u;
         } else {
-            const float *qf = static_cast<const float *>(p.q) + qoff;
+            const uint32_t *qf = static_cast<const uint32_t *>(p.q) + qoff;
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                yq[s] = qf[s];
+                qw[s] = qf[s];
         }
     }
+
+    // The chunk's BF16 rows: row j < nrows is position pos0 + j -- sink j (sink_k / sink_v), or
+    // a window position in ring slot t mod W (Dual-QK sec. 3.3 / 4.1), the slots of a chunk
+    // taken from one wrap point.  Window chunks are the window's part of the 64-aligned
+    // position blocks, so none crosses a RoPE bucket edge (buckets are multiples of 128
+    // positions).  The loads go out right after the query's (which are waited for first), so
+    // their latency overlaps the query work: lane j's whole key row (lane j scores position
+    // pos0 + j over all channels) and this lane's CPL channels of every value row; registers
+    // of rows past nrows hold zeros.
+    const int ns_all = p.n_sink < p.len ? p.n_sink : p.len;
+    const int wlo = p.q_end > ns_all ? p.q_end : ns_all; // first window position
+    int pos0 = 0, nrows = 0;
+    if (state) {
+        if (ch == 0) {
+            nrows = ns_all;
+        } else {
+            const int a0 = (wlo / kWave + ch - 1) * kWave; // the chunk's aligned block
+            pos0 = wlo > a0 ? wlo : a0;
+            nrows = (p.len < a0 + kWave ? p.len : a0 + kWave) - pos0;
+        }
+    }
+    const uint16_t *kbase = ch == 0 ? p.sink_k : p.recent_k;
+    const uint16_t *vbase = ch == 0 ? p.sink_v : p.recent_v;
+    const int slot0 = ch == 0 ? 0 : pos0 % p.n_recent;
+    auto row_off = [&](int j) -> size_t {
+        const int jj = j < nrows ? j : nrows - 1;
+        if (ch == 0)
+            return ((size_t)unit * p.n_sink + (size_t)jj) * D;
+        const int sl = slot0 + jj;
+        return ((size_t)unit * p.n_recent + (size_t)(sl >= p.n_recent ? sl - p.n_recent : sl)) * D;
+    };
+    uint4 kr[D / 8];   // key row of position pos0 + lane (bf16; lanes past nrows: zeros)
+    uint32_t vr[kWave]; // value rows: this lane's CPL bf16 channels of row j (CPL = 1: low half)
+    if (nrows > 0) {
+        const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + row_off(lane));
+#pragma unroll
+        for (int c = 0; c < D / 8; c++)
+            kr[c] = lane < nrows ? krow[c] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < kWave; j++) {
+            if (j < nrows) {
+                const uint16_t *vrow = vbase + row_off(j) + (size_t)lane * CPL;
+                vr[j] = CPL == 2 ? *reinterpret_cast<const uint32_t *>(vrow) : (uint32_t)vrow[0];
+            } else {
+                vr[j] = 0u;
+            }
+        }
+    }
+
+    float yq[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; s++)
+        yq[s] = p.q_bf16 ? bf16_to_f32(s == 0 ? qw[0] & 0xFFFFu : qw[0] >> 16) : __uint_as_float(qw[s]);
     const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
 
     // Sharp query (Dual-QK sec. 1 and 3.2: query energy concentrated in a few channels): the
@@ -346,7 +381,7 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
     // sharp head gets a second, residual fp16 half per channel (about 22 bits per channel in
     // all); one half keeps 11 bits relative to each channel, which the logits of a few very
     // large channels outgrow.
-    {
+    if (!wchunk) {
         float v[CPL];
 #pragma unroll
         for (int s = 0; s < CPL; s++)
@@ -447,13 +482,16 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         __syncthreads();
         return mask;
     };
-    const uint32_t mask = prep(bk);
-    bool sharp = false; // (ssharp is visible after prep's barriers)
+    // the record's bucket, or the window chunk's
+    const uint32_t mask = prep(wchunk && p.rope_lw ? pos0 >> p.rope_lw : bk);
+    bool sharp = false; // (ssharp is visible after prep's barriers; records only)
+    if (!wchunk) {
 #pragma unroll
-    for (int hh = 0; hh < G; hh++)
-        sharp = sharp || ssharp[hh] != 0;
+        for (int hh = 0; hh < G; hh++)
+            sharp = sharp || ssharp[hh] != 0;
+    }
 
-    if (!state && bk == 0) {
+    if (!wchunk && bk == 0) {
         // the decode kernel's tile and arrival counters of this unit's stripes, at the places
         // u + k * units
         for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
@@ -464,16 +502,76 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
         if (threadIdx.x == 0)
             p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
     }
-    if (threadIdx.x == 0 && !state) {
+    if (threadIdx.x == 0 && !wchunk) {
         rec[C::OFF_MASK] = mask;
         rec[C::OFF_SHARP] = sharp ? 1u : 0u;
         if (p.mask_out)
             p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
     }
 
-    // ---- the query operands of this record
+    // ---- the chunk's softmax state for this wave's head (the query of the chunk's bucket):
+    // log2 max m, sum l and o = sum_t 2^(l_t - m) v_t over its positions.  Lane j's logit is
+    // the dot of its key row with the masked, scaled query (0 on pruned channels); the values
+    // then go through with the weights, lane owning channels lane*CPL..  An empty chunk (no
+    // sinks) writes the empty state.  (Before the record's operands: the chunk's rows then
+    // leave the registers first.)
     if (state) {
-        // (a chunk workgroup writes no record)
+        float M = -__builtin_inff(), L = 0.0f;
+        float o[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            o[s] = 0.0f;
+        if (nrows > 0) {
+            // four partial sums (sum e takes channels 8i + 2e and 8i + 2e + 1): short dependency
+            // chains for a kernel that runs one or two waves per SIMD
+            float dp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int c = 0; c < D / 8; c++) {
+                const uint32_t kk[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    dp[e] = fmaf(sq_[h][8 * c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
+                    dp[e] = fmaf(sq_[h][8 * c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dp[e]);
+                }
+            }
+            const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
+            const bool valid = lane < nrows;
+            const float lw = valid ? dot : -__builtin_inff();
+            M = wave_max_dpp(lw); // finite: the chunk has a position
+            const float pw = valid ? __builtin_amdgcn_exp2f(lw - M) : 0.0f;
+            L = wave_sum_dpp(pw);
+            // values: even and odd rows in two sums per channel (shorter chains)
+            float oe[2][CPL];
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                oe[0][s] = oe[1][s] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kWave; j++) {
+                if (j < nrows) { // (a uniform test: the loop stays unrolled, vr in registers)
+                    const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), j));
+                    oe[j & 1][0] = fmaf(pj, bf16_to_f32(vr[j] & 0xFFFFu), oe[j & 1][0]);
+                    if constexpr (CPL == 2)
+                        oe[j & 1][1] = fmaf(pj, bf16_to_f32(vr[j] >> 16), oe[j & 1][1]);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                o[s] = oe[0][s] + oe[1][s];
+        }
+        // the chunk's state, in the partial-state layout (m, l, two unused words, o[D])
+        float *st = p.bstate + ((size_t)(unit * p.bch_max + ch) * G + h) * part_rec<D>();
+        if (lane == 0) {
+            st[0] = M;
+            st[1] = L;
+        }
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            st[4 + lane * CPL + s] = o[s];
+    }
+
+    // ---- the query operands of this record
+    if (wchunk) {
+        return; // (a window chunk's workgroup writes no record)
     } else if constexpr (KF == KVQ_K_LLOYD4) {
         // fp16 pairs of the query before the softmax scale (which goes into the fp32
         // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
@@ -554,134 +652,6 @@ __global__ __launch_bounds__(kWave * G) void qprep_kernel(DecodeParams p)
             recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
             recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[h][0] * (g2 * 0x1p-24f) : 0.0f;
         }
-    }
-    if (!state)
-        return;
-
-    // Chunk 0: the BF16 sink positions (t < min(n_sink, len), all in bucket 0): dense dot over
-    // the kept channels, then the head's softmax state over them -- log2 max m, sum l and
-    // o = sum_t 2^(l_t - m) v_t -- which the decode kernel folds into the unit's result.
-    // Lanes own channels; one wave-wide sum per sink gives its logit, lane t keeps that of
-    // sink t.  (A window chunk has n_sink = 0 here: an empty state.)
-    {
-        float mine = -__builtin_inff();
-        for (int t0 = 0; t0 < n_sink; t0 += SB) {
-            if (t0 > 0)
-                load_sinks(p.sink_k, t0, kv);
-#pragma unroll
-            for (int j = 0; j < SB; j++) {
-                if (t0 + j >= n_sink)
-                    break;
-                float part = 0.0f;
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    part = fmaf(qr[s], kv[j][s], part);
-                const float tot = wave_sum_dpp(part);
-                mine = lane == t0 + j ? tot : mine;
-            }
-        }
-        const float m = wave_max_dpp(mine);
-        const float pr = lane < n_sink ? __builtin_amdgcn_exp2f(mine - m) : 0.0f;
-        sp[h][lane] = pr;
-        const float l = wave_sum_dpp(pr);
-        __syncthreads();
-        float o[CPL];
-#pragma unroll
-        for (int s = 0; s < CPL; s++)
-            o[s] = 0.0f;
-        for (int t0 = 0; t0 < n_sink; t0 += SB) {
-            if (t0 > 0)
-                load_sinks(p.sink_v, t0, vv);
-#pragma unroll
-            for (int j = 0; j < SB; j++) {
-                if (t0 + j >= n_sink)
-                    break;
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    o[s] = fmaf(sp[h][t0 + j], vv[j][s], o[s]);
-            }
-        }
-        // chunk c >= 1: recent BF16 window positions [wlo, len) from 64 (c - 1) on, 64 at most,
-        // in ring slots t mod W (Dual-QK sec. 3.3 / 4.1), one bucket's positions at a time
-        // (the query of that bucket), lane j scoring position c0 + j over all channels from
-        // its ring row, folded into the state (m, l, o) online
-        float M = m, L = l;
-        const int ns_all = p.n_sink < p.len ? p.n_sink : p.len;
-        const int wlo = p.q_end > ns_all ? p.q_end : ns_all;
-        const int wa = ch > 0 ? wlo + kWave * (ch - 1) : p.len;
-        const int wb = min(p.len, wa + kWave);
-        int qb = 0; // bucket whose query qr / sq_ hold
-        for (int s0 = wa; s0 < wb;) {
-            const int bs = p.rope_lw ? s0 >> p.rope_lw : 0;
-            const int s1 = p.rope_lw ? min(wb, (bs + 1) << p.rope_lw) : wb;
-            if (bs != qb) {
-                (void)prep(bs);
-                qb = bs;
-            }
-            for (int c0 = s0; c0 < s1; c0 += kWave) {
-                const int nc = s1 - c0 < kWave ? s1 - c0 : kWave; // positions in this chunk
-                const bool valid = lane < nc;
-                // ring slot of the chunk's position j: slot0 + j, wrapped once at most (the window
-                // holds at most W positions); positions past the chunk repeat its last one
-                const int slot0 = c0 % p.n_recent;
-                auto slot = [&](int j) {
-                    const int sl = slot0 + (j < nc ? j : nc - 1);
-                    return sl >= p.n_recent ? sl - p.n_recent : sl;
-                };
-                const uint16_t *krow = p.recent_k + ((size_t)unit * p.n_recent + (size_t)slot(lane)) * D;
-                float dot = 0.0f;
-#pragma unroll
-                for (int c = 0; c < D; c += 8) {
-                    const uint4 kw = *reinterpret_cast<const uint4 *>(krow + c);
-                    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        dot = fmaf(sq_[h][c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dot);
-                        dot = fmaf(sq_[h][c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dot);
-                    }
-                }
-                const float lw = valid ? dot : -__builtin_inff();
-                const float Mn = fmaxf(M, wave_max_dpp(lw)); // finite: the chunk has a position
-                const float fo = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-                const float pw = valid ? __builtin_amdgcn_exp2f(lw - Mn) : 0.0f;
-                L = fmaf(L, fo, wave_sum_dpp(pw));
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    o[s] *= fo;
-                // values, 32 positions per batch of loads (rows past the chunk repeat its last
-                // position with weight 0); lane owns channels lane*CPL ..
-#pragma unroll
-                for (int b0 = 0; b0 < kWave; b0 += 32) {
-                    float vw[32][CPL];
-#pragma unroll
-                    for (int jj = 0; jj < 32; jj++) {
-                        const uint16_t *vrow =
-                            p.recent_v + ((size_t)unit * p.n_recent + (size_t)slot(b0 + jj)) * D + lane * CPL;
-#pragma unroll
-                        for (int s = 0; s < CPL; s++)
-                            vw[jj][s] = bf16_to_f32(vrow[s]);
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < 32; jj++) {
-                        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), b0 + jj));
-#pragma unroll
-                        for (int s = 0; s < CPL; s++)
-                            o[s] = fmaf(pj, vw[jj][s], o[s]);
-                    }
-                }
-                M = Mn;
-            }
-            s0 = s1;
-        }
-        // the chunk's state, in the partial-state layout (m, l, two unused words, o[D])
-        float *st = p.bstate + ((size_t)(unit * p.bch_max + ch) * G + h) * part_rec<D>();
-        if (lane == 0) {
-            st[0] = M;
-            st[1] = L;
-        }
-#pragma unroll
-        for (int s = 0; s < CPL; s++)
-            st[4 + lane * CPL + s] = o[s];
     }
 }
 
@@ -1771,11 +1741,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 template <int D, int G, int KF, int VF>
 hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
-    const unsigned qgrid = (unsigned)((p.n_qb + p.n_bch) * units); // records and BF16 chunks
-    if (p.n_sink > 8)
-        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 32>), dim3(qgrid), dim3(kWave * G), 0, s, p);
-    else
-        hipLaunchKernelGGL((qprep_kernel<D, G, KF, 8>), dim3(qgrid), dim3(kWave * G), 0, s, p);
+    // window chunks, then the records (bucket 0's also takes the sinks)
+    const unsigned qgrid = (unsigned)((p.n_bch - 1 + p.n_qb) * units);
+    hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3(qgrid), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -67,8 +67,9 @@ struct DecodeParams {
     const float *v_codebook; // KQV values: 8 centroids
     const uint32_t *v_qjl;   // KQV values: the sketch's sign diagonal (bit set: -1)
     float *bstate;      // softmax states of the BF16 chunks [unit][bch_max][G][D + 4] (query prep)
-    int n_bch;          // BF16 chunks of this call per unit: the sinks, then 64 window positions each
-    int bch_max;        // chunk records per unit (1 + ceil(n_recent / 64))
+    int n_bch;          // BF16 chunks of this call per unit: the sinks, then the window's part of
+                        // each 64-aligned block of positions it touches
+    int bch_max;        // chunk records per unit (1, or 2 + ceil(n_recent / 64) with a window)
 };
 
 hipError_t launch_append(int head_dim, const AppendParams &p, hipStream_t s);

@@ -214,11 +214,15 @@ hipError_t launch_decode(int D, int G, int kfmt, int vfmt, int units, const Deco
     CHECK(p.n_waves >= units);
     CHECK(p.n_waves == units || (p.n_waves <= kMaxWaves && p.n_waves <= units * p.tiles_per_unit));
     CHECK(p.n_cu == 256);
-    // BF16 chunks: the sinks, then the window [wlo, len) in chunks of 64
+    // BF16 chunks: the sinks, then one per 64-aligned block of positions the window
+    // [wlo, len) touches
     const int ns = c->n_sink < c->len ? c->n_sink : c->len;
     const int wlo = p.q_end > ns ? p.q_end : ns;
-    CHECK(p.n_bch == 1 + (c->len > wlo ? (c->len - wlo + 63) / 64 : 0));
-    CHECK(p.bch_max == 1 + (c->n_recent + 63) / 64 && p.n_bch <= p.bch_max);
+    int blocks = 0;
+    for (int a = wlo / 64 * 64; wlo < c->len && a < c->len; a += 64)
+        blocks++;
+    CHECK(p.n_bch == 1 + blocks);
+    CHECK(p.n_bch <= p.bch_max && p.bch_max <= 2 + (c->n_recent + 63) / 64);
     const int n_rb = c->rope_bucket > 0 ? (c->capacity + c->rope_bucket - 1) / c->rope_bucket : 1;
     CHECK(p.n_rb == n_rb && p.n_qb >= 1 && p.n_qb <= n_rb);
     // workspace regions: inside the workspace, 16-byte aligned, pairwise disjoint; then
