@@ -267,14 +267,30 @@ __device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB
 }
 
 // ===================================================================== query prep
-// One wave per query head of the GQA group in every workgroup.  Record workgroups, one per
-// (bucket, unit): stored-coordinate query (FWHT when keys are rotated), 16-channel group
+// Query records of kRecBuckets of one unit's buckets per workgroup, and chunks of up to 64
+// BF16 positions.  One bucket each: a workgroup prepares its buckets one after the other
+// (two barriers and several cross-lane rounds each), and with four per workgroup the 65
+// buckets of a 128K-position sequence under 2048-position buckets took 19 us instead of 15.
+constexpr int kRecBuckets = 1;
+// Sinks beyond this many get a workgroup of their own (else bucket 0's record workgroup
+// scores them).
+constexpr int kSinksInRecord = 8;
+
+// Workgroups of the query-prep grid for a call: the window's chunks, the sinks' chunk when it
+// has a workgroup of its own, then the record groups (each class unit-minor).
+__host__ __device__ inline int qprep_groups(const DecodeParams &p)
+{
+    return (p.n_bch - 1) + (p.n_sink > kSinksInRecord ? 1 : 0) + (p.n_qb + kRecBuckets - 1) / kRecBuckets;
+}
+
+// One wave per query head of the GQA group in every workgroup.  Record workgroups: for each
+// of their buckets, the stored-coordinate query (FWHT when keys are rotated), 16-channel group
 // energies (fp32 stride-halving tree, the order the format fixes), the group's mask, and the
 // head's query operands.  BF16 chunks of up to 64 positions each get the softmax state
 // (m, l, o) of their positions per head, which the decode kernel folds into the unit's
-// result: chunk 0, the sinks, in bucket 0's record workgroup; chunk c >= 1, the recent
-// window's positions from 64 (c - 1) on, in a workgroup of its own (these come first in the
-// grid: the longest work).
+// result: chunk 0, the sinks (in bucket 0's record workgroup, or in one of its own when there
+// are many), and chunk c >= 1, the recent window's part of one 64-aligned block of positions
+// (the chunks come first in the grid: the longest work).
 template <int D, int G, int KF>
 __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
 {
@@ -289,18 +305,20 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
 
     const int lane = threadIdx.x % kWave;
     const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
-    const int nwin = p.n_units * (p.n_bch - 1);
-    const bool wchunk = (int)blockIdx.x < nwin; // a window chunk's workgroup
-    const int bid = wchunk ? (int)blockIdx.x : (int)blockIdx.x - nwin;
-    const int bk = wchunk ? 0 : bid / p.n_units; // bucket of this record (0 without RoPE)
-    const int unit = bid % p.n_units;
-    const int ch = wchunk ? 1 + bid / p.n_units : 0; // BF16 chunk: 0 the sinks, c >= 1 the window's
-    const bool state = wchunk || bk == 0;            // computes chunk ch's softmax state
+    const int U = p.n_units;
+    const bool sink_wg = p.n_sink > kSinksInRecord;
+    const int nwin = U * (p.n_bch - 1), nsk = sink_wg ? U : 0;
+    const int bi = (int)blockIdx.x;
+    const bool wchunk = bi < nwin;                  // a window chunk's workgroup
+    const bool chunk_only = bi < nwin + nsk;        // a chunk's workgroup (window or sinks)
+    const int bid = wchunk ? bi : chunk_only ? bi - nwin : bi - nwin - nsk;
+    const int unit = bid % U;
+    const int grp = chunk_only ? 0 : bid / U;       // record group: buckets grp * kRecBuckets ..
+    const int ch = wchunk ? 1 + bid / U : 0;        // BF16 chunk: 0 the sinks, c >= 1 the window's
+    const bool state = chunk_only || (grp == 0 && !sink_wg); // computes chunk ch's softmax state
     const int b = unit / p.n_kv_heads;
     const int kvh = unit % p.n_kv_heads;
     const int n_q_heads = p.n_kv_heads * G;
-    uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
-    float *recf = reinterpret_cast<float *>(rec);
 
     // this head's query as given: its raw words are loaded first (the first thing waited
     // for), converted after the row loads below have gone out
@@ -369,6 +387,18 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
         }
     }
 
+    // the buckets this workgroup prepares: a chunk's own (the sinks': 0), or the record
+    // group's; the (cos, sin) of their anchors for this lane's channels (bucket-relative RoPE)
+    const int bk0 = chunk_only ? (wchunk && p.rope_lw ? pos0 >> p.rope_lw : 0) : grp * kRecBuckets;
+    const int bk1 = chunk_only ? bk0 + 1 : min(p.n_qb, bk0 + kRecBuckets);
+    float2 csr[kRecBuckets][CPL];
+    if (p.rope_lw) {
+#pragma unroll
+        for (int j = 0; j < kRecBuckets; j++)
+            if (bk0 + j < bk1)
+                anchor_cs<CPL>(csr[j], p.rope_cs + (size_t)(bk0 + j) * D, lane);
+    }
+
     float yq[CPL];
 #pragma unroll
     for (int s = 0; s < CPL; s++)
@@ -381,7 +411,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     // sharp head gets a second, residual fp16 half per channel (about 22 bits per channel in
     // all); one half keeps 11 bits relative to each channel, which the logits of a few very
     // large channels outgrow.
-    if (!wchunk) {
+    if (!chunk_only) {
         float v[CPL];
 #pragma unroll
         for (int s = 0; s < CPL; s++)
@@ -405,18 +435,18 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             ssharp[h] = m1 > 8.0f * fmaxf(m5, 0.0f) ? 1 : 0;
     }
 
-    // The query of bucket bq in stored coordinates (rotated back by the bucket's anchor under
-    // bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys are rotated),
-    // its group energies, the mask, and this head's scaled, masked query in qr and sq_[h].
-    // Every wave of the workgroup calls it together (two barriers).
-    float qr[CPL];
-    auto prep = [&](int bq) -> uint32_t {
+    // The query of bucket bk0 + jb in stored coordinates (rotated back by the bucket's anchor
+    // under bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys are
+    // rotated), its group energies, the mask, and this head's scaled, masked query in sq_[h]
+    // (and before the scale, in su_[h]).  Every wave of the workgroup calls it together (two
+    // barriers).
+    auto prep = [&](int jb) -> uint32_t {
         float y[CPL];
 #pragma unroll
         for (int s = 0; s < CPL; s++)
             y[s] = yq[s];
         if (p.rope_lw)
-            anchor_rotate<CPL>(y, p.rope_cs + (size_t)bq * D, lane);
+            anchor_apply<CPL>(y, csr[jb], lane);
         if (p.rotate)
             fwht_wave<CPL>(y, lane);
         float sq[CPL], am = 0.0f;
@@ -476,22 +506,12 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             const int c = lane * CPL + s;
             const bool kept = (mask >> (c / 16)) & 1u;
             su_[h][c] = kept ? sq_[h][c] : 0.0f;
-            qr[s] = kept ? sq_[h][c] * qscale : 0.0f;
-            sq_[h][c] = qr[s];
+            sq_[h][c] = kept ? sq_[h][c] * qscale : 0.0f;
         }
         __syncthreads();
         return mask;
     };
-    // the record's bucket, or the window chunk's
-    const uint32_t mask = prep(wchunk && p.rope_lw ? pos0 >> p.rope_lw : bk);
-    bool sharp = false; // (ssharp is visible after prep's barriers; records only)
-    if (!wchunk) {
-#pragma unroll
-        for (int hh = 0; hh < G; hh++)
-            sharp = sharp || ssharp[hh] != 0;
-    }
-
-    if (!wchunk && bk == 0) {
+    if (!chunk_only && grp == 0) {
         // the decode kernel's tile and arrival counters of this unit's stripes, at the places
         // u + k * units
         for (int k = threadIdx.x; k < p.n_waves / p.n_units + 1; k += kWave * G)
@@ -502,19 +522,14 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
         if (threadIdx.x == 0)
             p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
     }
-    if (threadIdx.x == 0 && !wchunk) {
-        rec[C::OFF_MASK] = mask;
-        rec[C::OFF_SHARP] = sharp ? 1u : 0u;
-        if (p.mask_out)
-            p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
-    }
 
+    const uint32_t mask0 = prep(0); // bucket bk0's
     // ---- the chunk's softmax state for this wave's head (the query of the chunk's bucket):
     // log2 max m, sum l and o = sum_t 2^(l_t - m) v_t over its positions.  Lane j's logit is
     // the dot of its key row with the masked, scaled query (0 on pruned channels); the values
     // then go through with the weights, lane owning channels lane*CPL..  An empty chunk (no
-    // sinks) writes the empty state.  (Before the record's operands: the chunk's rows then
-    // leave the registers first.)
+    // sinks) writes the empty state.  (Before the records: the chunk's rows then leave the
+    // registers first.)
     if (state) {
         float M = -__builtin_inff(), L = 0.0f;
         float o[CPL];
@@ -569,90 +584,116 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             st[4 + lane * CPL + s] = o[s];
     }
 
-    // ---- the query operands of this record
-    if (wchunk) {
-        return; // (a window chunk's workgroup writes no record)
-    } else if constexpr (KF == KVQ_K_LLOYD4) {
-        // fp16 pairs of the query before the softmax scale (which goes into the fp32
-        // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
-        // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
-        float amax = 0.0f;
+    if (chunk_only)
+        return; // (a chunk's workgroup writes no record)
+
+    // (unrolled over the group's buckets: the anchors' (cos, sin) stay in registers)
 #pragma unroll
-        for (int hh = 0; hh < G; hh++)
+    for (int jb = 0; jb < kRecBuckets; jb++) {
+        const int bk = bk0 + jb;
+        if (bk < bk1) {
+            const uint32_t mask = jb == 0 ? mask0 : prep(jb);
+            uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
+            float *recf = reinterpret_cast<float *>(rec);
+            bool sharp = false; // (ssharp is visible after prep's barriers)
 #pragma unroll
-            for (int g = 0; g < NP; g++)
-                if (mask >> g & 1u)
-                    amax = fmaxf(amax, sam[hh][g]);
-        int ex = 0;
-        (void)frexpf(amax, &ex);
-        const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
-        if (lane < KROWS * PPW) {
-            const int r = lane / PPW, j = lane % PPW;
-            const int ca = 8 * r + 2 * j;
-            const float a = su_[h][ca] * g2, b2 = su_[h][ca + 1] * g2;
-            const uint32_t hi = pack_f16x2(a, b2);
-            rec[C::OFF_QP + (r * G + h) * QW + j] = hi;
-            rec[C::OFF_QPL + (r * G + h) * QW + j] = sharp ? pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi)) : 0u;
-        }
-        if (lane == 0) {
-            recf[C::OFF_QSC + h] = qscale / g2;
-            recf[C::OFF_Q0 + h] = 0.0f;
-        }
-    } else {
-        // fp16 query halves.  The decode kernel spreads a key word into registers whose two
-        // halves hold the codes of channels (c, c + 32/KB/2) as subnormal integers
-        // P(c) * code * 2^-24 (place factor P, see spread_asym), and multiplies them with
-        // v_dot2_f32_f16 against halves q_c * g2 / P(c).  Every product is then
-        // q~_c * g2 * code_c * 2^-24 with q~ the query rounded to fp16: each channel keeps
-        // 11 bits relative to its own magnitude, so one sharp query channel costs the others
-        // nothing.  The halves hold the query before the softmax scale (which goes into the
-        // fp32 accumulator unit), and g2 (a power of two) puts the head's largest kept |q| in
-        // [2^12, 2^13): a bf16 query is then carried exactly.  Channel 0 (when protected) is
-        // scored from its BF16 copy: its half is 0.
-        float am = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < CPL; s2++) {
-            const int c = lane * CPL + s2;
-            if (!(p.ch0 && c == 0))
-                am = fmaxf(am, fabsf(su_[h][c]));
-        }
-        am = wave_max_dpp(am);
-        int ex = 0;
-        (void)frexpf(am, &ex);
-        const float g2 = am > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
-        // the half of channel c (0 for the protected channel 0) and, for a sharp query, the
-        // half of what it leaves (the residual, exact in fp32); g2 and the place factors are
-        // powers of two
-        auto qval = [&](int c) { return (p.ch0 && c == 0) ? 0.0f : su_[h][c] * (g2 / asym_place<KB>(c)); };
-        auto qhi = [&](int c) -> uint32_t { return f32_to_f16(qval(c)); };
-        auto qlo = [&](int c) -> uint32_t { return sharp ? f32_to_f16(qval(c) - f16_to_f32(qhi(c))) : 0u; };
-        // key word r, spread register k: halves hold channels asym_chan<KB>(r, k, 0 / 1)
-        if (lane < KROWS * QW) {
-            const int r = lane / QW, k = lane % QW;
-            const int c0 = asym_chan<KB>(r, k, 0), c1 = asym_chan<KB>(r, k, 1);
-            rec[C::OFF_QP + (r * G + h) * QW + k] = qhi(c0) | (qhi(c1) << 16);
-            rec[C::OFF_QPL + (r * G + h) * QW + k] = qlo(c0) | (qlo(c1) << 16);
-        }
-        // zero-term sums: the query as the halves carry it, in accumulator units g2 * 2^-24,
-        // summed over each 32-channel group (lanes of a group: 32/CPL consecutive lanes)
-        {
-            float si = 0.0f;
-#pragma unroll
-            for (int s2 = 0; s2 < CPL; s2++) {
-                const int c = lane * CPL + s2;
-                si += (f16_to_f32(qhi(c)) + f16_to_f32(qlo(c))) * (asym_place<KB>(c) * 0x1p-24f);
+            for (int hh = 0; hh < G; hh++)
+                sharp = sharp || ssharp[hh] != 0;
+            if (threadIdx.x == 0) {
+                rec[C::OFF_MASK] = mask;
+                rec[C::OFF_SHARP] = sharp ? 1u : 0u;
+                if (p.mask_out)
+                    p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
             }
+
+            // ---- the query operands of this record
+            if constexpr (KF == KVQ_K_LLOYD4) {
+                // fp16 pairs of the query before the softmax scale (which goes into the fp32
+                // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
+                // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
+                float amax = 0.0f;
 #pragma unroll
-            for (int m = 16 / CPL; m >= 1; m >>= 1)
-                si += __shfl_xor(si, m);
-            if (lane % (32 / CPL) == 0)
-                recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si;
+                for (int hh = 0; hh < G; hh++)
+#pragma unroll
+                    for (int g = 0; g < NP; g++)
+                        if (mask >> g & 1u)
+                            amax = fmaxf(amax, sam[hh][g]);
+                int ex = 0;
+                (void)frexpf(amax, &ex);
+                const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
+                if (lane < KROWS * PPW) {
+                    const int r = lane / PPW, j = lane % PPW;
+                    const int ca = 8 * r + 2 * j;
+                    const float a = su_[h][ca] * g2, b2 = su_[h][ca + 1] * g2;
+                    const uint32_t hi = pack_f16x2(a, b2);
+                    rec[C::OFF_QP + (r * G + h) * QW + j] = hi;
+                    rec[C::OFF_QPL + (r * G + h) * QW + j] = sharp ? pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi)) : 0u;
+                }
+                if (lane == 0) {
+                    recf[C::OFF_QSC + h] = qscale / g2;
+                    recf[C::OFF_Q0 + h] = 0.0f;
+                }
+            } else {
+                // fp16 query halves.  The decode kernel spreads a key word into registers whose two
+                // halves hold the codes of channels (c, c + 32/KB/2) as subnormal integers
+                // P(c) * code * 2^-24 (place factor P, see spread_asym), and multiplies them with
+                // v_dot2_f32_f16 against halves q_c * g2 / P(c).  Every product is then
+                // q~_c * g2 * code_c * 2^-24 with q~ the query rounded to fp16: each channel keeps
+                // 11 bits relative to its own magnitude, so one sharp query channel costs the others
+                // nothing.  The halves hold the query before the softmax scale (which goes into the
+                // fp32 accumulator unit), and g2 (a power of two) puts the head's largest kept |q| in
+                // [2^12, 2^13): a bf16 query is then carried exactly.  Channel 0 (when protected) is
+                // scored from its BF16 copy: its half is 0.
+                float am = 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < CPL; s2++) {
+                    const int c = lane * CPL + s2;
+                    if (!(p.ch0 && c == 0))
+                        am = fmaxf(am, fabsf(su_[h][c]));
+                }
+                am = wave_max_dpp(am);
+                int ex = 0;
+                (void)frexpf(am, &ex);
+                const float g2 = am > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
+                // the half of channel c (0 for the protected channel 0) and, for a sharp query, the
+                // half of what it leaves (the residual, exact in fp32); g2 and the place factors are
+                // powers of two
+                auto qval = [&](int c) { return (p.ch0 && c == 0) ? 0.0f : su_[h][c] * (g2 / asym_place<KB>(c)); };
+                auto qhi = [&](int c) -> uint32_t { return f32_to_f16(qval(c)); };
+                auto qlo = [&](int c) -> uint32_t { return sharp ? f32_to_f16(qval(c) - f16_to_f32(qhi(c))) : 0u; };
+                // key word r, spread register k: halves hold channels asym_chan<KB>(r, k, 0 / 1)
+                if (lane < KROWS * QW) {
+                    const int r = lane / QW, k = lane % QW;
+                    const int c0 = asym_chan<KB>(r, k, 0), c1 = asym_chan<KB>(r, k, 1);
+                    rec[C::OFF_QP + (r * G + h) * QW + k] = qhi(c0) | (qhi(c1) << 16);
+                    rec[C::OFF_QPL + (r * G + h) * QW + k] = qlo(c0) | (qlo(c1) << 16);
+                }
+                // zero-term sums: the query as the halves carry it, in accumulator units g2 * 2^-24,
+                // summed over each 32-channel group (lanes of a group: 32/CPL consecutive lanes)
+                {
+                    float si = 0.0f;
+#pragma unroll
+                    for (int s2 = 0; s2 < CPL; s2++) {
+                        const int c = lane * CPL + s2;
+                        si += (f16_to_f32(qhi(c)) + f16_to_f32(qlo(c))) * (asym_place<KB>(c) * 0x1p-24f);
+                    }
+#pragma unroll
+                    for (int m = 16 / CPL; m >= 1; m >>= 1)
+                        si += __shfl_xor(si, m);
+                    if (lane % (32 / CPL) == 0)
+                        recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si;
+                }
+                if (lane == 0) {
+                    recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
+                    recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[h][0] * (g2 * 0x1p-24f) : 0.0f;
+                }
+            }
+            // (the next bucket's prep() rewrites the shared query arrays that this bucket's
+            // operands read across heads)
+            if (bk + 1 < bk1)
+                __syncthreads();
         }
-        if (lane == 0) {
-            recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
-            recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[h][0] * (g2 * 0x1p-24f) : 0.0f;
-        }
-    }
+    } // buckets
 }
 
 // ===================================================================== decode
@@ -1741,8 +1782,8 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 template <int D, int G, int KF, int VF>
 hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], hipStream_t s)
 {
-    // window chunks, then the records (bucket 0's also takes the sinks)
-    const unsigned qgrid = (unsigned)((p.n_bch - 1 + p.n_qb) * units);
+    // window chunks, the sinks' chunk (many sinks), then the record groups
+    const unsigned qgrid = (unsigned)(qprep_groups(p) * units);
     hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3(qgrid), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -78,19 +78,35 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgc
 // which sits in lane l ^ 32.  cs = the bucket's (cos, sin) pairs [D/2][2].  With (c, s) of
 // pair i: y_i <- y_i c + y_{i+D/2} s, y_{i+D/2} <- y_{i+D/2} c - y_i s, each product rounded
 // before the sum (no contraction), as the format fixes.
+// anchor_cs: this lane's (c, s) pairs of a bucket; anchor_apply: the rotation with them.
 template <int CPL>
-__device__ __forceinline__ void anchor_rotate(float (&y)[CPL], const float *__restrict__ cs, int lane)
+__device__ __forceinline__ void anchor_cs(float2 (&e)[CPL], const float *__restrict__ cs, int lane)
+{
+#pragma unroll
+    for (int s = 0; s < CPL; s++)
+        e[s] = *reinterpret_cast<const float2 *>(cs + 2 * ((lane & 31) * CPL + s));
+}
+
+template <int CPL>
+__device__ __forceinline__ void anchor_apply(float (&y)[CPL], const float2 (&e)[CPL], int lane)
 {
 #pragma clang fp contract(off)
     const bool upper = lane >= 32;
 #pragma unroll
     for (int s = 0; s < CPL; s++) {
         const float other = __shfl_xor(y[s], 32);
-        const float2 e = *reinterpret_cast<const float2 *>(cs + 2 * ((lane & 31) * CPL + s));
-        const float a = y[s] * e.x;
-        const float b = other * e.y;
+        const float a = y[s] * e[s].x;
+        const float b = other * e[s].y;
         y[s] = upper ? a - b : a + b;
     }
+}
+
+template <int CPL>
+__device__ __forceinline__ void anchor_rotate(float (&y)[CPL], const float *__restrict__ cs, int lane)
+{
+    float2 e[CPL];
+    anchor_cs<CPL>(e, cs, lane);
+    anchor_apply<CPL>(y, e, lane);
 }
 
 __device__ __forceinline__ float uniformf(float v)
