@@ -139,7 +139,8 @@ struct Plan {
 // Work split of one decode call.  Every unit's positions [0, len) are cut into 128-position
 // tiles (at least one, so sink-only and empty contexts still produce their output).  The
 // grid is n_waves one-wave workgroups, n_waves >= units: wave w serves unit w % units, and
-// the waves of one unit draw its tiles from a shared counter at run time.  n_waves = the
+// the waves of one unit share its tiles (static shares, the last quarter of each stripe drawn
+// from a counter at run time; see the decode kernel).  n_waves = the
 // resident one-wave workgroups of the kernel instantiation (`slots`), so one pass of waves
 // covers the device, capped at one wave per tile; kvq_set_split_tiles overrides it with a
 // target number of tiles per wave.

@@ -1,7 +1,7 @@
 // kvq_decode.hip -- decode attention over the packed low-bit cache: the host side of the
 // decode kernels (launch, work-split queries) and the instantiations for INT4 values per
-// 32-channel group.  The kernels are in kvq_decode_impl.h; kvq_decode_v2.hip instantiates
-// them for per-token INT2 values.
+// 32-channel group.  The kernels are in kvq_decode_impl.h; kvq_decode_v2.hip and
+// kvq_decode_v3.hip instantiate them for per-token INT2 and KQV values.
 #include "kvq_decode_impl.h"
 
 namespace kvq {

@@ -1,6 +1,6 @@
 // kvq_decode_impl.h -- decode attention scored straight from the packed low-bit cache.
-// (Kernel templates; kvq_decode.hip and kvq_decode_v2.hip instantiate them for the two value
-// formats, in parallel compilations.)
+// (Kernel templates; kvq_decode.hip, kvq_decode_v2.hip and kvq_decode_v3.hip instantiate them
+// for the three value formats, in parallel compilations.)
 //
 // What it computes (the pages this library implements):
 //   * logits from packed key codes without decompressing keys (TurboQuant on Quantized
@@ -12,35 +12,34 @@
 //   * an optional per-GQA-group channel mask from the current queries (Dual-QK sec. 3.2,
 //     C.2): only the kept 16-channel key rows are loaded (channel-major rows, sec. 3.3);
 //   * one softmax over all positions (Dual-QK sec. 3.4), computed online by each wave over
-//     its tiles; the waves sharing a unit combine their states at the end (the last one to
-//     finish does it, after an agent-scope release / acquire on a per-unit counter);
-//   * values from INT4 codes per 32-channel group, or per-token INT2 codes (Dual-QK sec.
-//     B.2): o = sum_t p_t s_{t,g} code_{t,c} + sum_t p_t z_{t,g}.
+//     its tiles and by the query prep over the BF16 positions (sinks, recent window); the
+//     last wave of a unit's team to finish folds all of these states;
+//   * values from INT4 codes per 32-channel group, per-token INT2 codes (Dual-QK sec. B.2),
+//     or KQV's centroids and sketch bits: o = sum_t p_t s_{t,g} code_{t,c} + sum_t p_t z_{t,g}.
 //
 // Two kernels per decode call:
-//   qprep   one workgroup per (sequence, KV head), one wave per query head: query in stored
-//           coordinates, pruning mask, the integer / fp16 query operands and the sink
-//           positions' softmax state, written once to a small per-unit record.
+//   qprep   one wave per query head in every workgroup: per (unit, bucket) a record with the
+//           mask and the fp16 query operands; per chunk of up to 64 BF16 positions (sinks,
+//           recent window) the softmax state of those positions.
 //   decode  one wave per resident SIMD slot (at least one per unit); the waves serving a
-//           unit draw its 128-position tiles from a counter.  The query record is read
-//           with uniform loads, so its operands sit in scalar registers.
-//           * score phase, lane per position: each lane scores 2 consecutive positions; a
-//             key row is one dwordx2 load per lane (512 B contiguous per wave).  Asymmetric
-//             codes are spread into bytes by shift+mask and multiplied with v_dot4_i32_i8
-//             against the query held as a 16-bit integer (14 bits of magnitude for INT2
-//             keys, whose spread bytes carry code or 4*code) in two signed-byte planes: exact
-//             int32 sums, and the zero-point term uses the same integer query, so code and
-//             zero terms together equal q_int . k^ with no cancellation between them
-//             (heavy-tailed keys make the group zero large).  Lloyd-Max codes go through an
-//             LDS table of fp16 centroid pairs and v_dot2_f32_f16 against fp16 query pairs.
+//           unit take its 128-position tiles in static shares, the last quarter drawn from
+//           a counter.  The query record is read with uniform loads, so its operands sit in
+//           scalar registers.
+//           * score phase, lane per 2 positions: a key row is one dwordx2 load per lane
+//             (512 B contiguous per wave).  An asymmetric code word is spread by masking
+//             into registers whose fp16 halves hold one channel's code times a place factor
+//             as a subnormal integer, and v_dot2_f32_f16 multiplies them with fp16 halves of
+//             the query divided by the place factors: exact products, fp32 sums; a sharp
+//             query adds the residual halves.  Lloyd-Max codes go through an LDS table of
+//             fp16 centroid pairs and v_dot2_f32_f16 against fp16 query pairs.
 //           * softmax: a running maximum per head; a wave-wide DPP reduction and a rescale
 //             happen only when a tile holds a logit well above it (rare after the first
-//             tiles).
+//             tiles), or when a value scale needs a lower weight exponent.
 //           * value phase, lane per 8 channels: v_dot2_f32_f16 over position pairs (value
-//             words interleave two positions); a 4-bit code masked into the low mantissa
-//             bits of a half is the subnormal integer code * 2^-24 (or * 2^-20), so no
-//             conversion is needed.  The fp16 weights p*s of a position pair and scale
-//             group reach the value lanes through LDS, all heads in one 16-byte read.
+//             words interleave two positions); a code masked into the low mantissa bits of
+//             a half is a subnormal integer, so no conversion is needed.  The fp16 weights
+//             p*s*2^vexp of a position pair and scale group reach the value lanes through
+//             LDS, all heads in one 16-byte read.
 //           * the next tile's key-side words are loaded before the value phase of the
 //             current one; cache reads are non-temporal (each byte is read once).
 // No MFMA: this is a bandwidth-bound scan.

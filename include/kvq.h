@@ -230,9 +230,10 @@ kvq_status kvq_quant_append(kvq_cache *c, const void *k_new, const void *v_new, 
                             int32_t n_new, void *stream);
 
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (any len up to capacity)
- * and n_q_heads.  The workspace holds the per-unit query records, the partial softmax
- * states of units shared by several decode waves and one tile counter per unit; its
- * contents need no initialisation and are scratch between calls.                          */
+ * and n_q_heads.  The workspace holds the query records (one per sequence, KV head and RoPE
+ * bucket), the partial softmax states of the decode waves, the softmax states of the BF16
+ * positions (sinks and recent window) and the tile and arrival counters; its contents need
+ * no initialisation and are scratch between calls.                                         */
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t n_q_heads);
 
 /* Decode attention for one query step per sequence over positions [0, len).
