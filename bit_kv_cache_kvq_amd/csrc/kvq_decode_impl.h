@@ -368,9 +368,26 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
         const int sl = slot0 + jj;
         return ((size_t)unit * p.n_recent + (size_t)(sl >= p.n_recent ? sl - p.n_recent : sl)) * D;
     };
+    // A record workgroup's chunk (at most kSinksInRecord sinks) takes the few-rows path
+    // instead: every lane loads its CPL channels of each sink row, key j into vr[j] and value
+    // j into vr[kSinksInRecord + j]; each sink's logit is one wave-wide sum.
+    const bool few = state && !chunk_only;
+    static_assert(2 * kSinksInRecord <= kWave, "the few-rows path keeps its rows in vr");
     uint4 kr[D / 8];   // key row of position pos0 + lane (bf16; lanes past nrows: zeros)
     uint32_t vr[kWave]; // value rows: this lane's CPL bf16 channels of row j (CPL = 1: low half)
-    if (nrows > 0) {
+    if (few) {
+#pragma unroll
+        for (int j = 0; j < kSinksInRecord; j++) {
+            if (j < nrows) {
+                const size_t off = ((size_t)unit * p.n_sink + (size_t)j) * D + (size_t)lane * CPL;
+                vr[j] = CPL == 2 ? *reinterpret_cast<const uint32_t *>(p.sink_k + off) : (uint32_t)p.sink_k[off];
+                vr[kSinksInRecord + j] =
+                    CPL == 2 ? *reinterpret_cast<const uint32_t *>(p.sink_v + off) : (uint32_t)p.sink_v[off];
+            } else {
+                vr[j] = vr[kSinksInRecord + j] = 0u;
+            }
+        }
+    } else if (nrows > 0) {
         const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + row_off(lane));
 #pragma unroll
         for (int c = 0; c < D / 8; c++)
@@ -535,7 +552,37 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
 #pragma unroll
         for (int s = 0; s < CPL; s++)
             o[s] = 0.0f;
-        if (nrows > 0) {
+        if (few && nrows > 0) {
+            // (lane owns channels lane*CPL..: sink j's logit is a wave-wide sum; lane j keeps it)
+            float qo[CPL];
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                qo[s] = sq_[h][lane * CPL + s];
+            float mine = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < kSinksInRecord; j++) {
+                if (j < nrows) {
+                    float part = qo[0] * bf16_to_f32(vr[j] & 0xFFFFu);
+                    if constexpr (CPL == 2)
+                        part = fmaf(qo[1], bf16_to_f32(vr[j] >> 16), part);
+                    const float tot = wave_sum_dpp(part);
+                    mine = lane == j ? tot : mine;
+                }
+            }
+            M = wave_max_dpp(mine);
+            const float pw = lane < nrows ? __builtin_amdgcn_exp2f(mine - M) : 0.0f;
+            L = wave_sum_dpp(pw);
+#pragma unroll
+            for (int j = 0; j < kSinksInRecord; j++) {
+                if (j < nrows) {
+                    const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), j));
+                    const uint32_t v = vr[kSinksInRecord + j];
+                    o[0] = fmaf(pj, bf16_to_f32(v & 0xFFFFu), o[0]);
+                    if constexpr (CPL == 2)
+                        o[1] = fmaf(pj, bf16_to_f32(v >> 16), o[1]);
+                }
+            }
+        } else if (nrows > 0) {
             // four partial sums (sum e takes channels 8i + 2e and 8i + 2e + 1): short dependency
             // chains for a kernel that runs one or two waves per SIMD
             float dp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
