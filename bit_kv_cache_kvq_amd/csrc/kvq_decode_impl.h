@@ -266,11 +266,9 @@ __device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB
 }
 
 // ===================================================================== query prep
-// Query records of kRecBuckets of one unit's buckets per workgroup, and chunks of up to 64
-// BF16 positions.  One bucket each: a workgroup prepares its buckets one after the other
-// (two barriers and several cross-lane rounds each), and with four per workgroup the 65
-// buckets of a 128K-position sequence under 2048-position buckets took 19 us instead of 15.
-constexpr int kRecBuckets = 1;
+// Query records of up to kRecBuckets of one unit's buckets per workgroup, prepared side by
+// side (one pair of barriers for all of them), and chunks of up to 64 BF16 positions.
+constexpr int kRecBuckets = 4;
 // Sinks beyond this many get a workgroup of their own (else bucket 0's record workgroup
 // scores them).
 constexpr int kSinksInRecord = 8;
@@ -296,10 +294,10 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
     constexpr int CPL = C::CPL, QW = C::QW;
-    __shared__ float sq_[G][D];
-    __shared__ float su_[G][D]; // the masked query before the softmax scale (operand source)
-    __shared__ float se[G][NP];
-    __shared__ float sam[G][NP];
+    __shared__ float sq_[kRecBuckets][G][D];
+    __shared__ float su_[kRecBuckets][G][D]; // the masked query before the softmax scale (operand source)
+    __shared__ float se[kRecBuckets][G][NP];
+    __shared__ float sam[kRecBuckets][G][NP];
     __shared__ int ssharp[G];
 
     const int lane = threadIdx.x % kWave;
@@ -451,81 +449,86 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             ssharp[h] = m1 > 8.0f * fmaxf(m5, 0.0f) ? 1 : 0;
     }
 
-    // The query of bucket bk0 + jb in stored coordinates (rotated back by the bucket's anchor
-    // under bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys are
-    // rotated), its group energies, the mask, and this head's scaled, masked query in sq_[h]
-    // (and before the scale, in su_[h]).  Every wave of the workgroup calls it together (two
-    // barriers).
-    auto prep = [&](int jb) -> uint32_t {
-        float y[CPL];
+    // The queries of buckets bk0 .. bk1 - 1 in stored coordinates (rotated back by the bucket's
+    // anchor under bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys
+    // are rotated), their group energies, masks (masks[jb]), and this head's scaled, masked
+    // query per bucket in sq_[jb][h] (before the scale, in su_[jb][h]).  The buckets go through
+    // each step side by side, so their latencies overlap and one pair of barriers serves all.
+    // Every wave of the workgroup calls it.
+    uint32_t masks[kRecBuckets];
+    auto prep_all = [&]() {
 #pragma unroll
-        for (int s = 0; s < CPL; s++)
-            y[s] = yq[s];
-        if (p.rope_lw)
-            anchor_apply<CPL>(y, csr[jb], lane);
-        if (p.rotate)
-            fwht_wave<CPL>(y, lane);
-        float sq[CPL], am = 0.0f;
-#pragma unroll
-        for (int s = 0; s < CPL; s++) {
-            sq_[h][lane * CPL + s] = y[s];
-            sq[s] = y[s] * y[s];
-            am = fmaxf(am, fabsf(y[s]));
-        }
-        // stride-halving tree over the 16 channels of a group: lanes of one group are
-        // 16/CPL consecutive lanes; the xor butterfly reproduces the tree's sums.
-#pragma unroll
-        for (int m = 8 / CPL; m >= 1; m >>= 1) {
+        for (int jb = 0; jb < kRecBuckets; jb++) {
+            if (bk0 + jb >= bk1)
+                continue;
+            float y[CPL];
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                sq[s] = sq[s] + __shfl_xor(sq[s], m);
-            am = fmaxf(am, __shfl_xor(am, m));
-        }
-        float e = sq[0];
-        if constexpr (CPL == 2)
-            e = sq[0] + sq[1];
-        if ((lane % (16 / CPL)) == 0) {
-            se[h][lane / (16 / CPL)] = e;
-            sam[h][lane / (16 / CPL)] = am;
+                y[s] = yq[s];
+            if (p.rope_lw)
+                anchor_apply<CPL>(y, csr[jb], lane);
+            if (p.rotate)
+                fwht_wave<CPL>(y, lane);
+            float sq[CPL], am = 0.0f;
+#pragma unroll
+            for (int s = 0; s < CPL; s++) {
+                sq_[jb][h][lane * CPL + s] = y[s];
+                sq[s] = y[s] * y[s];
+                am = fmaxf(am, fabsf(y[s]));
+            }
+            // stride-halving tree over the 16 channels of a group: lanes of one group are
+            // 16/CPL consecutive lanes; the xor butterfly reproduces the tree's sums.
+#pragma unroll
+            for (int m = 8 / CPL; m >= 1; m >>= 1) {
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    sq[s] = sq[s] + __shfl_xor(sq[s], m);
+                am = fmaxf(am, __shfl_xor(am, m));
+            }
+            float e = sq[0];
+            if constexpr (CPL == 2)
+                e = sq[0] + sq[1];
+            if ((lane % (16 / CPL)) == 0) {
+                se[jb][h][lane / (16 / CPL)] = e;
+                sam[jb][h][lane / (16 / CPL)] = am;
+            }
         }
         __syncthreads();
 
-        // mask (every wave computes the same one): keep the `keep` highest group energies
-        // summed over the heads in ascending head order, ties to the lower group
-        uint32_t mask = (1u << NP) - 1u;
-        if (p.keep > 0 && p.keep < NP) {
-            float E[NP];
 #pragma unroll
-            for (int g = 0; g < NP; g++) {
-                float acc = se[0][g];
+        for (int jb = 0; jb < kRecBuckets; jb++) {
+            if (bk0 + jb >= bk1)
+                continue;
+            // mask (every wave computes the same one): keep the `keep` highest group energies
+            // summed over the heads in ascending head order, ties to the lower group.  Lane
+            // g < NP ranks group g against the others' sums (read from their lanes).
+            uint32_t mask = (1u << NP) - 1u;
+            if (p.keep > 0 && p.keep < NP) {
+                const int g = lane < NP ? lane : NP - 1;
+                float eg = se[jb][0][g];
 #pragma unroll
                 for (int hh = 1; hh < G; hh++)
-                    acc = acc + se[hh][g];
-                E[g] = acc;
-            }
-            mask = 0;
-#pragma unroll
-            for (int g = 0; g < NP; g++) {
+                    eg = eg + se[jb][hh][g];
                 int rank = 0;
 #pragma unroll
-                for (int o = 0; o < NP; o++)
-                    rank += (E[o] > E[g] || (E[o] == E[g] && o < g)) ? 1 : 0;
-                if (rank < p.keep)
-                    mask |= 1u << g;
+                for (int o = 0; o < NP; o++) {
+                    const float eo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg), o));
+                    rank += (eo > eg || (eo == eg && o < g)) ? 1 : 0;
+                }
+                mask = (uint32_t)__ballot(lane < NP && rank < p.keep);
+            }
+            masks[jb] = uniform(mask);
+
+            // this head's scaled, masked fp32 query
+#pragma unroll
+            for (int s = 0; s < CPL; s++) {
+                const int c = lane * CPL + s;
+                const bool kept = (masks[jb] >> (c / 16)) & 1u;
+                su_[jb][h][c] = kept ? sq_[jb][h][c] : 0.0f;
+                sq_[jb][h][c] = kept ? sq_[jb][h][c] * qscale : 0.0f;
             }
         }
-        mask = uniform(mask);
-
-        // this head's scaled, masked fp32 query
-#pragma unroll
-        for (int s = 0; s < CPL; s++) {
-            const int c = lane * CPL + s;
-            const bool kept = (mask >> (c / 16)) & 1u;
-            su_[h][c] = kept ? sq_[h][c] : 0.0f;
-            sq_[h][c] = kept ? sq_[h][c] * qscale : 0.0f;
-        }
         __syncthreads();
-        return mask;
     };
     if (!chunk_only && grp == 0) {
         // the decode kernel's tile and arrival counters of this unit's stripes, at the places
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
     }
 
-    const uint32_t mask0 = prep(0); // bucket bk0's
+    prep_all();
     // ---- the chunk's softmax state for this wave's head (the query of the chunk's bucket):
     // log2 max m, sum l and o = sum_t 2^(l_t - m) v_t over its positions.  Lane j's logit is
     // the dot of its key row with the masked, scaled query (0 on pruned channels); the values
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             float qo[CPL];
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                qo[s] = sq_[h][lane * CPL + s];
+                qo[s] = sq_[0][h][lane * CPL + s];
             float mine = -__builtin_inff();
 #pragma unroll
             for (int j = 0; j < kSinksInRecord; j++) {
@@ -591,8 +594,8 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
                 const uint32_t kk[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    dp[e] = fmaf(sq_[h][8 * c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
-                    dp[e] = fmaf(sq_[h][8 * c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dp[e]);
+                    dp[e] = fmaf(sq_[0][h][8 * c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
+                    dp[e] = fmaf(sq_[0][h][8 * c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dp[e]);
                 }
             }
             const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     for (int jb = 0; jb < kRecBuckets; jb++) {
         const int bk = bk0 + jb;
         if (bk < bk1) {
-            const uint32_t mask = jb == 0 ? mask0 : prep(jb);
+            const uint32_t mask = masks[jb];
             uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
             float *recf = reinterpret_cast<float *>(rec);
             bool sharp = false; // (ssharp is visible after prep's barriers)
@@ -663,14 +666,14 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
 #pragma unroll
                     for (int g = 0; g < NP; g++)
                         if (mask >> g & 1u)
-                            amax = fmaxf(amax, sam[hh][g]);
+                            amax = fmaxf(amax, sam[jb][hh][g]);
                 int ex = 0;
                 (void)frexpf(amax, &ex);
                 const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
                 if (lane < KROWS * PPW) {
                     const int r = lane / PPW, j = lane % PPW;
                     const int ca = 8 * r + 2 * j;
-                    const float a = su_[h][ca] * g2, b2 = su_[h][ca + 1] * g2;
+                    const float a = su_[jb][h][ca] * g2, b2 = su_[jb][h][ca + 1] * g2;
                     const uint32_t hi = pack_f16x2(a, b2);
                     rec[C::OFF_QP + (r * G + h) * QW + j] = hi;
                     rec[C::OFF_QPL + (r * G + h) * QW + j] = sharp ? pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi)) : 0u;
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
                 for (int s2 = 0; s2 < CPL; s2++) {
                     const int c = lane * CPL + s2;
                     if (!(p.ch0 && c == 0))
-                        am = fmaxf(am, fabsf(su_[h][c]));
+                        am = fmaxf(am, fabsf(su_[jb][h][c]));
                 }
                 am = wave_max_dpp(am);
                 int ex = 0;
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
                 // the half of channel c (0 for the protected channel 0) and, for a sharp query, the
                 // half of what it leaves (the residual, exact in fp32); g2 and the place factors are
                 // powers of two
-                auto qval = [&](int c) { return (p.ch0 && c == 0) ? 0.0f : su_[h][c] * (g2 / asym_place<KB>(c)); };
+                auto qval = [&](int c) { return (p.ch0 && c == 0) ? 0.0f : su_[jb][h][c] * (g2 / asym_place<KB>(c)); };
                 auto qhi = [&](int c) -> uint32_t { return f32_to_f16(qval(c)); };
                 auto qlo = [&](int c) -> uint32_t { return sharp ? f32_to_f16(qval(c) - f16_to_f32(qhi(c))) : 0u; };
                 // key word r, spread register k: halves hold channels asym_chan<KB>(r, k, 0 / 1)
@@ -731,13 +734,9 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
                 }
                 if (lane == 0) {
                     recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
-                    recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[h][0] * (g2 * 0x1p-24f) : 0.0f;
+                    recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[jb][h][0] * (g2 * 0x1p-24f) : 0.0f;
                 }
             }
-            // (the next bucket's prep() rewrites the shared query arrays that this bucket's
-            // operands read across heads)
-            if (bk + 1 < bk1)
-                __syncthreads();
         }
     } // buckets
 }
