@@ -237,6 +237,14 @@ __device__ __forceinline__ float asym_place(int c)
     const int j = c % FIELDS;
     return (float)(1u << (KB * (j < DIRECT ? j : j - DIRECT)));
 }
+template <int KB>
+__device__ __forceinline__ float asym_inv_place(int c) // 1 / asym_place(c), exactly
+{
+    constexpr int FIELDS = 16 / KB;
+    constexpr int DIRECT = KB == 2 ? 5 : 2;
+    const int j = c % FIELDS;
+    return __uint_as_float((uint32_t)(127 - KB * (j < DIRECT ? j : j - DIRECT)) << 23);
+}
 // a * b (fp16 pairs, fp32 sum) into a fresh register: the VOP3P form with an inline 0 (the
 // compiler would build it from the two-address form and a v_mov of 0)
 __device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b)
@@ -266,9 +274,8 @@ __device__ __forceinline__ void spread_asym(uint32_t x, uint32_t (&o)[asym_qw<KB
 }
 
 // ===================================================================== query prep
-// Query records of up to kRecBuckets of one unit's buckets per workgroup, prepared side by
-// side (one pair of barriers for all of them), and chunks of up to 64 BF16 positions.
-constexpr int kRecBuckets = 4;
+// One query record (one bucket of one unit) per workgroup, and chunks of up to 64 BF16
+// positions.
 // Sinks beyond this many get a workgroup of their own (else bucket 0's record workgroup
 // scores them).
 constexpr int kSinksInRecord = 8;
@@ -277,14 +284,95 @@ constexpr int kSinksInRecord = 8;
 // has a workgroup of its own, then the record groups (each class unit-minor).
 __host__ __device__ inline int qprep_groups(const DecodeParams &p)
 {
-    return (p.n_bch - 1) + (p.n_sink > kSinksInRecord ? 1 : 0) + (p.n_qb + kRecBuckets - 1) / kRecBuckets;
+    return (p.n_bch - 1) + (p.n_sink > kSinksInRecord ? 1 : 0) + p.n_qb;
 }
 
-// One wave per query head of the GQA group in every workgroup.  Record workgroups: for each
-// of their buckets, the stored-coordinate query (FWHT when keys are rotated), 16-channel group
-// energies (fp32 stride-halving tree, the order the format fixes), the group's mask, and the
-// head's query operands.  BF16 chunks of up to 64 positions each get the softmax state
-// (m, l, o) of their positions per head, which the decode kernel folds into the unit's
+// lane l ^ M's value (M < 32: within each half of the wave; LDS crossbar, no memory access)
+template <int M>
+__device__ __forceinline__ float swz_xor(float v)
+{
+    static_assert(M > 0 && M < 32, "swizzle xor within 32 lanes");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+}
+
+// max / sum over the RW consecutive lanes (RW a power of two) that hold this lane, in every
+// lane of them.  Sixteen lanes: DPP within the row (rotations by 8 and 4, then the quad
+// swaps); the max is the same in every lane, a sum may differ in its last bits between them.
+template <int RW>
+__device__ __forceinline__ float seg_max(float v)
+{
+    if constexpr (RW == 16) {
+        v = dpp_max_step<0x128, 0xF>(v); // row_ror:8
+        v = dpp_max_step<0x124, 0xF>(v); // row_ror:4
+        v = dpp_max_step<0xB1, 0xF>(v);  // quad_perm [1,0,3,2]
+        v = dpp_max_step<0x4E, 0xF>(v);  // quad_perm [2,3,0,1]
+    } else {
+        if constexpr (RW == 64)
+            v = fmaxf(v, __shfl_xor(v, 32));
+        if constexpr (RW >= 32)
+            v = fmaxf(v, swz_xor<16>(v));
+        if constexpr (RW >= 16)
+            v = fmaxf(v, swz_xor<8>(v));
+        v = fmaxf(v, swz_xor<4>(v));
+        v = fmaxf(v, swz_xor<2>(v));
+        v = fmaxf(v, swz_xor<1>(v));
+    }
+    return v;
+}
+
+template <int RW>
+__device__ __forceinline__ float seg_sum(float v)
+{
+    if constexpr (RW == 16) {
+        v = dpp_add_step<0x128, 0xF>(v);
+        v = dpp_add_step<0x124, 0xF>(v);
+        v = dpp_add_step<0xB1, 0xF>(v);
+        v = dpp_add_step<0x4E, 0xF>(v);
+    } else {
+        if constexpr (RW == 64)
+            v = v + __shfl_xor(v, 32);
+        if constexpr (RW >= 32)
+            v = v + swz_xor<16>(v);
+        if constexpr (RW >= 16)
+            v = v + swz_xor<8>(v);
+        v = v + swz_xor<4>(v);
+        v = v + swz_xor<2>(v);
+        v = v + swz_xor<1>(v);
+    }
+    return v;
+}
+
+
+// The group energies' tree: level M adds lane l ^ M's partial sums (and takes the max of the
+// largest |q|), for M = M0, M0/2, .., 1
+template <int M, int CPL>
+__device__ __forceinline__ void energy_tree(float (&sq)[CPL], float &am)
+{
+    if constexpr (M >= 1) {
+#pragma unroll
+        for (int s = 0; s < CPL; s++)
+            sq[s] = sq[s] + swz_xor<M>(sq[s]);
+        am = fmaxf(am, swz_xor<M>(am));
+        energy_tree<M / 2, CPL>(sq, am);
+    }
+}
+
+// sum over the 2M consecutive lanes holding this lane (xor butterfly M, M/2, .., 1)
+template <int M>
+__device__ __forceinline__ float bfly_sum(float v)
+{
+    if constexpr (M >= 1) {
+        v = v + swz_xor<M>(v);
+        v = bfly_sum<M / 2>(v);
+    }
+    return v;
+}
+
+// One wave per query head of the GQA group in every workgroup.  A record workgroup prepares
+// one bucket of one unit: the stored-coordinate query (FWHT when keys are rotated), 16-channel
+// group energies (fp32 stride-halving tree, the order the format fixes), the group's mask,
+// and the head's query operands.  BF16 chunks of up to 64 positions each get the softmax
+// state (m, l, o) of their positions per head, which the decode kernel folds into the unit's
 // result: chunk 0, the sinks (in bucket 0's record workgroup, or in one of its own when there
 // are many), and chunk c >= 1, the recent window's part of one 64-aligned block of positions
 // (the chunks come first in the grid: the longest work).
@@ -294,14 +382,21 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
     constexpr int CPL = C::CPL, QW = C::QW;
-    __shared__ float sq_[kRecBuckets][G][D];
-    __shared__ float su_[kRecBuckets][G][D]; // the masked query before the softmax scale (operand source)
-    __shared__ float se[kRecBuckets][G][NP];
-    __shared__ float sam[kRecBuckets][G][NP];
+    // a chunk's rows per wave (its workgroup's waves split the rows), and the value-row
+    // registers: a wave's share of a chunk, or the few sinks of a record workgroup
+    constexpr int RW = kWave / G;
+    constexpr int NVR = RW > 2 * kSinksInRecord ? RW : 2 * kSinksInRecord;
+    __shared__ float sq_[G][D + 4]; // (+4: the heads' rows start in other LDS banks)
+    __shared__ float su_[G][D];     // the masked query before the softmax scale
+    __shared__ float se[G][NP];
+    __shared__ float sam[G][NP];
+    __shared__ float cpo[G][G][D]; // a chunk's partial states: [row share][head]
+    __shared__ float cpm[G][G], cpl[G][G];
+    __shared__ uint32_t shalf[G][D]; // a head's fp16 query halves per channel (high | residual << 16)
     __shared__ int ssharp[G];
 
     const int lane = threadIdx.x % kWave;
-    const int h = (int)uniform(threadIdx.x / kWave); // this wave's head
+    const int h = (int)uniform(threadIdx.x / kWave); // this wave's head (a chunk's row share)
     const int U = p.n_units;
     const bool sink_wg = p.n_sink > kSinksInRecord;
     const int nwin = U * (p.n_bch - 1), nsk = sink_wg ? U : 0;
@@ -310,7 +405,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     const bool chunk_only = bi < nwin + nsk;        // a chunk's workgroup (window or sinks)
     const int bid = wchunk ? bi : chunk_only ? bi - nwin : bi - nwin - nsk;
     const int unit = bid % U;
-    const int grp = chunk_only ? 0 : bid / U;       // record group: buckets grp * kRecBuckets ..
+    const int grp = chunk_only ? 0 : bid / U;       // a record workgroup's bucket
     const int ch = wchunk ? 1 + bid / U : 0;        // BF16 chunk: 0 the sinks, c >= 1 the window's
     const bool state = chunk_only || (grp == 0 && !sink_wg); // computes chunk ch's softmax state
     const int b = unit / p.n_kv_heads;
@@ -341,9 +436,10 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     // taken from one wrap point.  Window chunks are the window's part of the 64-aligned
     // position blocks, so none crosses a RoPE bucket edge (buckets are multiples of 128
     // positions).  The loads go out right after the query's (which are waited for first), so
-    // their latency overlaps the query work: lane j's whole key row (lane j scores position
-    // pos0 + j over all channels) and this lane's CPL channels of every value row; registers
-    // of rows past nrows hold zeros.
+    // their latency overlaps the query work.  Wave h takes rows h*RW .. h*RW + RW - 1: lane l
+    // loads the whole key row h*RW + l % RW (the lanes of the G heads load the same rows), and
+    // its CPL channels of each of the wave's value rows; registers of rows past nrows hold
+    // zeros.
     const int ns_all = p.n_sink < p.len ? p.n_sink : p.len;
     const int wlo = p.q_end > ns_all ? p.q_end : ns_all; // first window position
     int pos0 = 0, nrows = 0;
@@ -370,9 +466,9 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     // instead: every lane loads its CPL channels of each sink row, key j into vr[j] and value
     // j into vr[kSinksInRecord + j]; each sink's logit is one wave-wide sum.
     const bool few = state && !chunk_only;
-    static_assert(2 * kSinksInRecord <= kWave, "the few-rows path keeps its rows in vr");
-    uint4 kr[D / 8];   // key row of position pos0 + lane (bf16; lanes past nrows: zeros)
-    uint32_t vr[kWave]; // value rows: this lane's CPL bf16 channels of row j (CPL = 1: low half)
+    uint4 kr[D / 8];  // key row h*RW + lane % RW (bf16; rows past nrows: zeros)
+    uint32_t vr[NVR]; // value rows: this lane's CPL bf16 channels of row j (CPL = 1: low half)
+    const int jrow = h * RW + lane % RW; // the row this lane scores
     if (few) {
 #pragma unroll
         for (int j = 0; j < kSinksInRecord; j++) {
@@ -386,32 +482,27 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             }
         }
     } else if (nrows > 0) {
-        const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + row_off(lane));
+        const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + row_off(jrow));
 #pragma unroll
         for (int c = 0; c < D / 8; c++)
-            kr[c] = lane < nrows ? krow[c] : make_uint4(0u, 0u, 0u, 0u);
+            kr[c] = jrow < nrows ? krow[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int j = 0; j < kWave; j++) {
-            if (j < nrows) {
-                const uint16_t *vrow = vbase + row_off(j) + (size_t)lane * CPL;
-                vr[j] = CPL == 2 ? *reinterpret_cast<const uint32_t *>(vrow) : (uint32_t)vrow[0];
+        for (int jr = 0; jr < RW; jr++) {
+            if (h * RW + jr < nrows) {
+                const uint16_t *vrow = vbase + row_off(h * RW + jr) + (size_t)lane * CPL;
+                vr[jr] = CPL == 2 ? *reinterpret_cast<const uint32_t *>(vrow) : (uint32_t)vrow[0];
             } else {
-                vr[j] = 0u;
+                vr[jr] = 0u;
             }
         }
     }
 
-    // the buckets this workgroup prepares: a chunk's own (the sinks': 0), or the record
-    // group's; the (cos, sin) of their anchors for this lane's channels (bucket-relative RoPE)
-    const int bk0 = chunk_only ? (wchunk && p.rope_lw ? pos0 >> p.rope_lw : 0) : grp * kRecBuckets;
-    const int bk1 = chunk_only ? bk0 + 1 : min(p.n_qb, bk0 + kRecBuckets);
-    float2 csr[kRecBuckets][CPL];
-    if (p.rope_lw) {
-#pragma unroll
-        for (int j = 0; j < kRecBuckets; j++)
-            if (bk0 + j < bk1)
-                anchor_cs<CPL>(csr[j], p.rope_cs + (size_t)(bk0 + j) * D, lane);
-    }
+    // the bucket this workgroup prepares (a chunk's own; the sinks': 0) and, under
+    // bucket-relative RoPE, the (cos, sin) of its anchor for this lane's channels
+    const int bk = chunk_only ? (wchunk && p.rope_lw ? pos0 >> p.rope_lw : 0) : grp;
+    float2 csr[CPL];
+    if (p.rope_lw)
+        anchor_cs<CPL>(csr, p.rope_cs + (size_t)bk * D, lane);
 
     float yq[CPL];
 #pragma unroll
@@ -419,117 +510,62 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
         yq[s] = p.q_bf16 ? bf16_to_f32(s == 0 ? qw[0] & 0xFFFFu : qw[0] >> 16) : __uint_as_float(qw[s]);
     const float qscale = p.sm_log2e / (p.rotate ? (float)D : 1.0f);
 
-    // Sharp query (Dual-QK sec. 1 and 3.2: query energy concentrated in a few channels): the
-    // head's largest |q_c| above 8 times its fifth largest, in the coordinates the query is
-    // given in (channel 0 left out when it is scored from its BF16 copy).  A unit with a
-    // sharp head gets a second, residual fp16 half per channel (about 22 bits per channel in
-    // all); one half keeps 11 bits relative to each channel, which the logits of a few very
-    // large channels outgrow.
+    // Sharp query (Dual-QK sec. 1 and 3.2: query energy concentrated in a few channels): fewer
+    // than five channels of the head with |q_c| at or above an eighth of its largest, in the
+    // coordinates the query is given in (channel 0 left out when it is scored from its BF16
+    // copy).  A unit with a sharp head gets a second, residual fp16 half per channel (about 22
+    // bits per channel in all); one half keeps 11 bits relative to each channel, which the
+    // logits of a few very large channels outgrow.
     if (!chunk_only) {
-        float v[CPL];
+        float v[CPL], lm = 0.0f;
+#pragma unroll
+        for (int s = 0; s < CPL; s++) {
+            v[s] = (p.ch0 && lane * CPL + s == 0) ? 0.0f : fabsf(yq[s]);
+            lm = fmaxf(lm, v[s]);
+        }
+        const float m1 = wave_max_dpp(lm);
+        const float t = m1 * 0.125f;
+        int big = 0;
 #pragma unroll
         for (int s = 0; s < CPL; s++)
-            v[s] = (p.ch0 && lane * CPL + s == 0) ? 0.0f : fabsf(yq[s]);
-        float m1 = 0.0f, m5 = 0.0f;
-#pragma unroll
-        for (int it = 0; it < 5; it++) {
-            float lm = v[0];
-#pragma unroll
-            for (int s = 1; s < CPL; s++)
-                lm = fmaxf(lm, v[s]);
-            const float wm = wave_max_dpp(lm);
-            if (it == 0)
-                m1 = wm;
-            m5 = wm;
-#pragma unroll
-            for (int s = 0; s < CPL; s++)
-                v[s] = v[s] == wm ? -1.0f : v[s]; // (ties leave together: m5 only gets smaller)
-        }
+            big += __popcll(__ballot(v[s] >= t));
         if (lane == 0)
-            ssharp[h] = m1 > 8.0f * fmaxf(m5, 0.0f) ? 1 : 0;
+            ssharp[h] = m1 > 0.0f && big < 5 ? 1 : 0;
     }
 
-    // The queries of buckets bk0 .. bk1 - 1 in stored coordinates (rotated back by the bucket's
-    // anchor under bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys
-    // are rotated), their group energies, masks (masks[jb]), and this head's scaled, masked
-    // query per bucket in sq_[jb][h] (before the scale, in su_[jb][h]).  The buckets go through
-    // each step side by side, so their latencies overlap and one pair of barriers serves all.
-    // Every wave of the workgroup calls it.
-    uint32_t masks[kRecBuckets];
-    auto prep_all = [&]() {
+    // The query of the bucket in stored coordinates (rotated back by the bucket's anchor
+    // under bucket-relative RoPE, Dual-QK sec. 3.4 / C.4; then Walsh-Hadamard when keys are
+    // rotated), its group energies (se) and largest |q| per group (sam; channel 0 left out
+    // when it is scored from its BF16 copy), the mask, and this head's masked query (ym,
+    // su_[h]) and scaled, masked query (sq_[h]).
+    float ym[CPL];
+    {
+        float y[CPL];
 #pragma unroll
-        for (int jb = 0; jb < kRecBuckets; jb++) {
-            if (bk0 + jb >= bk1)
-                continue;
-            float y[CPL];
+        for (int s = 0; s < CPL; s++)
+            y[s] = yq[s];
+        if (p.rope_lw)
+            anchor_apply<CPL>(y, csr, lane);
+        if (p.rotate)
+            fwht_wave<CPL>(y, lane);
+        float sq[CPL], am = 0.0f;
 #pragma unroll
-            for (int s = 0; s < CPL; s++)
-                y[s] = yq[s];
-            if (p.rope_lw)
-                anchor_apply<CPL>(y, csr[jb], lane);
-            if (p.rotate)
-                fwht_wave<CPL>(y, lane);
-            float sq[CPL], am = 0.0f;
-#pragma unroll
-            for (int s = 0; s < CPL; s++) {
-                sq_[jb][h][lane * CPL + s] = y[s];
-                sq[s] = y[s] * y[s];
-                am = fmaxf(am, fabsf(y[s]));
-            }
-            // stride-halving tree over the 16 channels of a group: lanes of one group are
-            // 16/CPL consecutive lanes; the xor butterfly reproduces the tree's sums.
-#pragma unroll
-            for (int m = 8 / CPL; m >= 1; m >>= 1) {
-#pragma unroll
-                for (int s = 0; s < CPL; s++)
-                    sq[s] = sq[s] + __shfl_xor(sq[s], m);
-                am = fmaxf(am, __shfl_xor(am, m));
-            }
-            float e = sq[0];
-            if constexpr (CPL == 2)
-                e = sq[0] + sq[1];
-            if ((lane % (16 / CPL)) == 0) {
-                se[jb][h][lane / (16 / CPL)] = e;
-                sam[jb][h][lane / (16 / CPL)] = am;
-            }
+        for (int s = 0; s < CPL; s++) {
+            ym[s] = y[s];
+            sq[s] = y[s] * y[s];
+            am = fmaxf(am, (p.ch0 && lane * CPL + s == 0) ? 0.0f : fabsf(y[s]));
         }
-        __syncthreads();
-
-#pragma unroll
-        for (int jb = 0; jb < kRecBuckets; jb++) {
-            if (bk0 + jb >= bk1)
-                continue;
-            // mask (every wave computes the same one): keep the `keep` highest group energies
-            // summed over the heads in ascending head order, ties to the lower group.  Lane
-            // g < NP ranks group g against the others' sums (read from their lanes).
-            uint32_t mask = (1u << NP) - 1u;
-            if (p.keep > 0 && p.keep < NP) {
-                const int g = lane < NP ? lane : NP - 1;
-                float eg = se[jb][0][g];
-#pragma unroll
-                for (int hh = 1; hh < G; hh++)
-                    eg = eg + se[jb][hh][g];
-                int rank = 0;
-#pragma unroll
-                for (int o = 0; o < NP; o++) {
-                    const float eo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg), o));
-                    rank += (eo > eg || (eo == eg && o < g)) ? 1 : 0;
-                }
-                mask = (uint32_t)__ballot(lane < NP && rank < p.keep);
-            }
-            masks[jb] = uniform(mask);
-
-            // this head's scaled, masked fp32 query
-#pragma unroll
-            for (int s = 0; s < CPL; s++) {
-                const int c = lane * CPL + s;
-                const bool kept = (masks[jb] >> (c / 16)) & 1u;
-                su_[jb][h][c] = kept ? sq_[jb][h][c] : 0.0f;
-                sq_[jb][h][c] = kept ? sq_[jb][h][c] * qscale : 0.0f;
-            }
+        // stride-halving tree over the 16 channels of a group: lanes of one group are
+        // 16/CPL consecutive lanes; the xor butterfly reproduces the tree's sums.
+        energy_tree<8 / CPL, CPL>(sq, am);
+        float e = sq[0];
+        if constexpr (CPL == 2)
+            e = sq[0] + sq[1];
+        if ((lane % (16 / CPL)) == 0) {
+            se[h][lane / (16 / CPL)] = e;
+            sam[h][lane / (16 / CPL)] = am;
         }
-        __syncthreads();
-    };
+    }
     if (!chunk_only && grp == 0) {
         // the decode kernel's tile and arrival counters of this unit's stripes, at the places
         // u + k * units
@@ -541,14 +577,41 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
         if (threadIdx.x == 0)
             p.tile_ctr[2 * p.n_waves + unit] = 0u; // the decode kernel's count of this unit's members done
     }
+    __syncthreads();
 
-    prep_all();
-    // ---- the chunk's softmax state for this wave's head (the query of the chunk's bucket):
-    // log2 max m, sum l and o = sum_t 2^(l_t - m) v_t over its positions.  Lane j's logit is
-    // the dot of its key row with the masked, scaled query (0 on pruned channels); the values
-    // then go through with the weights, lane owning channels lane*CPL..  An empty chunk (no
-    // sinks) writes the empty state.  (Before the records: the chunk's rows then leave the
-    // registers first.)
+    // mask (every wave computes the same one): keep the `keep` highest group energies summed
+    // over the heads in ascending head order, ties to the lower group.  Lane g < NP ranks
+    // group g against the others' sums (read from their lanes).
+    uint32_t mask = (1u << NP) - 1u;
+    if (p.keep > 0 && p.keep < NP) {
+        const int g = lane < NP ? lane : NP - 1;
+        float eg = se[0][g];
+#pragma unroll
+        for (int hh = 1; hh < G; hh++)
+            eg = eg + se[hh][g];
+        int rank = 0;
+#pragma unroll
+        for (int o = 0; o < NP; o++) {
+            const float eo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg), o));
+            rank += (eo > eg || (eo == eg && o < g)) ? 1 : 0;
+        }
+        mask = (uint32_t)__ballot(lane < NP && rank < p.keep);
+    }
+    mask = uniform(mask);
+#pragma unroll
+    for (int s = 0; s < CPL; s++) {
+        const int c = lane * CPL + s;
+        const bool kept = (mask >> (c / 16)) & 1u;
+        ym[s] = kept ? ym[s] : 0.0f;
+        su_[h][c] = ym[s];
+        sq_[h][c] = ym[s] * qscale;
+    }
+    __syncthreads();
+
+    // ---- the chunk's softmax state per head (the query of the chunk's bucket): log2 max m,
+    // sum l and o = sum_t 2^(l_t - m) v_t over its positions, written by wave h for head h.
+    // An empty chunk (no sinks) writes the empty state.  (Before the record: the chunk's rows
+    // then leave the registers first.)
     if (state) {
         float M = -__builtin_inff(), L = 0.0f;
         float o[CPL];
@@ -560,7 +623,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             float qo[CPL];
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                qo[s] = sq_[0][h][lane * CPL + s];
+                qo[s] = sq_[h][lane * CPL + s];
             float mine = -__builtin_inff();
 #pragma unroll
             for (int j = 0; j < kSinksInRecord; j++) {
@@ -586,41 +649,69 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
                 }
             }
         } else if (nrows > 0) {
-            // four partial sums (sum e takes channels 8i + 2e and 8i + 2e + 1): short dependency
-            // chains for a kernel that runs one or two waves per SIMD
+            // Wave h's share of the rows for every head: lane l scores row jrow against head
+            // l / RW's masked, scaled query (four partial sums, sum e taking channels 8i + 2e and
+            // 8i + 2e + 1: short dependency chains), the share's max and sum per head over its
+            // RW lanes, then every lane sums its CPL channels of the share's value rows for every
+            // head.  The shares' states meet in LDS; wave h merges head h's.
+            const int hl = lane / RW; // the head this lane scores for
             float dp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int c = 0; c < D / 8; c++) {
                 const uint32_t kk[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    dp[e] = fmaf(sq_[0][h][8 * c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
-                    dp[e] = fmaf(sq_[0][h][8 * c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dp[e]);
+                    dp[e] = fmaf(sq_[hl][8 * c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
+                    dp[e] = fmaf(sq_[hl][8 * c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dp[e]);
                 }
             }
             const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
-            const bool valid = lane < nrows;
+            const bool valid = jrow < nrows;
             const float lw = valid ? dot : -__builtin_inff();
-            M = wave_max_dpp(lw); // finite: the chunk has a position
-            const float pw = valid ? __builtin_amdgcn_exp2f(lw - M) : 0.0f;
-            L = wave_sum_dpp(pw);
-            // values: even and odd rows in two sums per channel (shorter chains)
-            float oe[2][CPL];
+            const float mw = seg_max<RW>(lw); // -inf for a share without rows
+            const float pw = valid ? __builtin_amdgcn_exp2f(lw - mw) : 0.0f;
+            const float lsum = seg_sum<RW>(pw);
+            float ow[G][CPL];
 #pragma unroll
-            for (int s = 0; s < CPL; s++)
-                oe[0][s] = oe[1][s] = 0.0f;
+            for (int g = 0; g < G; g++)
 #pragma unroll
-            for (int j = 0; j < kWave; j++) {
-                if (j < nrows) { // (a uniform test: the loop stays unrolled, vr in registers)
-                    const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), j));
-                    oe[j & 1][0] = fmaf(pj, bf16_to_f32(vr[j] & 0xFFFFu), oe[j & 1][0]);
-                    if constexpr (CPL == 2)
-                        oe[j & 1][1] = fmaf(pj, bf16_to_f32(vr[j] >> 16), oe[j & 1][1]);
+                for (int s = 0; s < CPL; s++)
+                    ow[g][s] = 0.0f;
+#pragma unroll
+            for (int jr = 0; jr < RW; jr++) {
+                if (h * RW + jr < nrows) { // (a uniform test: the loop stays unrolled, vr in registers)
+#pragma unroll
+                    for (int g = 0; g < G; g++) {
+                        const float pj =
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), g * RW + jr));
+                        ow[g][0] = fmaf(pj, bf16_to_f32(vr[jr] & 0xFFFFu), ow[g][0]);
+                        if constexpr (CPL == 2)
+                            ow[g][1] = fmaf(pj, bf16_to_f32(vr[jr] >> 16), ow[g][1]);
+                    }
                 }
             }
 #pragma unroll
-            for (int s = 0; s < CPL; s++)
-                o[s] = oe[0][s] + oe[1][s];
+            for (int g = 0; g < G; g++)
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    cpo[h][g][lane * CPL + s] = ow[g][s];
+            if (lane % RW == 0) {
+                cpm[h][hl] = mw;
+                cpl[h][hl] = lsum;
+            }
+            __syncthreads();
+            // head h over the G shares (share 0 holds row 0: M is finite)
+#pragma unroll
+            for (int w = 0; w < G; w++)
+                M = fmaxf(M, cpm[w][h]);
+#pragma unroll
+            for (int w = 0; w < G; w++) {
+                const float f = __builtin_amdgcn_exp2f(cpm[w][h] - M); // (0 for a share without rows)
+                L = fmaf(cpl[w][h], f, L);
+#pragma unroll
+                for (int s = 0; s < CPL; s++)
+                    o[s] = fmaf(cpo[w][h][lane * CPL + s], f, o[s]);
+            }
         }
         // the chunk's state, in the partial-state layout (m, l, two unused words, o[D])
         float *st = p.bstate + ((size_t)(unit * p.bch_max + ch) * G + h) * part_rec<D>();
@@ -636,109 +727,96 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     if (chunk_only)
         return; // (a chunk's workgroup writes no record)
 
-    // (unrolled over the group's buckets: the anchors' (cos, sin) stay in registers)
+    // ---- the record of bucket bk
+    bool sharp = false; // (ssharp is visible after the barriers)
 #pragma unroll
-    for (int jb = 0; jb < kRecBuckets; jb++) {
-        const int bk = bk0 + jb;
-        if (bk < bk1) {
-            const uint32_t mask = masks[jb];
-            uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
-            float *recf = reinterpret_cast<float *>(rec);
-            bool sharp = false; // (ssharp is visible after prep's barriers)
+    for (int hh = 0; hh < G; hh++)
+        sharp = sharp || ssharp[hh] != 0;
+    uint32_t *rec = p.qprep + ((size_t)unit * p.n_rb + bk) * C::QREC;
+    float *recf = reinterpret_cast<float *>(rec);
+    if (threadIdx.x == 0) {
+        rec[C::OFF_MASK] = mask;
+        rec[C::OFF_SHARP] = sharp ? 1u : 0u;
+        if (p.mask_out)
+            p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
+    }
+    if constexpr (KF == KVQ_K_LLOYD4) {
+        // fp16 pairs of the query before the softmax scale (which goes into the fp32
+        // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
+        // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
+        float amax = 0.0f;
 #pragma unroll
-            for (int hh = 0; hh < G; hh++)
-                sharp = sharp || ssharp[hh] != 0;
-            if (threadIdx.x == 0) {
-                rec[C::OFF_MASK] = mask;
-                rec[C::OFF_SHARP] = sharp ? 1u : 0u;
-                if (p.mask_out)
-                    p.mask_out[(size_t)unit * p.n_rb + bk] = (uint8_t)mask;
-            }
-
-            // ---- the query operands of this record
-            if constexpr (KF == KVQ_K_LLOYD4) {
-                // fp16 pairs of the query before the softmax scale (which goes into the fp32
-                // accumulator unit), scaled so the largest kept |q| of the group lands in [2^12, 2^13);
-                // byte j of key word r holds channels (8r + 2j, 8r + 2j + 1)
-                float amax = 0.0f;
+        for (int hh = 0; hh < G; hh++)
 #pragma unroll
-                for (int hh = 0; hh < G; hh++)
-#pragma unroll
-                    for (int g = 0; g < NP; g++)
-                        if (mask >> g & 1u)
-                            amax = fmaxf(amax, sam[jb][hh][g]);
-                int ex = 0;
-                (void)frexpf(amax, &ex);
-                const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
-                if (lane < KROWS * PPW) {
-                    const int r = lane / PPW, j = lane % PPW;
-                    const int ca = 8 * r + 2 * j;
-                    const float a = su_[jb][h][ca] * g2, b2 = su_[jb][h][ca + 1] * g2;
-                    const uint32_t hi = pack_f16x2(a, b2);
-                    rec[C::OFF_QP + (r * G + h) * QW + j] = hi;
-                    rec[C::OFF_QPL + (r * G + h) * QW + j] = sharp ? pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi)) : 0u;
-                }
-                if (lane == 0) {
-                    recf[C::OFF_QSC + h] = qscale / g2;
-                    recf[C::OFF_Q0 + h] = 0.0f;
-                }
-            } else {
-                // fp16 query halves.  The decode kernel spreads a key word into registers whose two
-                // halves hold the codes of channels (c, c + 32/KB/2) as subnormal integers
-                // P(c) * code * 2^-24 (place factor P, see spread_asym), and multiplies them with
-                // v_dot2_f32_f16 against halves q_c * g2 / P(c).  Every product is then
-                // q~_c * g2 * code_c * 2^-24 with q~ the query rounded to fp16: each channel keeps
-                // 11 bits relative to its own magnitude, so one sharp query channel costs the others
-                // nothing.  The halves hold the query before the softmax scale (which goes into the
-                // fp32 accumulator unit), and g2 (a power of two) puts the head's largest kept |q| in
-                // [2^12, 2^13): a bf16 query is then carried exactly.  Channel 0 (when protected) is
-                // scored from its BF16 copy: its half is 0.
-                float am = 0.0f;
-#pragma unroll
-                for (int s2 = 0; s2 < CPL; s2++) {
-                    const int c = lane * CPL + s2;
-                    if (!(p.ch0 && c == 0))
-                        am = fmaxf(am, fabsf(su_[jb][h][c]));
-                }
-                am = wave_max_dpp(am);
-                int ex = 0;
-                (void)frexpf(am, &ex);
-                const float g2 = am > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
-                // the half of channel c (0 for the protected channel 0) and, for a sharp query, the
-                // half of what it leaves (the residual, exact in fp32); g2 and the place factors are
-                // powers of two
-                auto qval = [&](int c) { return (p.ch0 && c == 0) ? 0.0f : su_[jb][h][c] * (g2 / asym_place<KB>(c)); };
-                auto qhi = [&](int c) -> uint32_t { return f32_to_f16(qval(c)); };
-                auto qlo = [&](int c) -> uint32_t { return sharp ? f32_to_f16(qval(c) - f16_to_f32(qhi(c))) : 0u; };
-                // key word r, spread register k: halves hold channels asym_chan<KB>(r, k, 0 / 1)
-                if (lane < KROWS * QW) {
-                    const int r = lane / QW, k = lane % QW;
-                    const int c0 = asym_chan<KB>(r, k, 0), c1 = asym_chan<KB>(r, k, 1);
-                    rec[C::OFF_QP + (r * G + h) * QW + k] = qhi(c0) | (qhi(c1) << 16);
-                    rec[C::OFF_QPL + (r * G + h) * QW + k] = qlo(c0) | (qlo(c1) << 16);
-                }
-                // zero-term sums: the query as the halves carry it, in accumulator units g2 * 2^-24,
-                // summed over each 32-channel group (lanes of a group: 32/CPL consecutive lanes)
-                {
-                    float si = 0.0f;
-#pragma unroll
-                    for (int s2 = 0; s2 < CPL; s2++) {
-                        const int c = lane * CPL + s2;
-                        si += (f16_to_f32(qhi(c)) + f16_to_f32(qlo(c))) * (asym_place<KB>(c) * 0x1p-24f);
-                    }
-#pragma unroll
-                    for (int m = 16 / CPL; m >= 1; m >>= 1)
-                        si += __shfl_xor(si, m);
-                    if (lane % (32 / CPL) == 0)
-                        recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si;
-                }
-                if (lane == 0) {
-                    recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
-                    recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? su_[jb][h][0] * (g2 * 0x1p-24f) : 0.0f;
-                }
-            }
+            for (int g = 0; g < NP; g++)
+                amax = fmaxf(amax, (mask >> g & 1u) ? sam[hh][g] : 0.0f);
+        int ex = 0;
+        (void)frexpf(amax, &ex);
+        const float g2 = amax > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
+        if (lane < KROWS * PPW) {
+            const int r = lane / PPW, j = lane % PPW;
+            const int ca = 8 * r + 2 * j;
+            const float a = su_[h][ca] * g2, b2 = su_[h][ca + 1] * g2;
+            const uint32_t hi = pack_f16x2(a, b2);
+            rec[C::OFF_QP + (r * G + h) * QW + j] = hi;
+            rec[C::OFF_QPL + (r * G + h) * QW + j] = sharp ? pack_f16x2(a - lo_f16(hi), b2 - hi_f16(hi)) : 0u;
         }
-    } // buckets
+        if (lane == 0) {
+            recf[C::OFF_QSC + h] = qscale / g2;
+            recf[C::OFF_Q0 + h] = 0.0f;
+        }
+    } else {
+        // fp16 query halves.  The decode kernel spreads a key word into registers whose two
+        // halves hold the codes of channels (c, c + 32/KB/2) as subnormal integers
+        // P(c) * code * 2^-24 (place factor P, see spread_asym), and multiplies them with
+        // v_dot2_f32_f16 against halves q_c * g2 / P(c).  Every product is then
+        // q~_c * g2 * code_c * 2^-24 with q~ the query rounded to fp16: each channel keeps 11
+        // bits relative to its own magnitude, so one sharp query channel costs the others
+        // nothing.  The halves hold the query before the softmax scale (which goes into the
+        // fp32 accumulator unit), and g2 (a power of two) puts the head's largest kept |q| (the
+        // largest of the kept groups' maxima) in [2^12, 2^13): a bf16 query is then carried
+        // exactly.  Channel 0 (when protected) is scored from its BF16 copy: its half is 0.
+        float am = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NP; g++)
+            am = fmaxf(am, (mask >> g & 1u) ? sam[h][g] : 0.0f);
+        int ex = 0;
+        (void)frexpf(am, &ex);
+        const float g2 = am > 0.0f ? ldexpf(1.0f, 13 - ex) : 1.0f;
+        // this lane's channels: the half of channel c (0 for the protected channel 0) and, for
+        // a sharp query, the half of what it leaves (the residual, exact in fp32; g2 and the
+        // place factors are powers of two); the zero-term sum of the query as the halves carry
+        // it, in accumulator units g2 * 2^-24, over each 32-channel group (lanes of a group:
+        // 32/CPL consecutive lanes)
+        float si = 0.0f;
+#pragma unroll
+        for (int s = 0; s < CPL; s++) {
+            const int c = lane * CPL + s;
+            const float x = (p.ch0 && c == 0) ? 0.0f : ym[s] * (g2 * asym_inv_place<KB>(c));
+            const uint32_t hv = f32_to_f16(x);
+            const uint32_t lv = sharp ? f32_to_f16(x - f16_to_f32(hv)) : 0u;
+            si += (f16_to_f32(hv) + f16_to_f32(lv)) * (asym_place<KB>(c) * 0x1p-24f);
+            shalf[h][c] = hv | (lv << 16);
+        }
+        // (the halves go to the lanes of the key words that hold their channels: within the wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // key word r, spread register k: halves hold channels asym_chan<KB>(r, k, 0 / 1)
+        if (lane < KROWS * QW) {
+            const int r = lane / QW, k = lane % QW;
+            const uint32_t a0 = shalf[h][asym_chan<KB>(r, k, 0)], a1 = shalf[h][asym_chan<KB>(r, k, 1)];
+            rec[C::OFF_QP + (r * G + h) * QW + k] = (a0 & 0xFFFFu) | (a1 << 16);
+            rec[C::OFF_QPL + (r * G + h) * QW + k] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+        }
+        si = bfly_sum<16 / CPL>(si);
+        if (lane % (32 / CPL) == 0)
+            recf[C::OFF_QZ + h * NG + lane / (32 / CPL)] = si;
+        if (lane == 0) {
+            recf[C::OFF_QSC + h] = qscale * (0x1p24f / g2);
+            recf[C::OFF_Q0 + h] = (p.ch0 && (mask & 1u)) ? ym[0] * (g2 * 0x1p-24f) : 0.0f;
+        }
+    }
 }
 
 // ===================================================================== decode
