@@ -262,6 +262,11 @@ def test_token_int2_values_teams_and_heavy_tails(oracle_mod):
     (128, 2, 1, 0, 4, 3, 0, 700, 256, 1, [200, 500]),
     (64, 0, 0, 1, 8, 2, 3, 333, 64, 0, [100, 233]),
     (64, 2, 0, 0, 2, 0, 0, 130, 130, 1, [60, 70]),
+    # more than 8 sinks (a chunk workgroup of their own) with a window, under G = 8, 1 and 4:
+    # the chunk's rows split over 8, 1 and 4 waves
+    (128, 0, 0, 1, 8, 3, 16, 500, 96, 0, [250, 250]),
+    (128, 1, 0, 0, 1, 0, 12, 300, 70, 1, [150, 150]),
+    (64, 0, 0, 0, 4, 2, 9, 200, 33, 0, None),
 ])
 def test_recent_window(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, nr, vfmt, chunks):
     _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, keep=keep, ns=ns, T=T, nr=nr, vfmt=vfmt,
@@ -286,6 +291,7 @@ def test_recent_window_single_token_steps(oracle_mod):
     (128, 2, 0, 0, 2, 0, 0, 300, 100, 0, 128, [150, 150]),
     (64, 0, 0, 1, 1, 3, 3, 640, 200, 0, 128, [300, 340]),
     (64, 2, 1, 0, 8, 2, 0, 333, 0, 1, 1024, None),
+    (128, 0, 0, 1, 8, 4, 12, 900, 150, 1, 256, [450, 450]),
 ])
 def test_rope_buckets(oracle_mod, d, kfmt, rot, ch0, G, keep, ns, T, nr, vfmt, rope, chunks):
     _run(oracle_mod, d=d, kfmt=kfmt, rot=rot, ch0=ch0, G=G, keep=keep, ns=ns, T=T, nr=nr, vfmt=vfmt, rope=rope,
