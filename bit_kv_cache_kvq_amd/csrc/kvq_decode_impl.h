@@ -1097,22 +1097,51 @@ __device__ __forceinline__ void load_batch(CombineBatch<D, G> &b, rsrc_t r, uint
                                              : 0.0f;
 }
 
-// Fold `count` partial states (slots first, first + step, ... in units of records, of an
-// array of `slots` records at `base`) into the state (M, L, O).
+// A batch of the states of two arrays taken as one sequence: records 0 .. n1 - 1 are those
+// of r1 (ub1, ub1 + st1, ... bytes), the next ones those of r2 (ub2, ub2 + st2, ...); `total`
+// states in all.  (The m / l lanes load from both arrays and keep the one that applies.)
 template <int D, int G>
-__device__ __forceinline__ void fold_states(const float *base, int slots, int first, int step, int count, int lane,
-                                            float (&M)[G], float (&L)[G], float (&O)[G][D / 64])
+__device__ __forceinline__ void load_batch_two(CombineBatch<D, G> &b, rsrc_t r1, uint32_t ub1, uint32_t st1, int n1,
+                                               rsrc_t r2, uint32_t ub2, uint32_t st2, int k0, int total, int lane)
 {
     using CB = CombineBatch<D, G>;
     constexpr int CPL = CB::CPL, NB = CB::NB, PR = part_rec<D>();
-    const uint32_t stride = (uint32_t)step * G * PR * 4u; // bytes between the states
-    const rsrc_t r = make_rsrc(base, (uint32_t)slots * G * PR * 4u);
-    const uint32_t ub = (uint32_t)first * G * PR * 4u;    // first state, head 0
+    const int jm = lane % NB, hm = lane / NB;
+    const int idx = k0 + jm;
+    const bool mine = hm < G && idx < total, in1 = idx < n1;
+    const uint32_t hb = (uint32_t)(mine ? hm : 0) * PR * 4u;
+    const uint32_t p1 = ub1 + (uint32_t)(in1 ? idx : 0) * st1 + hb;
+    const uint32_t p2 = ub2 + (uint32_t)(in1 ? 0 : idx - n1) * st2 + hb;
+    const float m1 = load_shared(r1, p1), l1 = load_shared(r1, p1 + 4u);
+    const float m2 = load_shared(r2, p2), l2 = load_shared(r2, p2 + 4u);
+    b.m = mine ? (in1 ? m1 : m2) : -__builtin_inff();
+    b.l = mine ? (in1 ? l1 : l2) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        const int k = k0 + j; // (uniform)
+        const bool f = k < n1;
+        const rsrc_t r = f ? r1 : r2;
+        const uint32_t rec = f ? ub1 + (uint32_t)k * st1 : ub2 + (uint32_t)(k - n1) * st2;
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int s = 0; s < CPL; s++)
+                b.o[h][j][s] = k < total ? load_shared(r, rec + ((uint32_t)h * PR + 4u + lane + 64u * s) * 4u) : 0.0f;
+    }
+}
+
+// Fold `count` states into the state (M, L, O), in order; load(batch, k0) loads the batch of
+// states k0 .. k0 + NB - 1 (double-buffered: the next batch is in flight during a fold).
+template <int D, int G, typename Load>
+__device__ __forceinline__ void fold_run(Load &&load, int count, float (&M)[G], float (&L)[G], float (&O)[G][D / 64])
+{
+    using CB = CombineBatch<D, G>;
+    constexpr int CPL = CB::CPL, NB = CB::NB;
     CB cur, nxt;
-    load_batch<D, G>(cur, r, ub, stride, 0, count, lane);
+    load(cur, 0);
     for (int k0 = 0; k0 < count; k0 += NB) {
         if (k0 + NB < count)
-            load_batch<D, G>(nxt, r, ub, stride, k0 + NB, count, lane);
+            load(nxt, k0 + NB);
 #pragma unroll
         for (int h = 0; h < G; h++) {
 #pragma unroll
@@ -1135,13 +1164,28 @@ __device__ __forceinline__ void fold_states(const float *base, int slots, int fi
     }
 }
 
-// The unit's team, last step: fold unit u's BF16 chunk states and `count` states (stripe or
-// member states) and write the normalised output out_u[h][D].
+// Fold `count` partial states (slots first, first + step, ... in units of records, of an
+// array of `slots` records at `base`) into the state (M, L, O).
+template <int D, int G>
+__device__ __forceinline__ void fold_states(const float *base, int slots, int first, int step, int count, int lane,
+                                            float (&M)[G], float (&L)[G], float (&O)[G][D / 64])
+{
+    constexpr int PR = part_rec<D>();
+    const uint32_t stride = (uint32_t)step * G * PR * 4u; // bytes between the states
+    const rsrc_t r = make_rsrc(base, (uint32_t)slots * G * PR * 4u);
+    const uint32_t ub = (uint32_t)first * G * PR * 4u;    // first state, head 0
+    fold_run<D, G>([&](CombineBatch<D, G> &b, int k0) { load_batch<D, G>(b, r, ub, stride, k0, count, lane); },
+                   count, M, L, O);
+}
+
+// The unit's team, last step: fold unit u's BF16 chunk states, then `count` states (stripe or
+// member states), and write the normalised output out_u[h][D].  The two runs are folded as
+// one sequence, so the chunk states and the first member states arrive in one batch.
 template <int D, int G>
 __device__ __forceinline__ void combine_unit(const DecodeParams &p, int u, int first, int step, int count, int lane,
                                              float *out_u)
 {
-    constexpr int CPL = D / 64;
+    constexpr int CPL = D / 64, PR = part_rec<D>();
     float M[G], L[G], O[G][CPL];
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -1151,8 +1195,14 @@ __device__ __forceinline__ void combine_unit(const DecodeParams &p, int u, int f
         for (int s = 0; s < CPL; s++)
             O[h][s] = 0.0f;
     }
-    fold_states<D, G>(p.bstate, p.n_units * p.bch_max, u * p.bch_max, 1, p.n_bch, lane, M, L, O);
-    fold_states<D, G>(p.part, p.n_waves, first, step, count, lane, M, L, O);
+    const rsrc_t rb = make_rsrc(p.bstate, (uint32_t)(p.n_units * p.bch_max) * G * PR * 4u);
+    const uint32_t ubb = (uint32_t)(u * p.bch_max) * G * PR * 4u, sb = (uint32_t)G * PR * 4u;
+    const rsrc_t rp = make_rsrc(p.part, (uint32_t)p.n_waves * G * PR * 4u);
+    const uint32_t ubp = (uint32_t)first * G * PR * 4u, sp = (uint32_t)step * G * PR * 4u;
+    const int nb = p.n_bch, total = nb + count;
+    fold_run<D, G>([&](CombineBatch<D, G> &b, int k0) {
+        load_batch_two<D, G>(b, rb, ubb, sb, nb, rp, ubp, sp, k0, total, lane);
+    }, total, M, L, O);
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
