@@ -1633,6 +1633,69 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                     lg[i][h] = 0.0f;
             if constexpr (KF != KVQ_K_LLOYD4) {
                 score_asym<D, G, KF, VF, ALL, CH0, PREC>(cur, rq, mcur, lg);
+            } else if constexpr (ALL && !PREC) {
+                // Every row kept: a two-stage pipeline over the rows.  Row r + 1's table
+                // lookups and query words go out after row r's first products, so their
+                // latency hides behind the rest of row r.  The LDS reads and the uniform
+                // loads share one wait counter, and a wait for the scalar loads covers every
+                // outstanding read: loads issued before a row's first products would be waited
+                // for there.  The scheduling barriers keep this order (the compiler would move
+                // the uniform loads next to their use).
+                uint32_t pr[2][TPL][4];
+                auto lookup = [&](uint32_t (&o)[TPL][4], int r) {
+#pragma unroll
+                    for (int i = 0; i < TPL; i++) {
+                        const uint32_t x = i == 0 ? cur.kc[r].x : cur.kc[r].y;
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            o[i][j] = sm.lut[(x >> (8 * j)) & 0xFFu];
+                    }
+                };
+                static_assert(G * C::QW % 4 == 0, "a row's query words in uint4 loads");
+                uint4 qb[2][G * C::QW / 4]; // a row's query words (uniform)
+                auto loadq = [&](uint4 (&o)[G * C::QW / 4], int r) {
+                    const uint4 *q4 = reinterpret_cast<const uint4 *>(rq + C::OFF_QP + r * G * C::QW);
+#pragma unroll
+                    for (int e = 0; e < G * C::QW / 4; e++)
+                        o[e] = q4[e];
+                };
+                lookup(pr[0], 0);
+                loadq(qb[0], 0);
+#pragma unroll
+                for (int r = 0; r < KROWS; r++) {
+                    uint32_t(&cp)[TPL][4] = pr[r & 1];
+                    const uint4(&qc)[G * C::QW / 4] = qb[r & 1];
+                    auto qword = [&](int h, int j) {
+                        const uint4 v = qc[(h * C::QW + j) / 4];
+                        const int e = (h * C::QW + j) % 4;
+                        return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+                    };
+#pragma unroll
+                    for (int i = 0; i < TPL; i++)
+                        lg[i][0] = dot2(cp[i][0], qword(0, 0), lg[i][0]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (r + 1 < KROWS) {
+                        lookup(pr[(r + 1) & 1], r + 1);
+                        loadq(qb[(r + 1) & 1], r + 1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+#pragma unroll
+                        for (int j = (h == 0 ? 1 : 0); j < 4; j++) {
+#pragma unroll
+                            for (int i = 0; i < TPL; i++)
+                                lg[i][h] = dot2(cp[i][j], qword(h, j), lg[i][h]);
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int i = 0; i < TPL; i++) {
+                    const float rho = f16_to_f32(i == 0 ? (cur.kx & 0xFFFFu) : (cur.kx >> 16));
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        lg[i][h] *= rho;
+                }
             } else {
 #pragma unroll
                 for (int r = 0; r < KROWS; r++) {
