@@ -174,11 +174,20 @@ constexpr int kNonTemporal = 2;
 constexpr uint32_t kNoAccess = 0x80000000u;
 // log2 slack of the lazily raised softmax maximum (weights stay below 2^kSlack)
 constexpr float kSlack = 2.0f;
+// A raised maximum is set this far (log2) above the largest logit seen, so the next raise
+// waits for a logit kRaiseRoom + kSlack above it: fewer raises, at the price of weights
+// 2^kRaiseRoom smaller, which raises by as much the point where small fp16 weights turn
+// subnormal (they carry 2^vexp, so that point stays far below the largest weight).
+constexpr float kRaiseRoom = 2.0f;
 // Largest value-weight exponent (see the decode kernel): the weights 2^(l - m + vexp) stay
 // below 2^(kSlack + kVexpMax) = 2^15 in fp16.
 constexpr int kVexpMax = 13;
+// A lowered value exponent leaves this many binades below the 2^13 bound for the largest
+// scale seen, so a later, larger scale lowers it again only when it is 2^kVexpRoom times
+// larger.
+constexpr int kVexpRoom = 3;
 // fp16 bits of the largest value scale s allowed with exponent e (s * 2^e < 2^13), in both
-// halves; e = -3 allows every finite fp16.
+// halves; e = -3 allows every finite fp16 (the smallest exponent used).
 __device__ __forceinline__ uint32_t vexp_thr(int e)
 {
     const uint32_t b = ((uint32_t)(28 - e) << 10) - 1u;
@@ -1371,10 +1380,13 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
     float bacc[G][KQ ? 8 : 1]; // KQV: sketch-bit sums per channel
     float zacc[G][NGV];
     float lsum[G];
-    // Softmax state per head: the raise threshold mthr (accumulator units; -inf while the
-    // state is empty) and msub = m - vexp, the running maximum m in the weights' units, so
-    // m = msub + vexp (no register of its own).
-    float mthr[G];
+    // Softmax state per head: msub = m - vexp, the running maximum m in the weights' units,
+    // so m = msub + vexp (no register of its own).  A weight's exponent is
+    // x = l - msub = l - m + vexp; the maximum is raised when some x exceeds the wave-uniform
+    // threshold xthr = kSlack + vexp, i.e. a logit exceeds m + kSlack.  xthr is -inf while the
+    // state is empty (every head's at once: logits are masked by position, the same for all
+    // heads), so the first tile with a finite logit sets m.
+    float xthr = -__builtin_inff();
     // Value weights carry a power of two 2^vexp (wave-uniform): the fp16 products p * s
     // (p < 2^kSlack, s a value scale) must stay finite and normal whatever the values'
     // magnitude.  vexp starts at kVexpMax and is lowered (the state rescaled, as for a raised
@@ -1388,7 +1400,6 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
 #pragma unroll
         for (int h = 0; h < G; h++) {
             lsum[h] = 0.0f;
-            mthr[h] = -__builtin_inff();
             msub[h] = -(float)kVexpMax;
 #pragma unroll
             for (int j = 0; j < 8; j++)
@@ -1434,7 +1445,7 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             __syncthreads();
             const float ls = wave_sum_dpp(lsum[h]);
             // the state's maximum in the weights' units (they carry 2^vexp)
-            const float mst = mthr[h] == -__builtin_inff() ? -__builtin_inff() : msub[h];
+            const float mst = xthr == -__builtin_inff() ? -__builtin_inff() : msub[h];
             float zs[NGV];
 #pragma unroll
             for (int g = 0; g < NGV; g++)
@@ -1617,13 +1628,9 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             const int bt = RP ? t >> tlw : 0;
             const uint32_t *__restrict__ rq = rec + ((uint32_t)t >> 31) + (size_t)bt * C::QREC;
             if (RP && bt != qbk) {
-                // a tile of another bucket: its scales, and the raise threshold in its units
+                // a tile of another bucket: its scales (the raise test is in log2 units)
                 load_scales(bt);
                 qbk = bt;
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    if (mthr[h] != -__builtin_inff())
-                        mthr[h] = (msub[h] + (float)vexp + kSlack) / acc_to_logit[h];
             }
             float lg[TPL][G];
 #pragma unroll
@@ -1790,48 +1797,56 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
             // ---- online softmax (log2 units), per head.  The running maximum m is raised
             // (wave-wide DPP max, rescale of that head's state) only when a logit exceeds
             // m + kSlack; otherwise weights 2^(l - m) may reach 2^kSlack, and the raise is
-            // rare after the first tile.  The test runs in accumulator units against
-            // mthr = (m + kSlack) / acc_to_logit; a rounding miss is harmless.  A value scale
-            // beyond sthr lowers vexp in the same branch (every head's state rescaled).
-            // One branch per tile covers all heads: one per head splits the tile's code into
-            // blocks the compiler cannot schedule across, which costs far more than the
-            // raises themselves (about one per two tiles over all heads).
-            uint64_t above[G];
-            uint64_t any_above = s_above;
+            // rare after the first tile.  The weights' exponents x = l - msub are computed
+            // first and their lane maximum is tested against xthr = kSlack + vexp (one compare
+            // for all heads and positions); a rounding miss is harmless.  A value scale beyond
+            // sthr lowers vexp in the same branch (every head's state rescaled).  One branch
+            // per tile covers all heads: one per head splits the tile's code into blocks the
+            // compiler cannot schedule across, which costs far more than the raises
+            // themselves (about one per two tiles over all heads).
+            float xw[TPL][G];
+            float xmx = -__builtin_inff();
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                above[h] = 0;
+            for (int h = 0; h < G; h++)
 #pragma unroll
-                for (int i = 0; i < TPL; i++)
-                    above[h] |= __ballot(lg[i][h] > mthr[h]);
-                any_above |= above[h];
-            }
-            if (any_above) {
+                for (int i = 0; i < TPL; i++) {
+                    xw[i][h] = fmaf(lg[i][h], acc_to_logit[h], -msub[h]);
+                    xmx = fmaxf(xmx, xw[i][h]);
+                }
+            if (s_above | __ballot(xmx > xthr)) {
                 int enew = vexp;
                 if (s_above) {
                     // the wave's largest scale: 2^(e-15) <= s < 2^(e-14) for exponent field e,
-                    // so vexp = 27 - e keeps s * 2^vexp below 2^13
+                    // so vexp = 27 - e keeps s * 2^vexp below 2^13; kVexpRoom binades lower
+                    // (not below -3, which admits every finite scale) leaves room for larger
+                    // scales to come
                     const uint32_t lm = (smx & 0xFFFFu) > (smx >> 16) ? (smx & 0xFFFFu) : (smx >> 16);
                     const int e = (int)wave_max_dpp((float)lm) >> 10;
-                    enew = min(vexp, 27 - e);
+                    enew = min(vexp, max(-3, 27 - kVexpRoom - e));
                 }
                 const float fe = ldexpf(1.0f, enew - vexp);
+                bool filled = xthr != -__builtin_inff();
 #pragma unroll
                 for (int h = 0; h < G; h++) {
-                    if (!above[h] && enew == vexp)
+                    float xh = xw[0][h];
+#pragma unroll
+                    for (int i = 1; i < TPL; i++)
+                        xh = fmaxf(xh, xw[i][h]);
+                    const bool above = __ballot(xh > xthr) != 0;
+                    if (!above && enew == vexp)
                         continue;
-                    const float mold = mthr[h] == -__builtin_inff() ? -__builtin_inff() : msub[h] + (float)vexp;
+                    const float mold = xthr == -__builtin_inff() ? -__builtin_inff() : msub[h] + (float)vexp;
                     float mnew = mold;
-                    if (above[h]) {
+                    if (above) {
                         float mt = lg[0][h];
 #pragma unroll
                         for (int i = 1; i < TPL; i++)
                             mt = fmaxf(mt, lg[i][h]);
-                        mnew = fmaxf(mold, wave_max_dpp(mt * acc_to_logit[h]));
+                        mnew = fmaxf(mold, wave_max_dpp(mt * acc_to_logit[h]) + kRaiseRoom);
                     }
+                    filled = filled || mnew != -__builtin_inff();
                     // (a state still empty, m = -inf, is all zeros: any finite factor keeps it)
                     const float alpha = mold == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mold - mnew) * fe;
-                    mthr[h] = mnew == -__builtin_inff() ? mnew : (mnew + kSlack) / acc_to_logit[h];
                     // (a maximum still at -inf means every logit so far, this tile's included,
                     // is -inf: subtract -vexp instead so the weights come out 0, not NaN)
                     msub[h] = (mnew == -__builtin_inff() ? 0.0f : mnew) - (float)enew;
@@ -1847,16 +1862,20 @@ void decode_kernel(DecodeParams p, const uint32_t *__restrict__ qrec)
                         for (int j = 0; j < 8; j++)
                             bacc[h][j] *= alpha;
                     }
+#pragma unroll
+                    for (int i = 0; i < TPL; i++)
+                        xw[i][h] = fmaf(lg[i][h], acc_to_logit[h], -msub[h]);
                 }
                 vexp = enew;
                 sthr = vexp_thr(enew);
+                xthr = filled ? kSlack + (float)enew : -__builtin_inff();
             }
             float pw[TPL][G];
 #pragma unroll
             for (int h = 0; h < G; h++)
 #pragma unroll
                 for (int i = 0; i < TPL; i++)
-                    pw[i][h] = __builtin_amdgcn_exp2f(fmaf(lg[i][h], acc_to_logit[h], -msub[h]));
+                    pw[i][h] = __builtin_amdgcn_exp2f(xw[i][h]);
             // zero-point term and the fp16 weights p*s of this lane's position pair (-> LDS),
             // from the weights rounded to fp16 pairs: one packed product and one dot2 per
             // (group, head)
