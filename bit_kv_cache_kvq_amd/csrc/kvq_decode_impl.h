@@ -384,9 +384,13 @@ __device__ __forceinline__ float bfly_sum(float v)
 // state (m, l, o) of their positions per head, which the decode kernel folds into the unit's
 // result: chunk 0, the sinks (in bucket 0's record workgroup, or in one of its own when there
 // are many), and chunk c >= 1, the recent window's part of one 64-aligned block of positions
-// (the chunks come first in the grid: the longest work).
-template <int D, int G, int KF>
-__global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
+// (the chunks come first in the grid: the longest work).  REC: a grid of mostly record
+// workgroups; with four heads it is compiled for eight waves per SIMD (at most 64 registers
+// per lane), so the many short record workgroups (bucket-relative RoPE, large batches)
+// overlap their latencies, while the chunk paths, which few of its workgroups take, keep some
+// values in scratch.  A grid of mostly chunks takes the build without that bound.
+template <int D, int G, int KF, bool REC>
+__global__ __launch_bounds__(kWave * G, REC && G == 4 ? 8 : 2) void qprep_kernel(DecodeParams p)
 {
     using C = Cfg<D, G, KF>;
     constexpr int KB = C::KB, KROWS = C::KROWS, PPW = C::PPW, NG = C::NG, NP = C::NP;
@@ -395,7 +399,12 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     // registers: a wave's share of a chunk, or the few sinks of a record workgroup
     constexpr int RW = kWave / G;
     constexpr int NVR = RW > 2 * kSinksInRecord ? RW : 2 * kSinksInRecord;
-    __shared__ float sq_[G][D + 4]; // (+4: the heads' rows start in other LDS banks)
+    // A chunk lane holds the channels of one of the G parts of its key row (CPP channels, KQ
+    // 16-byte words).  The scaled, masked queries sit in LDS with 4 words of padding after each
+    // part (and 4 more per head), so the lanes of the G parts read them from different banks.
+    constexpr int CPP = D / G, KQ = CPP / 8, SQS = D + 4 * G + 4;
+    __shared__ float sq_[G * SQS];
+    auto sqi = [](int g, int c) { return g * SQS + c + 4 * (c / CPP); };
     __shared__ float su_[G][D];     // the masked query before the softmax scale
     __shared__ float se[G][NP];
     __shared__ float sam[G][NP];
@@ -475,7 +484,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
     // instead: every lane loads its CPL channels of each sink row, key j into vr[j] and value
     // j into vr[kSinksInRecord + j]; each sink's logit is one wave-wide sum.
     const bool few = state && !chunk_only;
-    uint4 kr[D / 8];  // key row h*RW + lane % RW (bf16; rows past nrows: zeros)
+    uint4 kr[KQ];     // part lane / RW of key row h*RW + lane % RW (bf16; rows past nrows: zeros)
     uint32_t vr[NVR]; // value rows: this lane's CPL bf16 channels of row j (CPL = 1: low half)
     const int jrow = h * RW + lane % RW; // the row this lane scores
     if (few) {
@@ -491,9 +500,9 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             }
         }
     } else if (nrows > 0) {
-        const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + row_off(jrow));
+        const uint4 *krow = reinterpret_cast<const uint4 *>(kbase + row_off(jrow)) + (lane / RW) * KQ;
 #pragma unroll
-        for (int c = 0; c < D / 8; c++)
+        for (int c = 0; c < KQ; c++)
             kr[c] = jrow < nrows ? krow[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int jr = 0; jr < RW; jr++) {
@@ -613,7 +622,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
         const bool kept = (mask >> (c / 16)) & 1u;
         ym[s] = kept ? ym[s] : 0.0f;
         su_[h][c] = ym[s];
-        sq_[h][c] = ym[s] * qscale;
+        sq_[sqi(h, c)] = ym[s] * qscale;
     }
     __syncthreads();
 
@@ -632,7 +641,7 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
             float qo[CPL];
 #pragma unroll
             for (int s = 0; s < CPL; s++)
-                qo[s] = sq_[h][lane * CPL + s];
+                qo[s] = sq_[sqi(h, lane * CPL + s)];
             float mine = -__builtin_inff();
 #pragma unroll
             for (int j = 0; j < kSinksInRecord; j++) {
@@ -658,23 +667,39 @@ __global__ __launch_bounds__(kWave * G, 2) void qprep_kernel(DecodeParams p)
                 }
             }
         } else if (nrows > 0) {
-            // Wave h's share of the rows for every head: lane l scores row jrow against head
-            // l / RW's masked, scaled query (four partial sums, sum e taking channels 8i + 2e and
-            // 8i + 2e + 1: short dependency chains), the share's max and sum per head over its
-            // RW lanes, then every lane sums its CPL channels of the share's value rows for every
-            // head.  The shares' states meet in LDS; wave h merges head h's.
-            const int hl = lane / RW; // the head this lane scores for
-            float dp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // Wave h's share of the rows for every head: the G lanes l % RW + k * RW hold the G
+            // parts of row jrow; each scores its part against every head's masked, scaled query
+            // (four partial sums, sum e taking channels 8i + 2e and 8i + 2e + 1: short dependency
+            // chains), the parts are summed over those lanes (an xor butterfly: every lane of the
+            // row gets the same sums), and lane l keeps head l / RW's.  Then the share's max and
+            // sum per head over its RW lanes, and every lane sums its CPL channels of the share's
+            // value rows for every head.  The shares' states meet in LDS; wave h merges head h's.
+            const int hl = lane / RW; // the head this lane keeps (and the part it holds)
+            float dg[G];
 #pragma unroll
-            for (int c = 0; c < D / 8; c++) {
-                const uint32_t kk[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+            for (int g = 0; g < G; g++) {
+                float dp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    dp[e] = fmaf(sq_[hl][8 * c + 2 * e], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
-                    dp[e] = fmaf(sq_[hl][8 * c + 2 * e + 1], bf16_to_f32(kk[e] >> 16), dp[e]);
+                for (int c = 0; c < KQ; c++) {
+                    const uint32_t kk[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+                    const int c0 = hl * CPP + 8 * c;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        dp[e] = fmaf(sq_[sqi(g, c0 + 2 * e)], bf16_to_f32(kk[e] & 0xFFFFu), dp[e]);
+                        dp[e] = fmaf(sq_[sqi(g, c0 + 2 * e + 1)], bf16_to_f32(kk[e] >> 16), dp[e]);
+                    }
                 }
+                dg[g] = (dp[0] + dp[1]) + (dp[2] + dp[3]);
             }
-            const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
+#pragma unroll
+            for (int o = RW; o < kWave; o <<= 1)
+#pragma unroll
+                for (int g = 0; g < G; g++)
+                    dg[g] += __shfl_xor(dg[g], o);
+            float dot = dg[0];
+#pragma unroll
+            for (int g = 1; g < G; g++)
+                dot = hl == g ? dg[g] : dot;
             const bool valid = jrow < nrows;
             const float lw = valid ? dot : -__builtin_inff();
             const float mw = seg_max<RW>(lw); // -inf for a share without rows
@@ -2039,7 +2064,11 @@ hipError_t launch_one(int units, const DecodeParams &p, hipEvent_t const ev[2], 
 {
     // window chunks, the sinks' chunk (many sinks), then the record groups
     const unsigned qgrid = (unsigned)(qprep_groups(p) * units);
-    hipLaunchKernelGGL((qprep_kernel<D, G, KF>), dim3(qgrid), dim3(kWave * G), 0, s, p);
+    const int chunk_wgs = (p.n_bch - 1 + (p.n_sink > kSinksInRecord ? 1 : 0)) * units;
+    if ((int)qgrid - chunk_wgs >= 4 * chunk_wgs)
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, true>), dim3(qgrid), dim3(kWave * G), 0, s, p);
+    else
+        hipLaunchKernelGGL((qprep_kernel<D, G, KF, false>), dim3(qgrid), dim3(kWave * G), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
